@@ -1,0 +1,253 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each pin takes the oracle module as an argument so the mutation test can run
+the same pins against a copy of the oracle with a planted mistake.
+
+Sources: Kamera preprint ("Kamera: Unified Position-Invariant Multimodal KV
+Cache for Training-Free Reuse") §1 (R(delta)R(p) = R(p+delta)), §3 (V and c_KV
+never rotated; MLA rotates only the 64-d k_rope; patch both channels), §5
+(survivors need rotation only), §6 (paged KV pool), Fig. 2 (layout sizes),
+App. A (rotate first, then add U @ V^T; factors kept as U*Sigma, V^T).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+try:
+    import mpmath
+except ImportError:  # pragma: no cover
+    mpmath = None
+
+RNG = np.random.default_rng(20260602)
+
+
+def _x(T, F, seed=0):
+    return np.random.default_rng(seed).standard_normal((T, F))
+
+
+# --------------------------------------------------------------------- theta
+def pin_theta_geometric(o):
+    """Textbook RoPE frequencies: a geometric run that starts at 1 and would reach
+    1/base after d_rot/2 steps; checked against 40-digit mpmath."""
+    mpmath.mp.dps = 40
+    for d, base in [(64, 1e4), (128, 1e4), (128, 1e6), (64, 1e6)]:
+        th = o.inv_freq(d, base)
+        assert th.shape == (d // 2,)
+        ratio = mpmath.power(mpmath.mpf(base), mpmath.mpf(-2) / d)
+        for i in range(d // 2):
+            want = mpmath.power(ratio, i)
+            assert abs(th[i] - float(want)) <= 4e-16 * float(want), (d, base, i)
+        assert abs(float(mpmath.power(ratio, d // 2)) * base - 1) < 1e-30 + 1e-15
+
+
+def pin_pairs_from_pages(o):
+    """Kamera Fig. 2: 128-d GQA heads carry 64 rope pairs; MLA k_rope 64-d = 32 pairs,
+    and the band is the trailing 64 columns after the 512-d c_KV."""
+    p, q = o.pair_columns(128, o.NEOX)
+    assert len(p) == 64 and sorted(np.concatenate([p, q]).tolist()) == list(range(128))
+    p, q = o.pair_columns(64, o.NEOX)
+    assert len(p) == 32
+    assert o.band_offsets(o.MLA, latent_dim=512) == [512]
+    assert o.band_offsets(o.GQA, num_kv_heads=4, head_dim=128) == [0, 128, 256, 384]
+
+
+# --------------------------------------------------------------------- rotation
+def pin_complex_multiply(o):
+    """R(delta) on a pair equals (a + ib) * exp(i delta theta) (RoFormer's RoPE).
+    NeoX pairs column i with i + d/2; GPT-J uses numpy's own complex layout
+    (interleaved re, im) via a dtype view. Phase from mpmath at 30 digits."""
+    mpmath.mp.dps = 30
+    for d, base, delta in [(128, 1e6, 32768), (64, 1e4, 4096), (128, 1e4, -1234), (64, 1e4, 65536)]:
+        x = _x(5, d, seed=d + abs(delta))
+        th = [mpmath.power(mpmath.mpf(base), mpmath.mpf(-2 * i) / d) for i in range(d // 2)]
+        e = np.array([complex(mpmath.cos(delta * t), mpmath.sin(delta * t)) for t in th])
+        # NeoX
+        z = x[:, : d // 2] + 1j * x[:, d // 2:]
+        want = z * e[None, :]
+        y = o.rotate(x, delta, [0], d, base, o.NEOX)
+        got = y[:, : d // 2] + 1j * y[:, d // 2:]
+        tol = 1e-14 + abs(delta) * 2.0 ** -52 * 4
+        assert np.max(np.abs(got - want)) <= tol * np.max(np.abs(x)) * 2, (d, delta)
+        # GPT-J: numpy complex128 memory layout is (re, im) interleaved
+        zc = np.ascontiguousarray(x).view(np.complex128)
+        wantj = (zc * e[None, :]).view(np.float64)
+        yj = o.rotate(x, delta, [0], d, base, o.GPTJ)
+        assert np.max(np.abs(yj - wantj)) <= tol * np.max(np.abs(x)) * 2, (d, delta)
+
+
+def pin_composition(o):
+    """Kamera §1: R(d) R(p) = R(p + d), against direct rotation at p + d."""
+    rng = np.random.default_rng(7)
+    for _ in range(12):
+        p, d = (int(v) for v in rng.integers(-2 ** 17, 2 ** 17, size=2))
+        x = _x(4, 128, seed=abs(p) % 1000)
+        a = o.rotate(o.rotate(x, p, [0], 128, 1e6, o.NEOX), d, [0], 128, 1e6, o.NEOX)
+        b = o.rotate(x, p + d, [0], 128, 1e6, o.NEOX)
+        # angles are rounded fp64 products: |phi| 2^-52 per product, three products
+        assert np.max(np.abs(a - b)) <= 1e-10 * np.max(np.abs(x)), (p, d)
+
+
+def pin_norm_and_inverse(o):
+    """A rotation keeps each pair's norm, and R(-delta) undoes R(delta)."""
+    x = _x(16, 256, seed=3)
+    for delta in (1, 777, -40000, 65536):
+        y = o.rotate(x, delta, [0, 128], 128, 1e4, o.NEOX)
+        p, q = o.pair_columns(128, o.NEOX)
+        for off in (0, 128):
+            n0 = x[:, off + p] ** 2 + x[:, off + q] ** 2
+            n1 = y[:, off + p] ** 2 + y[:, off + q] ** 2
+            assert np.max(np.abs(n1 - n0) / n0) < 1e-14
+        back = o.rotate(y, -delta, [0, 128], 128, 1e4, o.NEOX)
+        assert np.max(np.abs(back - x)) < 1e-13
+
+
+def pin_identity(o):
+    """delta = 0 with no patch returns the stored codes bit for bit (bf16 and fp32)."""
+    bits = np.random.default_rng(1).integers(0, 0x7F00, size=(32, 256), dtype=np.uint16)
+    bits[:, ::7] |= 0x8000
+    x = o.upcast(bits, o.BF16)
+    yk, yv = o.rehydrate_gqa(x, x, 0, num_kv_heads=2, head_dim=128, base=1e6, patch=False)
+    assert np.array_equal(o.round_bf16(yk), bits) and np.array_equal(o.round_bf16(yv), bits)
+    f = np.random.default_rng(2).standard_normal((8, 128)).astype(np.float32)
+    yk, _ = o.rehydrate_gqa(f.astype(np.float64), f.astype(np.float64), 0, num_kv_heads=2, head_dim=64,
+                            base=1e4, patch=False)
+    assert np.array_equal(o.round_f32(yk).view(np.uint32), f.view(np.uint32))
+
+
+def pin_large_delta_phase(o):
+    """cos/sin of delta*theta_i at large |delta| against 40-digit mpmath: error is only
+    the fp64 rounding of the product (|phi| 2^-53) plus the libm rounding."""
+    mpmath.mp.dps = 40
+    for delta in (65536, 2 ** 31 - 1, -(2 ** 31 - 1), 1_000_003):
+        c, s = o.phases(delta, 128, 1e6)
+        th = [mpmath.power(mpmath.mpf(10) ** 6, mpmath.mpf(-2 * i) / 128) for i in range(64)]
+        for i in (0, 1, 17, 63):
+            phi = delta * th[i]
+            bound = abs(float(phi)) * 2.0 ** -52 + 2.0 ** -52
+            assert abs(c[i] - float(mpmath.cos(phi))) <= bound, (delta, i)
+            assert abs(s[i] - float(mpmath.sin(phi))) <= bound, (delta, i)
+
+
+# --------------------------------------------------------------------- patch
+def pin_patch_is_matmul(o):
+    """Y(patch) - Y(no patch) = U @ V^T by BLAS dgemm, on K (rotated) and V; the
+    patch is added after the rotation and is itself not rotated (App. A)."""
+    T, H, d, m = 40, 2, 64, 8
+    k, v = _x(T, H * d, 4), _x(T, H * d, 5)
+    fac = [o.Factor(0, 0, _x(T, m, 6), _x(m, H * d, 7)), o.Factor(1, 0, _x(T, m, 8), _x(m, H * d, 9))]
+    yk, yv = o.rehydrate_gqa(k, v, 321, num_kv_heads=H, head_dim=d, base=1e4, factors=fac)
+    zk, zv = o.rehydrate_gqa(k, v, 321, num_kv_heads=H, head_dim=d, base=1e4, factors=fac, patch=False)
+    for got, f in ((yk - zk, fac[0]), (yv - zv, fac[1])):
+        want = f.u @ f.vt
+        assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want)) * 4
+    # V rows are not rotated: no-patch V equals the input exactly
+    assert np.array_equal(zv, v)
+    # a factor covering part of a row touches only its columns
+    row = _x(T, 576, 10)
+    fb = o.Factor(0, 512, _x(T, m, 11), _x(m, 64, 12))
+    y = o.rehydrate_mla(row, 99, latent_dim=512, rope_dim=64, base=1e4, factors=[fb])
+    z = o.rehydrate_mla(row, 99, latent_dim=512, rope_dim=64, base=1e4, factors=[fb], patch=False)
+    d_ = y - z
+    assert np.all(d_[:, :512] == 0)
+    assert np.max(np.abs(d_[:, 512:] - fb.u @ fb.vt)) <= 1e-13 * 8
+
+
+def pin_full_rank_reconstructs(o):
+    """A full-rank patch from LAPACK's SVD of a random Delta rebuilds it (rank = min(T,F))."""
+    import scipy.linalg
+    T, F = 24, 16
+    delta = _x(T, F, 13)
+    u, s, vt = scipy.linalg.svd(delta, full_matrices=False)
+    x = _x(T, F, 14)
+    y = o.rehydrate_tensor(x, tensor=1, family=o.GQA, delta=0, rotate_this=False, bands=[], d_rot=16,
+                           base=1e4, pairing=o.NEOX, factors=[o.Factor(1, 0, u * s, vt)])
+    assert np.max(np.abs(y - (x + delta))) < 1e-12
+
+
+# --------------------------------------------------------------------- survivors / MLA
+def pin_survivor_rotation_only(o):
+    """Kamera §5: survivors get R(delta) only; V (and MLA c_KV) untouched."""
+    k, v = _x(20, 256, 15), _x(20, 256, 16)
+    y = o.relocate(k, -3000, family=o.GQA, num_kv_heads=2, head_dim=128, base=1e6)
+    z, zv = o.rehydrate_gqa(k, v, -3000, num_kv_heads=2, head_dim=128, base=1e6, patch=False)
+    assert np.array_equal(y, z) and np.array_equal(zv, v)
+    row = _x(20, 576, 17)
+    ym = o.relocate(row, 12345, family=o.MLA, latent_dim=512, rope_dim=64, base=1e4)
+    assert np.array_equal(ym[:, :512], row[:, :512])          # c_KV byte-for-byte
+    assert not np.allclose(ym[:, 512:], row[:, 512:])          # the band did move
+
+
+# --------------------------------------------------------------------- paging
+def pin_paging_bruteforce(o):
+    """Every slot0 in a 16-token page: gather by block table returns the rows in order,
+    and every slot outside [slot0, slot0+T) keeps its sentinel."""
+    P, F = 16, 4
+    for T in (1, 15, 16, 17, 33, 48):
+        for slot0 in range(P):
+            npg = -(-(slot0 + T) // P)
+            table = np.random.default_rng(T * 31 + slot0).permutation(8)[:npg]
+            pool = np.full((8, P, F), -7.0)
+            rows = np.arange(T * F, dtype=np.float64).reshape(T, F)
+            o.scatter_to_pool(pool, rows, table, slot0)
+            written = np.zeros((8, P), bool)
+            for t in range(T):                       # independent walk of the slots
+                slot = slot0 + t
+                pg, off = table[slot // P], slot % P
+                assert np.array_equal(pool[pg, off], rows[t])
+                written[pg, off] = True
+            assert np.all(pool[~written] == -7.0)
+
+
+# --------------------------------------------------------------------- rounding
+def pin_bf16_rounding(o):
+    """Exhaustive over bf16 codes: exact values round to themselves; midpoints between
+    neighbours go to the even code; a hair above/below goes to the nearer one; torch's
+    fp32 -> bf16 cast (RNE) agrees on random fp32 values."""
+    import torch
+    codes = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = o.upcast(codes, o.BF16)
+    finite = np.isfinite(vals)
+    assert np.array_equal(o.round_bf16(vals[finite]), codes[finite])
+    pos = codes[(codes < 0x7F7F) & (codes > 0)]                # positive finite with a finite successor
+    lo, hi = o.upcast(pos, o.BF16), o.upcast(pos + 1, o.BF16)
+    mid = (lo + hi) / 2                                        # exact in fp64
+    even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint16)
+    assert np.array_equal(o.round_bf16(mid), even)
+    assert np.array_equal(o.round_bf16(-mid), even | 0x8000)
+    up = np.nextafter(mid, np.inf)
+    dn = np.nextafter(mid, -np.inf)
+    assert np.array_equal(o.round_bf16(up), (pos + 1).astype(np.uint16))
+    assert np.array_equal(o.round_bf16(dn), pos)
+    r = np.random.default_rng(5).integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = r.view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) < 3.3e38)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.round_bf16(f.astype(np.float64)), want)
+
+
+# --------------------------------------------------------------------- builder
+def pin_builder_planted(b):
+    """Planted spectrum Delta = Q1 diag(sigma) Q2^T with sigma_i = 0.3*0.9^i: the top-m
+    singular values are the planted ones, and the Eckart-Young residual
+    ||Delta - U_m V_m^T||_F^2 equals sum_{i>=m} sigma_i^2 (closed form)."""
+    rng = np.random.default_rng(11)
+    T, F, r, m = 96, 64, 40, 8
+    q1, _ = np.linalg.qr(rng.standard_normal((T, r)))
+    q2, _ = np.linalg.qr(rng.standard_normal((F, r)))
+    sig = 0.3 * 0.9 ** np.arange(r)
+    delta = (q1 * sig) @ q2.T
+    us, vt, s = b.truncated_svd(delta, m)
+    assert np.allclose(s[:r], sig, rtol=1e-12, atol=1e-15)
+    res = b.residual_energy(delta, us, vt)
+    assert abs(res - np.sum(sig[m:] ** 2)) <= 1e-12 * np.sum(sig ** 2)
+    # the compile-step deficit subtracts the relocated canonical (App. A)
+    x = rng.standard_normal((T, 128))
+    cond = x + 0.0
+    d = b.deficit(cond, x, 0, bands=[0], d_rot=128, base=1e4, pairing=0)
+    assert np.all(d == 0)
+
+
+ORACLE_PINS = [pin_theta_geometric, pin_pairs_from_pages, pin_complex_multiply, pin_composition,
+               pin_norm_and_inverse, pin_identity, pin_large_delta_phase, pin_patch_is_matmul,
+               pin_full_rank_reconstructs, pin_survivor_rotation_only, pin_paging_bruteforce,
+               pin_bf16_rounding]

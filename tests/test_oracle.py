@@ -1,0 +1,151 @@
+"""The fp64 oracle against its pins, and planted mistakes against the pins (CPU only)."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import oracle.builder_oracle as builder
+import oracle.kamera_oracle as O
+from oracle import tolerance as tol
+from tests.oracle_pins import ORACLE_PINS, pin_builder_planted
+
+ORACLE_PATH = os.path.join(os.path.dirname(O.__file__), "kamera_oracle.py")
+
+
+@pytest.mark.parametrize("pin", ORACLE_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(O)
+
+
+def test_builder_pin():
+    pin_builder_planted(builder)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _fresh_oracle():
+    spec = importlib.util.spec_from_file_location("kamera_oracle_mutant", ORACLE_PATH)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _mut_sign(m):
+    orig = m.phases
+    m.phases = lambda d, r, b: (orig(d, r, b)[0], -orig(d, r, b)[1])
+
+
+def _mut_cos_sin_swapped(m):
+    orig = m.phases
+    m.phases = lambda d, r, b: tuple(reversed(orig(d, r, b)))
+
+
+def _mut_pairing(m):
+    orig = m.pair_columns
+    m.pair_columns = lambda d, p: orig(d, m.GPTJ if p == m.NEOX else m.NEOX)
+
+
+def _mut_theta_half(m):
+    m.inv_freq = lambda d, b: np.float64(b) ** (-1.0 * np.arange(d // 2) / d)
+
+
+def _mut_theta_shift(m):
+    m.inv_freq = lambda d, b: np.float64(b) ** (-2.0 * (np.arange(d // 2) + 1) / d)
+
+
+def _mut_theta_f32(m):
+    m.inv_freq = lambda d, b: (np.float32(b) ** (np.float32(-2.0) * np.arange(d // 2, dtype=np.float32)
+                                                 / np.float32(d))).astype(np.float64)
+
+
+def _mut_patch_before_rotate(m):
+    def rt(x, *, tensor, family, delta, rotate_this, bands, d_rot, base, pairing, factors=(), patch=True):
+        y = np.array(x, dtype=np.float64)
+        if patch:
+            for f in factors:
+                if f.tensor == tensor:
+                    m.add_patch(y, f.u, f.vt, f.col0)
+        return m.rotate(y, delta, bands, d_rot, base, pairing) if rotate_this else y
+    m.rehydrate_tensor = rt
+
+
+def _mut_patch_rank_reversed(m):
+    def ap(y, u, vt, col0):
+        w, k = vt.shape[1], u.shape[1]
+        for j in range(k):
+            y[:, col0:col0 + w] += np.outer(u[:, j], vt[k - 1 - j, :])
+        return y
+    m.add_patch = ap
+
+
+def _mut_round_truncate(m):
+    def rb(y):
+        r32 = np.asarray(y, np.float64).astype(np.float32)
+        return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    m.round_bf16 = rb
+
+
+def _mut_round_double(m):
+    import torch
+    def rb(y):
+        f = np.asarray(y, np.float64).astype(np.float32)
+        return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    m.round_bf16 = rb
+
+
+def _mut_page_no_slot0(m):
+    def ps(T, bt, slot0, P):
+        s = np.arange(T)
+        return np.asarray(bt)[s // P], s % P
+    m.page_slots = ps
+
+
+def _mut_v_rotated(m):
+    orig = m.rehydrate_gqa
+    def rg(k, v, delta, **kw):
+        yk, yv = orig(k, v, delta, **kw)
+        return yk, m.rotate(yv, delta, m.band_offsets(m.GQA, kw["num_kv_heads"], kw["head_dim"]),
+                            kw["head_dim"], kw["base"], kw.get("pairing", m.NEOX))
+    m.rehydrate_gqa = rg
+
+
+def _mut_mla_latent_band(m):
+    orig = m.band_offsets
+    m.band_offsets = lambda fam, h=0, d=0, lat=0: [0] if fam == m.MLA else orig(fam, h, d, lat)
+
+
+MUTANTS = [_mut_sign, _mut_cos_sin_swapped, _mut_pairing, _mut_theta_half, _mut_theta_shift,
+           _mut_theta_f32, _mut_patch_before_rotate, _mut_patch_rank_reversed, _mut_round_truncate,
+           _mut_round_double, _mut_page_no_slot0, _mut_v_rotated, _mut_mla_latent_band]
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__[5:])
+def test_pins_catch_planted_mistake(mutate):
+    m = _fresh_oracle()
+    mutate(m)
+    caught = []
+    for pin in ORACLE_PINS:
+        try:
+            pin(m)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {mutate.__name__}"
+
+
+# ---------------------------------------------------------------- tolerance predicate
+def test_tolerance_predicate():
+    y = np.array([1.0, -2.5, 3.0e-3, 100.0])
+    r = O.round_bf16(y)
+    S = np.abs(y)
+    assert tol.check_bf16(r, y, r, S, 8)["fail"] == 0
+    one_up = (r.astype(np.int64) + 1).astype(np.uint16)
+    assert tol.check_bf16(one_up, y, r, S, 8)["fail"] == 0          # one ulp away: P1
+    two_up = (r.astype(np.int64) + 2).astype(np.uint16)
+    assert tol.check_bf16(two_up, y, r, S, 8)["fail"] == 4          # two ulps, small S: both fail
+    # cancellation: |y| tiny next to S; an error within gamma_n*S passes through P2 only
+    y2 = np.array([1e-9]); S2 = np.array([4.0]); r2 = O.round_bf16(y2)
+    g2 = O.round_bf16(np.array([1e-9 + 5 * 4.0 * 2.0 ** -24]))
+    res = tol.check_bf16(g2, y2, r2, S2, 8)
+    assert res["fail"] == 0 and res["p2_only"] == 1
+    assert tol.bf16_ord(np.array([0x0000, 0x8000], np.uint16)).tolist() == [0, 0]
+    assert tol.bf16_ord(np.array([0x8001], np.uint16))[0] == -1
