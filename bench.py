@@ -1,0 +1,204 @@
+"""Throughput of the Kamera rehydrate operator on one MI355X.
+
+One step = one kamera_rehydrate_batched call over the whole workload (every
+chunk, every layer, K and V), inputs already resident in HBM. The default
+workload is the GQA vision-language-7B-like batch: 28 layers, 4 KV heads x
+128, bf16, 8 video segments of 1024 tokens with their own delta, rank-32
+patches on K and V.
+
+Prints one JSON line: whole-job tokens/s (rehydrated tokens per second of wall
+time), the dominant kernel's roofline figures measured with HIP events on the
+launch stream, and the fp64 CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rehydrated KV tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {
+    "C2": "GQA VL-7B-like: 28 layers, 4 KV heads x 128, bf16, 8 chunks x 1024 tokens, "
+          "per-chunk delta in [0,32768], rank-32 K and V patches",
+    "C3": "MLA V2-Lite-like: 27 layers, c_KV 512 + k_rope 64, bf16, 16 chunks x 1024 tokens, "
+          "rank-32 row and rope-band patches",
+    "C4": "MHA 7B reorder: 32 layers, 32 heads x 128, bf16, 6 orderings x 4 chunks x 2048 tokens, rank-32",
+    "C5": "GQA sliding-window deque: 36 layers, 8 KV heads x 128, bf16, 64 ragged chunks (48 in-place "
+          "survivors, 16 recalled with rank-32 patches) into a 16-token paged pool",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kamera_kernels.hip", "kamera_desc.h"):
+        with open(os.path.join(ROOT, "position_free_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{cfg}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+def _oracle_units(args):
+    """Worker: draw its (chunk, layer) inputs first, then time only the oracle on them."""
+    cfg, units = args
+    import torch
+    from threadpoolctl import threadpool_limits
+    torch.set_num_threads(1)          # one thread per worker process: no oversubscription
+    threadpool_limits(1)
+    import oracle.kamera_oracle as O
+    from tests.expect import oracle_factors
+    from workloads import make_workload
+    wl = make_workload(cfg)
+    lay = wl.layout
+    prepared = []
+    for ci, layer in units:
+        ch = wl.chunks[ci]
+        k = O.upcast(wl.canonical(ch.canon_id, layer, 0), lay.dtype)
+        v = O.upcast(wl.canonical(ch.canon_id, layer, 1), lay.dtype)
+        prepared.append((ch, k, v, oracle_factors(wl, ch, layer)))
+    t0 = time.perf_counter()
+    for ch, k, v, facs in prepared:
+        yk, yv = O.rehydrate_gqa(k, v, ch.delta, num_kv_heads=lay.num_kv_heads, head_dim=lay.head_dim,
+                                 base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched)
+        O.round_to(yk, lay.dtype)
+        O.round_to(yv, lay.dtype)
+    return time.perf_counter() - t0, len(prepared)
+
+
+def cpu_baseline(cfg: str, wl, sample_units: int):
+    import multiprocessing as mp
+    cores = max(1, min(16, os.cpu_count() or 1))
+    units = [(ci, layer) for ci in range(len(wl.chunks)) for layer in range(wl.layout.num_layers)][:sample_units]
+    parts = [(cfg, units[i::cores]) for i in range(cores) if units[i::cores]]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(len(parts)) as pool:
+        res = pool.map(_oracle_units, parts)
+    wall = max(r[0] for r in res)
+    n_units = sum(r[1] for r in res)
+    T = wl.chunks[0].num_tokens
+    tokens = n_units * T / wl.layout.num_layers     # a token is rehydrated once all its layers are done
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": len(parts), "kind": "oracle",
+            "sample": f"{n_units} (chunk, layer) units of {T} tokens (K and V, fp64, rounded to bf16) of the "
+                      f"{cfg} workload, spread over {len(parts)} processes; {wall:.1f} s wall, input drawing "
+                      f"excluded"}
+
+
+# ----------------------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-units", type=int, default=224, help="(chunk, layer) units timed on the CPU oracle")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
+                                   "several GPUs would each run their own share (see DESIGN.md); only --gpus 1 "
+                                   "is measured"}), flush=True)
+        return 2
+
+    from workloads import make_workload
+    wl = make_workload(args.config)
+    # The CPU oracle leg forks worker processes, so it runs before this process
+    # touches the GPU (forking a process whose HIP runtime threads are live can deadlock).
+    cpu = None
+    if not args.no_cpu and wl.layout.family == 0 and not any(c.in_place for c in wl.chunks):
+        t_cpu = time.perf_counter()
+        cpu = cpu_baseline(args.config, wl, args.cpu_units)
+        print(f"# cpu oracle leg done in {time.perf_counter() - t_cpu:.1f} s", file=sys.stderr, flush=True)
+
+    import torch
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+
+    torch.cuda.set_device(0)
+    abi.lib()
+    t_stage = time.perf_counter()
+    dw = DeviceWorkload(wl)
+    print(f"# staged {args.config} in {time.perf_counter() - t_stage:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        dw.run(stream)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # ---- whole calls (validation + descriptor upload + kernel): the step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        dw.run(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    call_ms_gpu = e0.elapsed_time(e1) / args.steps
+
+    # ---- the kernel alone: same batch, uploaded once, launched K times on the same stream
+    plan = dw.plan(stream)
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for _ in range(args.steps):
+        abi.plan_launch(plan, stream)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    kernel_us = e2.elapsed_time(e3) / args.steps * 1e3
+
+    ms_per_step = wall_s / args.steps * 1e3
+    tokens = wl.total_tokens
+    alg_bytes = dw.algorithmic_bytes()
+    achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.config)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) canonical KV, orthonormal factors with geometric spectra",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "chunks": len(wl.chunks),
+                   "tokens": tokens, "layers": wl.layout.num_layers, "row_width": wl.layout.row_width},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "kernel_us": kernel_us,
+        "call_us_gpu": call_ms_gpu * 1e3,
+        "algorithmic_bytes": alg_bytes,
+        "kernel_tokens_per_s": tokens / (kernel_us * 1e-6),
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+/*
+ * kamera.h - C ABI of the Kamera position-free KV reuse operator on AMD gfx950.
+ *
+ * The operator (Kamera preprint, "Kamera: Unified Position-Invariant Multimodal
+ * KV Cache for Training-Free Reuse", Eq. 1 in §1; stated cleanly as Eq. 1 in §2
+ * of the page's Dutch summary) rebuilds a cached chunk's KV at a new position:
+ *
+ *     KV^(B|A) = R(delta) . KV(B|empty) + U_m V_m^T
+ *
+ *   R(delta)   exact RoPE phase re-rotation of the stored keys' rotary band by
+ *              delta = p1 - p0 (preprint §3 "Relocate"); V and the MLA latent
+ *              c_KV are never rotated.
+ *   U_m V_m^T  rank-m conditioning patch, stored as U*Sigma [T][m] and
+ *              V^T [m][width] (preprint App. A compile listing; Fig. 2(d)),
+ *              added after the rotation (preprint App. A serve listing).
+ *
+ * Layout families (preprint §3, Fig. 2):
+ *   KAMERA_GQA  rows of K and of V, F = num_kv_heads * head_dim; every key head
+ *               is one rotary band of head_dim columns (MHA = GQA with one KV
+ *               head per query head). K and V may each carry factors.
+ *   KAMERA_MLA  one row per token, F = latent_dim + rope_dim: the latent c_KV
+ *               followed by the decoupled k_rope band, the only rotated part.
+ *               Factors may cover any column range of that row (the preprint
+ *               patches the latent and adds a small k_rope-band patch).
+ *
+ * Rotary convention: theta_i = rope_base^(-2i/d_rot), phi_i = delta * theta_i
+ * formed in fp64; a pair (a, b) becomes (a cos phi - b sin phi,
+ * a sin phi + b cos phi). NEOX pairs column i with i + d_rot/2 of the band,
+ * GPTJ pairs 2i with 2i+1. Arithmetic is fp32 (cos/sin rounded once from fp64,
+ * patch products accumulated in fp32); each output is rounded once to the
+ * storage dtype (bf16: round-to-nearest-even).
+ *
+ * Memory and ownership
+ *   - All tensor pointers are DEVICE pointers owned by the caller; element
+ *     type is the layout dtype; rows are contiguous (row stride F elements).
+ *   - Block tables and descriptor arrays are HOST memory, read only during the
+ *     call; they may be freed or reused as soon as the call returns.
+ *   - The caller supplies a device workspace of at least
+ *     kamera_workspace_bytes(...) bytes; the library copies the packed batch
+ *     description there (stream-ordered). The workspace must not be reused
+ *     by another call until the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL: the null stream). Work is enqueued
+ *     asynchronously; nothing is synchronised.
+ *   - The library never allocates device memory. It keeps a small ring of
+ *     pinned host staging buffers per device for the descriptor upload.
+ *
+ * Errors
+ *   Every entry point returns a kamera_status. Arguments are validated on the
+ *   host before anything is enqueued; on any error nothing is enqueued and
+ *   kamera_last_error() (thread-local) describes the first problem found.
+ *   KAMERA_E_HIP reports a failed HIP call (launch, copy). Faults inside a
+ *   kernel surface on the stream like any other HIP error.
+ */
+#ifndef KAMERA_H_
+#define KAMERA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kamera_status {
+  KAMERA_OK = 0,
+  KAMERA_E_NULL = 1,        /* a required pointer is NULL                               */
+  KAMERA_E_SHAPE = 2,       /* a dimension, count or stride is out of range              */
+  KAMERA_E_DTYPE = 3,       /* unknown dtype                                             */
+  KAMERA_E_RANK = 4,        /* patch rank out of range for this layout                   */
+  KAMERA_E_DELTA = 5,       /* |delta| >= 2^31                                           */
+  KAMERA_E_PAGE = 6,        /* page id outside [0, num_pages) or slot0 outside the page  */
+  KAMERA_E_OVERLAP = 7,     /* two chunks of one batch write the same pool slot          */
+  KAMERA_E_ALIGN = 8,       /* a pointer is not aligned to its element size              */
+  KAMERA_E_WORKSPACE = 9,   /* workspace NULL or smaller than kamera_workspace_bytes()   */
+  KAMERA_E_UNSUPPORTED = 10,/* unknown family/pairing/flag, or a layout not supported    */
+  KAMERA_E_HIP = 11         /* a HIP runtime call failed                                 */
+} kamera_status;
+
+enum { KAMERA_GQA = 0, KAMERA_MLA = 1 };
+enum { KAMERA_F32 = 0, KAMERA_BF16 = 1 };
+enum { KAMERA_NEOX = 0, KAMERA_GPTJ = 1 };
+
+/* chunk flags */
+enum {
+  KAMERA_PATCH = 1u,     /* add the chunk's factors (else rotation only; V, c_KV copied as stored) */
+  KAMERA_IN_PLACE = 2u   /* read the rows from the destination itself and write them back       */
+};
+
+enum { KAMERA_MAX_FACTORS = 4, KAMERA_MAX_RANK = 256 };
+
+typedef struct kamera_layout {
+  int32_t family;        /* KAMERA_GQA or KAMERA_MLA                                      */
+  int32_t dtype;         /* KAMERA_BF16 or KAMERA_F32 (all tensors of a call share it)    */
+  int32_t num_layers;    /* L >= 1                                                        */
+  int32_t num_kv_heads;  /* GQA: H_kv >= 1                                                */
+  int32_t head_dim;      /* GQA: even, >= 2; the rotary band is the whole head            */
+  int32_t latent_dim;    /* MLA: c_KV width >= 0                                          */
+  int32_t rope_dim;      /* MLA: k_rope width, even, >= 2                                 */
+  int32_t pairing;       /* KAMERA_NEOX or KAMERA_GPTJ                                    */
+  int32_t page_size;     /* tokens per pool page (>= 1); used by paged destinations       */
+  int32_t reserved;      /* must be 0                                                     */
+  double rope_base;      /* RoPE base (> 0, finite), e.g. 1e4 or 1e6                      */
+} kamera_layout;
+
+/* One stored factor pair of a chunk (preprint App. A: U[:, :m]*S[:m], Vt[:m]). */
+typedef struct kamera_factor {
+  const void* u;         /* device [L - layer0][T][rank]: U*Sigma, row-major               */
+  const void* vt;        /* device [L - layer0][rank][width]: V^T, row-major               */
+  int32_t tensor;        /* 0: K (GQA) or the MLA row; 1: V (GQA only)                     */
+  int32_t col0;          /* first patched column of that tensor's row                     */
+  int32_t width;         /* patched columns [col0, col0 + width), within the row          */
+  int32_t rank;          /* m, 0 <= m <= KAMERA_MAX_RANK (0: no-op)                        */
+  int32_t layer0;        /* layers below layer0 carry no factor (layer-sparse patches)    */
+  int32_t reserved;      /* must be 0                                                     */
+} kamera_factor;
+
+/* One chunk to relocate/rehydrate across all L layers. */
+typedef struct kamera_chunk {
+  int32_t num_tokens;          /* T >= 0 (0: nothing to do)                                   */
+  uint32_t flags;              /* KAMERA_PATCH | KAMERA_IN_PLACE                              */
+  int64_t delta;               /* signed position shift p1 - p0, |delta| < 2^31              */
+  const void* k_src;           /* device [L][T][F] canonical K (MLA: the row); unused in place */
+  const void* v_src;           /* device [L][T][F] canonical V (GQA); unused for MLA/in place */
+  int64_t src_layer_stride;    /* elements between layers of k_src/v_src; 0 means T*F          */
+  void* k_dst;                 /* dense destination [L][T][F] when block_table == NULL         */
+  void* v_dst;                 /* (GQA only)                                                   */
+  int64_t dst_layer_stride;    /* elements between layers of k_dst/v_dst; 0 means T*F          */
+  const int32_t* block_table;  /* HOST page ids; token t lives at slot s = slot0 + t, page
+                                  block_table[s / page_size], offset s % page_size of the pool;
+                                  NULL selects the dense destination                          */
+  int32_t slot0;               /* 0 <= slot0 < page_size                                       */
+  int32_t num_factors;         /* 0 .. KAMERA_MAX_FACTORS                                      */
+  kamera_factor factors[KAMERA_MAX_FACTORS];
+} kamera_chunk;
+
+/* Paged KV pool (preprint §6: the rebuilt KV is written into the engine's pool). */
+typedef struct kamera_pool {
+  void* k_pool;            /* device [L][num_pages][page_size][F] (MLA: the rows)          */
+  void* v_pool;            /* device, same shape (GQA only)                                 */
+  int32_t num_pages;       /* pages per layer                                              */
+  int32_t reserved;        /* must be 0                                                    */
+  int64_t layer_stride;    /* elements between layers; 0 means num_pages*page_size*F       */
+} kamera_pool;
+
+/* Launch summary produced by kamera_plan_upload and consumed by kamera_plan_launch. */
+typedef struct kamera_plan {
+  void* workspace;         /* device workspace holding the packed batch                    */
+  int64_t num_tasks;       /* wave tasks of the main kernel (0: nothing to launch)         */
+  int32_t kernel;          /* 0 none, 1 MFMA bf16 path, 2 generic VALU path                */
+  int32_t variant;         /* register-budget instantiation of the chosen kernel           */
+  int32_t num_chunks;
+  int32_t reserved[9];
+} kamera_plan;
+
+/* Bytes of device workspace needed for a batch of `num_chunks` chunks whose block
+ * tables hold `total_block_table_entries` page ids in total. */
+size_t kamera_workspace_bytes(int32_t num_chunks, int64_t total_block_table_entries);
+
+/* Rotation-only relocation in place (preprint §5: sliding-window survivors need only
+ * R(delta)): rotates the K rotary bands (GQA) or the k_rope band (MLA) of tokens
+ * [0, num_tokens) stored in `pool`; V and c_KV are neither read nor written.
+ * block_table (HOST) maps slots as in kamera_chunk; NULL maps slot s to pool row s
+ * (page s / page_size, offset s % page_size), i.e. the pool as dense rows. */
+kamera_status kamera_relocate(const kamera_layout* layout, const kamera_pool* pool,
+                              const int32_t* block_table, int32_t slot0, int32_t num_tokens,
+                              int64_t delta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Eq. 1 for one chunk across all layers (preprint App. A serve listing). */
+kamera_status kamera_rehydrate(const kamera_layout* layout, const kamera_chunk* chunk,
+                               const kamera_pool* pool, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Eq. 1 for a batch of chunks in one launch: each chunk has its own delta, patch flag,
+ * factors and destination (dense rows, or pages of `pool`). Pool slots written by two
+ * chunks of one batch are rejected (KAMERA_E_OVERLAP); dense destinations are the
+ * caller's to keep disjoint. `pool` may be NULL when no chunk uses a block table. */
+kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera_chunk* chunks,
+                                       int32_t num_chunks, const kamera_pool* pool,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split form of kamera_rehydrate_batched: validate and upload the batch once, then
+ * launch it any number of times (for example from a captured graph). The plan stays
+ * valid while the workspace and every pointer it references are untouched. */
+kamera_status kamera_plan_upload(const kamera_layout* layout, const kamera_chunk* chunks,
+                                 int32_t num_chunks, const kamera_pool* pool, void* workspace,
+                                 size_t workspace_bytes, void* stream, kamera_plan* plan);
+kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kamera_status_string(kamera_status status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* kamera_last_error(void);
+/* Library version string. */
+const char* kamera_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAMERA_H_ */

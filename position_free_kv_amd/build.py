@@ -1,0 +1,60 @@
+"""Build libkamera.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m position_free_kv_amd.build
+
+The library is the C ABI of include/kamera.h: host validation and packing
+(csrc/kamera_host.cpp) plus the gfx950 kernels (csrc/kamera_kernels.hip).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libkamera.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = os.environ.get("KAMERA_OFFLOAD_ARCH", "gfx950")
+
+# Packed fp32 VALU forms stay disabled: plain fp32 code only.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose_asm: bool = False) -> str:
+    cc = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    kobj = os.path.join(objdir, "kamera_kernels.o")
+    hobj = os.path.join(objdir, "kamera_host.o")
+    _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
+          os.path.join(CSRC, "kamera_kernels.hip"), "-o", kobj])
+    _run([cc, "-x", "c++", *COMMON, "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-c",
+          os.path.join(CSRC, "kamera_host.cpp"), "-o", hobj])
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose_asm:
+        _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "--cuda-device-only", "-S",
+              os.path.join(CSRC, "kamera_kernels.hip"), "-o", os.path.join(objdir, "kamera_kernels.s")])
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose_asm="--asm" in sys.argv)

@@ -1,0 +1,79 @@
+// Internal packed batch description shared by the host packer and the kernels.
+// Not part of the public ABI (include/kamera.h is).
+#pragma once
+
+#include <stdint.h>
+
+namespace kamera {
+
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
+constexpr int kSlab = 64;          // columns per slab of the MFMA path
+constexpr int kTileTokens = 16;    // tokens per MFMA tile (the N dimension)
+constexpr int kMaxFactors = 4;
+
+// MFMA path: per-wave register budget of (slab x k-step) operand sets.
+// Variant v holds up to kBudget[v] sets of 8 bf16 x 4 tiles per lane.
+constexpr int kNumVariants = 3;
+constexpr int kBudget[kNumVariants] = {2, 4, 8};
+
+struct alignas(16) DevFactor {
+  const void* u;        // [L - layer0][T][rank]
+  const void* vt;       // [L - layer0][rank][width]
+  int32_t tensor;
+  int32_t col0;
+  int32_t width;
+  int32_t rank;
+  int32_t layer0;
+  int32_t pad[3];
+};
+static_assert(sizeof(DevFactor) == 48, "DevFactor layout");
+
+// Per-chunk record. Task space of a chunk (both kernels):
+//   task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+// stream indexes the tensors this chunk touches (stream_tensor[]), tb the token
+// block, g the column group (MFMA path: head or slab; generic path: unused = 1).
+struct alignas(16) DevChunk {
+  const void* src[2];   // per tensor: first source row of layer 0 (in place: == dst)
+  void* dst[2];         // per tensor: dense destination, or pool base (paged)
+  int64_t src_ls;       // elements between layers (source)
+  int64_t dst_ls;       // elements between layers (destination / pool)
+  int64_t delta;
+  const int32_t* pages; // device copy of the block table (NULL: dense destination)
+  int64_t task0;        // first task id of this chunk
+  int32_t T;
+  uint32_t flags;
+  int32_t slot0;
+  int32_t nfac;
+  int32_t ntb;          // token blocks
+  int32_t tb_tokens;    // tokens per block
+  int32_t nstreams;     // tensors touched (1 or 2)
+  int32_t ngroups;      // column groups per tensor (MFMA path)
+  int32_t group0;       // first group id (MLA in-place rotation touches only the rope group)
+  int32_t stream_tensor[2];
+  int32_t pad;
+  DevFactor fac[kMaxFactors];
+};
+
+struct alignas(16) DevHeader {
+  int64_t total_tasks;
+  int32_t nchunks;
+  int32_t family;
+  int32_t dtype;
+  int32_t L;
+  int32_t F;            // row width
+  int32_t H;            // GQA heads
+  int32_t head_dim;
+  int32_t latent_dim;
+  int32_t rope_dim;
+  int32_t d_rot;        // rotary band width
+  int32_t pairing;
+  int32_t page_size;
+  int32_t group_cols;   // MFMA path: columns per group (64 or 128)
+  int32_t rope_group;   // MFMA path, MLA: group id of the rope band (-1 for GQA)
+  double rope_base;
+  int32_t pad[2];
+};
+
+}  // namespace kamera

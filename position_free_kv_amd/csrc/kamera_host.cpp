@@ -1,0 +1,527 @@
+// Host side of the Kamera C ABI (include/kamera.h): argument validation, batch
+// packing, the stream-ordered descriptor upload and kernel selection/launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kamera.h"
+#include "kamera_desc.h"
+
+namespace kamera {
+hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
+                       hipStream_t stream);
+hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
+                          hipStream_t stream);
+}  // namespace kamera
+
+using namespace kamera;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kamera_status fail(kamera_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t ws_bytes(int64_t nchunks, int64_t pages) {
+  return round_up(sizeof(DevHeader), kAlign) + round_up((size_t)nchunks * sizeof(DevChunk), kAlign) +
+         round_up((size_t)pages * sizeof(int32_t), kAlign);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ------------------------------------------------------------------ staging ring
+// Pinned host buffers used as the source of the stream-ordered descriptor copy.
+// A slot is reused only after the copy that last read it has completed.
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+constexpr int kSlots = 8;
+constexpr int kMaxDevices = 64;
+struct Ring {
+  std::mutex mu;
+  Slot slot[kSlots];
+  int next = 0;
+};
+Ring g_ring[kMaxDevices];
+
+kamera_status upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(KAMERA_E_HIP, "hipGetDevice failed");
+  Ring& ring = g_ring[dev];
+  std::lock_guard<std::mutex> lock(ring.mu);
+  Slot& s = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % kSlots;
+  if (s.pending) {
+    if (hipEventSynchronize(s.done) != hipSuccess) return fail(KAMERA_E_HIP, "hipEventSynchronize failed");
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max(round_up(bytes, 64 * 1024), (size_t)64 * 1024);
+    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(KAMERA_E_HIP, "hipHostMalloc(%zu) failed", cap);
+    s.cap = cap;
+  }
+  if (!s.done && hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess)
+    return fail(KAMERA_E_HIP, "hipEventCreate failed");
+  std::memcpy(s.host, src, bytes);
+  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return fail(KAMERA_E_HIP, "hipMemcpyAsync of %zu descriptor bytes failed", bytes);
+  if (hipEventRecord(s.done, stream) != hipSuccess) return fail(KAMERA_E_HIP, "hipEventRecord failed");
+  s.pending = true;
+  return KAMERA_OK;
+}
+
+// ------------------------------------------------------------------ validation
+kamera_status check_layout(const kamera_layout* L) {
+  if (!L) return fail(KAMERA_E_NULL, "layout is NULL");
+  if (L->family != KAMERA_GQA && L->family != KAMERA_MLA)
+    return fail(KAMERA_E_UNSUPPORTED, "unknown family %d", L->family);
+  if (L->dtype != KAMERA_BF16 && L->dtype != KAMERA_F32) return fail(KAMERA_E_DTYPE, "unknown dtype %d", L->dtype);
+  if (L->num_layers < 1) return fail(KAMERA_E_SHAPE, "num_layers must be >= 1 (got %d)", L->num_layers);
+  if (L->pairing != KAMERA_NEOX && L->pairing != KAMERA_GPTJ)
+    return fail(KAMERA_E_UNSUPPORTED, "unknown pairing %d", L->pairing);
+  if (L->page_size < 1) return fail(KAMERA_E_SHAPE, "page_size must be >= 1 (got %d)", L->page_size);
+  if (L->reserved != 0) return fail(KAMERA_E_SHAPE, "layout.reserved must be 0");
+  if (!(L->rope_base > 0.0) || !std::isfinite(L->rope_base))
+    return fail(KAMERA_E_SHAPE, "rope_base must be positive and finite");
+  if (L->family == KAMERA_GQA) {
+    if (L->num_kv_heads < 1) return fail(KAMERA_E_SHAPE, "num_kv_heads must be >= 1");
+    if (L->head_dim < 2 || L->head_dim % 2 || L->head_dim > 512)
+      return fail(KAMERA_E_SHAPE, "head_dim must be even in [2, 512] (got %d)", L->head_dim);
+    if ((int64_t)L->num_kv_heads * L->head_dim > (1 << 20)) return fail(KAMERA_E_SHAPE, "row too wide");
+  } else {
+    if (L->latent_dim < 0) return fail(KAMERA_E_SHAPE, "latent_dim must be >= 0");
+    if (L->rope_dim < 2 || L->rope_dim % 2 || L->rope_dim > 512)
+      return fail(KAMERA_E_SHAPE, "rope_dim must be even in [2, 512] (got %d)", L->rope_dim);
+    if ((int64_t)L->latent_dim + L->rope_dim > (1 << 20)) return fail(KAMERA_E_SHAPE, "row too wide");
+  }
+  return KAMERA_OK;
+}
+
+int row_width(const kamera_layout* L) {
+  return L->family == KAMERA_GQA ? L->num_kv_heads * L->head_dim : L->latent_dim + L->rope_dim;
+}
+
+struct Packed {
+  std::vector<unsigned char> blob;  // header | chunks | pages
+  std::vector<int64_t> page_off;    // per chunk: offset (entries) of its page table, -1 if dense
+  size_t bytes = 0;
+  int64_t tasks = 0;
+  int kernel = 0;   // 0 none, 1 mfma, 2 generic
+  int variant = 0;
+};
+
+// Is the bf16 MFMA kernel able to run this layout at all?
+bool mfma_layout_ok(const kamera_layout* L) {
+  if (L->dtype != KAMERA_BF16) return false;
+  if (L->family == KAMERA_GQA) return L->head_dim == 64 || L->head_dim == 128;
+  return L->latent_dim % kSlab == 0 && L->rope_dim == kSlab;
+}
+
+kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
+                         Packed& out) {
+  kamera_status st = check_layout(L);
+  if (st != KAMERA_OK) return st;
+  if (n < 0) return fail(KAMERA_E_SHAPE, "num_chunks must be >= 0");
+  if (n > 0 && !chunks) return fail(KAMERA_E_NULL, "chunks is NULL");
+  const int F = row_width(L);
+  const int P = L->page_size;
+  const size_t es = L->dtype == KAMERA_BF16 ? 2 : 4;
+  const int ntensors = L->family == KAMERA_GQA ? 2 : 1;
+  const int d_rot = L->family == KAMERA_GQA ? L->head_dim : L->rope_dim;
+
+  bool any_paged = false;
+  int64_t total_pages = 0;
+  for (int i = 0; i < n; ++i)
+    if (chunks[i].block_table && chunks[i].num_tokens > 0) {
+      any_paged = true;
+      total_pages += (chunks[i].slot0 + (int64_t)chunks[i].num_tokens + P - 1) / P;
+    }
+  if (any_paged) {
+    if (!pool) return fail(KAMERA_E_NULL, "a chunk has a block table but pool is NULL");
+    if (pool->num_pages < 1) return fail(KAMERA_E_SHAPE, "pool.num_pages must be >= 1");
+    if (pool->reserved != 0) return fail(KAMERA_E_SHAPE, "pool.reserved must be 0");
+    if (!pool->k_pool) return fail(KAMERA_E_NULL, "pool.k_pool is NULL");
+    if (!aligned(pool->k_pool, es) || (pool->v_pool && !aligned(pool->v_pool, es)))
+      return fail(KAMERA_E_ALIGN, "pool pointers must be aligned to %zu bytes", es);
+    if (pool->layer_stride < 0) return fail(KAMERA_E_SHAPE, "pool.layer_stride must be >= 0");
+    const int64_t min_ls = (int64_t)pool->num_pages * P * F;
+    if (pool->layer_stride != 0 && pool->layer_stride < min_ls)
+      return fail(KAMERA_E_SHAPE, "pool.layer_stride %lld smaller than one layer (%lld)",
+                  (long long)pool->layer_stride, (long long)min_ls);
+  }
+
+  // -------------------------------------------------------------- per-chunk checks
+  bool mfma = mfma_layout_ok(L);
+  int need_budget = 0;
+  std::vector<uint8_t> slot_used;
+  if (any_paged) slot_used.assign((size_t)pool->num_pages * P, 0);
+
+  for (int i = 0; i < n; ++i) {
+    const kamera_chunk& c = chunks[i];
+    if (c.num_tokens < 0) return fail(KAMERA_E_SHAPE, "chunk %d: num_tokens < 0", i);
+    if (c.flags & ~(uint32_t)(KAMERA_PATCH | KAMERA_IN_PLACE))
+      return fail(KAMERA_E_UNSUPPORTED, "chunk %d: unknown flag bits 0x%x", i, c.flags);
+    if (c.delta <= -(int64_t(1) << 31) || c.delta >= (int64_t(1) << 31))
+      return fail(KAMERA_E_DELTA, "chunk %d: |delta| must be < 2^31", i);
+    if (c.num_factors < 0 || c.num_factors > KAMERA_MAX_FACTORS)
+      return fail(KAMERA_E_SHAPE, "chunk %d: num_factors must be in [0, %d]", i, KAMERA_MAX_FACTORS);
+    if (c.num_tokens == 0) continue;
+    const bool in_place = c.flags & KAMERA_IN_PLACE;
+    const bool patch = c.flags & KAMERA_PATCH;
+    const bool paged = c.block_table != nullptr;
+    const int64_t T = c.num_tokens;
+    // sources
+    if (!in_place) {
+      if (!c.k_src || (ntensors == 2 && !c.v_src)) return fail(KAMERA_E_NULL, "chunk %d: source pointer is NULL", i);
+      if (!aligned(c.k_src, es) || (c.v_src && !aligned(c.v_src, es)))
+        return fail(KAMERA_E_ALIGN, "chunk %d: source pointers must be aligned to %zu bytes", i, es);
+      if (c.src_layer_stride < 0 || (c.src_layer_stride != 0 && c.src_layer_stride < T * F))
+        return fail(KAMERA_E_SHAPE, "chunk %d: src_layer_stride smaller than T*F", i);
+      if (mfma && (!aligned(c.k_src, 16) || (c.v_src && !aligned(c.v_src, 16)) || c.src_layer_stride % 8))
+        mfma = false;
+    }
+    // destination
+    const bool touches_v = ntensors == 2 && !(in_place && !patch);
+    if (paged) {
+      if (touches_v && !pool->v_pool) return fail(KAMERA_E_NULL, "chunk %d: pool.v_pool is NULL", i);
+      if (c.slot0 < 0 || c.slot0 >= P) return fail(KAMERA_E_PAGE, "chunk %d: slot0 must be in [0, page_size)", i);
+      const int64_t np = (c.slot0 + T + P - 1) / P;
+      for (int64_t k = 0; k < np; ++k) {
+        const int32_t pg = c.block_table[k];
+        if (pg < 0 || pg >= pool->num_pages)
+          return fail(KAMERA_E_PAGE, "chunk %d: block_table[%lld] = %d outside [0, %d)", i, (long long)k, pg,
+                      pool->num_pages);
+      }
+      for (int64_t t = 0; t < T; ++t) {
+        const int64_t s = c.slot0 + t;
+        const size_t slot = (size_t)c.block_table[s / P] * P + (size_t)(s % P);
+        if (slot_used[slot])
+          return fail(KAMERA_E_OVERLAP, "chunk %d token %lld: pool page %d offset %lld already written in this batch",
+                      i, (long long)t, c.block_table[s / P], (long long)(s % P));
+        slot_used[slot] = 1;
+      }
+      if (mfma && (!aligned(pool->k_pool, 16) || (pool->v_pool && !aligned(pool->v_pool, 16)) ||
+                   pool->layer_stride % 8))
+        mfma = false;
+    } else {
+      if (!c.k_dst || (touches_v && !c.v_dst))
+        return fail(KAMERA_E_NULL, "chunk %d: destination pointer is NULL", i);
+      if (!aligned(c.k_dst, es) || (c.v_dst && !aligned(c.v_dst, es)))
+        return fail(KAMERA_E_ALIGN, "chunk %d: destination pointers must be aligned to %zu bytes", i, es);
+      if (c.dst_layer_stride < 0 || (c.dst_layer_stride != 0 && c.dst_layer_stride < T * F))
+        return fail(KAMERA_E_SHAPE, "chunk %d: dst_layer_stride smaller than T*F", i);
+      if (mfma && (!aligned(c.k_dst, 16) || (c.v_dst && !aligned(c.v_dst, 16)) || c.dst_layer_stride % 8))
+        mfma = false;
+    }
+    // factors
+    if (patch) {
+      for (int f = 0; f < c.num_factors; ++f) {
+        const kamera_factor& fa = c.factors[f];
+        if (fa.reserved != 0) return fail(KAMERA_E_SHAPE, "chunk %d factor %d: reserved must be 0", i, f);
+        if (fa.tensor < 0 || fa.tensor >= ntensors)
+          return fail(KAMERA_E_SHAPE, "chunk %d factor %d: tensor %d invalid for this family", i, f, fa.tensor);
+        if (fa.rank < 0 || fa.rank > KAMERA_MAX_RANK)
+          return fail(KAMERA_E_RANK, "chunk %d factor %d: rank %d outside [0, %d]", i, f, fa.rank, KAMERA_MAX_RANK);
+        if (fa.rank == 0) continue;
+        if (fa.col0 < 0 || fa.width < 1 || (int64_t)fa.col0 + fa.width > F)
+          return fail(KAMERA_E_SHAPE, "chunk %d factor %d: columns [%d, %d) outside the row of %d", i, f, fa.col0,
+                      fa.col0 + fa.width, F);
+        if (fa.layer0 < 0 || fa.layer0 >= L->num_layers)
+          return fail(KAMERA_E_SHAPE, "chunk %d factor %d: layer0 outside [0, L)", i, f);
+        if (!fa.u || !fa.vt) return fail(KAMERA_E_NULL, "chunk %d factor %d: u or vt is NULL", i, f);
+        if (!aligned(fa.u, es) || !aligned(fa.vt, es))
+          return fail(KAMERA_E_ALIGN, "chunk %d factor %d: factor pointers must be aligned to %zu bytes", i, f, es);
+      }
+      // MFMA register budget: slabs per group x k-steps of the factors covering it
+      if (mfma) {
+        const int gcols = L->family == KAMERA_GQA ? L->head_dim : kSlab;
+        const int ngroups = F / gcols;
+        for (int t = 0; t < ntensors; ++t)
+          for (int g = 0; g < ngroups; ++g) {
+            int ks = 0;
+            for (int f = 0; f < c.num_factors; ++f) {
+              const kamera_factor& fa = c.factors[f];
+              if (fa.rank == 0 || fa.tensor != t || fa.col0 >= (g + 1) * gcols || fa.col0 + fa.width <= g * gcols)
+                continue;
+              ks += (fa.rank + 31) / 32;
+            }
+            need_budget = std::max(need_budget, ks * (gcols / kSlab));
+          }
+      }
+    }
+  }
+  if (mfma && need_budget > kBudget[kNumVariants - 1]) mfma = false;
+
+  // -------------------------------------------------------------- pack
+  out.bytes = ws_bytes(n, total_pages);
+  out.blob.assign(out.bytes, 0);
+  DevHeader* hd = reinterpret_cast<DevHeader*>(out.blob.data());
+  DevChunk* dc = reinterpret_cast<DevChunk*>(out.blob.data() + round_up(sizeof(DevHeader), kAlign));
+  int32_t* pg = reinterpret_cast<int32_t*>(out.blob.data() + round_up(sizeof(DevHeader), kAlign) +
+                                           round_up((size_t)n * sizeof(DevChunk), kAlign));
+  hd->nchunks = n;
+  hd->family = L->family;
+  hd->dtype = L->dtype;
+  hd->L = L->num_layers;
+  hd->F = F;
+  hd->H = L->family == KAMERA_GQA ? L->num_kv_heads : 0;
+  hd->head_dim = L->head_dim;
+  hd->latent_dim = L->latent_dim;
+  hd->rope_dim = L->rope_dim;
+  hd->d_rot = d_rot;
+  hd->pairing = L->pairing;
+  hd->page_size = P;
+  hd->rope_base = L->rope_base;
+  hd->group_cols = mfma ? (L->family == KAMERA_GQA ? L->head_dim : kSlab) : F;
+  hd->rope_group = (mfma && L->family == KAMERA_MLA) ? L->latent_dim / kSlab : -1;
+
+  const int tb_tokens = mfma ? 128 : 16;
+  int64_t task = 0;
+  int64_t page_cursor = 0;
+  out.page_off.assign((size_t)n, -1);
+  const int64_t pool_ls = (any_paged && pool->layer_stride == 0) ? (int64_t)pool->num_pages * P * F
+                                                                 : (pool ? pool->layer_stride : 0);
+  for (int i = 0; i < n; ++i) {
+    const kamera_chunk& c = chunks[i];
+    DevChunk& d = dc[i];
+    d.task0 = task;
+    d.T = c.num_tokens;
+    d.flags = c.flags;
+    d.delta = c.delta;
+    d.slot0 = c.slot0;
+    if (c.num_tokens == 0) continue;
+    const bool in_place = c.flags & KAMERA_IN_PLACE;
+    const bool patch = c.flags & KAMERA_PATCH;
+    const bool paged = c.block_table != nullptr;
+    const int64_t T = c.num_tokens;
+    if (paged) {
+      const int64_t np = (c.slot0 + T + P - 1) / P;
+      std::memcpy(pg + page_cursor, c.block_table, (size_t)np * sizeof(int32_t));
+      out.page_off[(size_t)i] = page_cursor;  // turned into a device address once the workspace is known
+      page_cursor += np;
+      d.dst[0] = pool->k_pool;
+      d.dst[1] = pool->v_pool;
+      d.dst_ls = pool_ls;
+    } else {
+      d.pages = nullptr;
+      d.dst[0] = c.k_dst;
+      d.dst[1] = c.v_dst;
+      d.dst_ls = c.dst_layer_stride ? c.dst_layer_stride : T * F;
+    }
+    if (in_place) {
+      d.src[0] = d.dst[0];
+      d.src[1] = d.dst[1];
+      d.src_ls = d.dst_ls;
+    } else {
+      d.src[0] = c.k_src;
+      d.src[1] = c.v_src;
+      d.src_ls = c.src_layer_stride ? c.src_layer_stride : T * F;
+    }
+    d.nfac = patch ? c.num_factors : 0;
+    bool v_factor = false;
+    for (int f = 0; f < d.nfac; ++f) {
+      const kamera_factor& fa = c.factors[f];
+      DevFactor& df = d.fac[f];
+      df.u = fa.u;
+      df.vt = fa.vt;
+      df.tensor = fa.tensor;
+      df.col0 = fa.col0;
+      df.width = fa.width;
+      df.rank = fa.rank;
+      df.layer0 = fa.layer0;
+      df.pad[0] = (fa.rank % 8 == 0 && aligned(fa.u, 16)) ? 1 : 0;
+      if (fa.tensor == 1 && fa.rank > 0) v_factor = true;
+    }
+    // streams: tensors this chunk touches
+    if (L->family == KAMERA_GQA) {
+      d.stream_tensor[0] = 0;
+      d.stream_tensor[1] = 1;
+      d.nstreams = (in_place && !(patch && v_factor)) ? 1 : 2;
+    } else {
+      d.stream_tensor[0] = 0;
+      d.stream_tensor[1] = 0;
+      d.nstreams = 1;
+    }
+    d.tb_tokens = tb_tokens;
+    d.ntb = (int32_t)((T + tb_tokens - 1) / tb_tokens);
+    if (mfma) {
+      const int ngroups = F / hd->group_cols;
+      if (L->family == KAMERA_MLA && in_place && !patch) {
+        d.group0 = hd->rope_group;
+        d.ngroups = 1;
+      } else {
+        d.group0 = 0;
+        d.ngroups = ngroups;
+      }
+    } else {
+      d.group0 = 0;
+      d.ngroups = 1;
+    }
+    task += (int64_t)d.nstreams * L->num_layers * d.ntb * d.ngroups;
+  }
+  hd->total_tasks = task;
+  out.tasks = task;
+  out.kernel = task == 0 ? 0 : (mfma ? 1 : 2);
+  out.variant = 0;
+  if (mfma)
+    while (out.variant < kNumVariants - 1 && kBudget[out.variant] < need_budget) ++out.variant;
+  return KAMERA_OK;
+}
+
+kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
+                          void* ws, size_t ws_size, void* stream, kamera_plan* plan) {
+  Packed pk;
+  kamera_status st = pack_batch(L, chunks, n, pool, pk);
+  if (st != KAMERA_OK) return st;
+  if (!ws) return fail(KAMERA_E_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(KAMERA_E_ALIGN, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_size < pk.bytes) return fail(KAMERA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_size, pk.bytes);
+  // turn page-table offsets into device addresses inside the workspace
+  const size_t pages_off = round_up(sizeof(DevHeader), kAlign) + round_up((size_t)n * sizeof(DevChunk), kAlign);
+  DevChunk* dc = reinterpret_cast<DevChunk*>(pk.blob.data() + round_up(sizeof(DevHeader), kAlign));
+  for (int i = 0; i < n; ++i)
+    dc[i].pages = pk.page_off[(size_t)i] < 0
+                      ? nullptr
+                      : reinterpret_cast<const int32_t*>((char*)ws + pages_off +
+                                                         (size_t)pk.page_off[(size_t)i] * sizeof(int32_t));
+  if (pk.tasks > 0) {
+    st = upload(pk.blob.data(), pk.bytes, ws, (hipStream_t)stream);
+    if (st != KAMERA_OK) return st;
+  }
+  std::memset(plan, 0, sizeof(*plan));
+  plan->workspace = ws;
+  plan->num_tasks = pk.tasks;
+  plan->kernel = pk.kernel;
+  plan->variant = pk.variant;
+  plan->num_chunks = n;
+  plan->reserved[0] = L->dtype;
+  return KAMERA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kamera_workspace_bytes(int32_t num_chunks, int64_t total_block_table_entries) {
+  if (num_chunks < 0 || total_block_table_entries < 0) return 0;
+  return ws_bytes(num_chunks, total_block_table_entries);
+}
+
+kamera_status kamera_plan_upload(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks,
+                                 const kamera_pool* pool, void* workspace, size_t workspace_bytes, void* stream,
+                                 kamera_plan* plan) {
+  g_last_error.clear();
+  if (!plan) return fail(KAMERA_E_NULL, "plan is NULL");
+  return upload_plan(layout, chunks, num_chunks, pool, workspace, workspace_bytes, stream, plan);
+}
+
+kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(KAMERA_E_NULL, "plan is NULL");
+  if (plan->num_tasks <= 0 || plan->kernel == 0) return KAMERA_OK;
+  if (!plan->workspace) return fail(KAMERA_E_WORKSPACE, "plan has no workspace");
+  const DevHeader* hd = reinterpret_cast<const DevHeader*>(plan->workspace);
+  const DevChunk* dc = reinterpret_cast<const DevChunk*>((const char*)plan->workspace +
+                                                         round_up(sizeof(DevHeader), kAlign));
+  hipError_t e;
+  if (plan->kernel == 1) e = launch_mfma(plan->variant, hd, dc, plan->num_tasks, (hipStream_t)stream);
+  else if (plan->kernel == 2) e = launch_generic(plan->reserved[0], hd, dc, plan->num_tasks, (hipStream_t)stream);
+  else return fail(KAMERA_E_UNSUPPORTED, "plan names unknown kernel %d", plan->kernel);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks,
+                                       const kamera_pool* pool, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  kamera_plan plan;
+  kamera_status st = kamera_plan_upload(layout, chunks, num_chunks, pool, workspace, workspace_bytes, stream, &plan);
+  if (st != KAMERA_OK) return st;
+  return kamera_plan_launch(&plan, stream);
+}
+
+kamera_status kamera_rehydrate(const kamera_layout* layout, const kamera_chunk* chunk, const kamera_pool* pool,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!chunk) return fail(KAMERA_E_NULL, "chunk is NULL");
+  return kamera_rehydrate_batched(layout, chunk, 1, pool, workspace, workspace_bytes, stream);
+}
+
+kamera_status kamera_relocate(const kamera_layout* layout, const kamera_pool* pool, const int32_t* block_table,
+                              int32_t slot0, int32_t num_tokens, int64_t delta, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  kamera_status st = check_layout(layout);
+  if (st != KAMERA_OK) return st;
+  if (!pool) return fail(KAMERA_E_NULL, "pool is NULL");
+  if (num_tokens < 0) return fail(KAMERA_E_SHAPE, "num_tokens < 0");
+  const int P = layout->page_size;
+  std::vector<int32_t> ident;
+  if (!block_table && num_tokens > 0) {
+    if (slot0 < 0) return fail(KAMERA_E_PAGE, "slot0 < 0");
+    const int64_t np = ((int64_t)slot0 % P + num_tokens + P - 1) / P;
+    const int64_t first = slot0 / P;
+    ident.resize((size_t)np);
+    for (int64_t k = 0; k < np; ++k) ident[(size_t)k] = (int32_t)(first + k);
+    block_table = ident.data();
+    slot0 = slot0 % P;
+  }
+  kamera_chunk c;
+  std::memset(&c, 0, sizeof(c));
+  c.num_tokens = num_tokens;
+  c.flags = KAMERA_IN_PLACE;
+  c.delta = delta;
+  c.block_table = block_table;
+  c.slot0 = slot0;
+  return kamera_rehydrate_batched(layout, &c, 1, pool, workspace, workspace_bytes, stream);
+}
+
+const char* kamera_status_string(kamera_status s) {
+  switch (s) {
+    case KAMERA_OK: return "KAMERA_OK";
+    case KAMERA_E_NULL: return "KAMERA_E_NULL";
+    case KAMERA_E_SHAPE: return "KAMERA_E_SHAPE";
+    case KAMERA_E_DTYPE: return "KAMERA_E_DTYPE";
+    case KAMERA_E_RANK: return "KAMERA_E_RANK";
+    case KAMERA_E_DELTA: return "KAMERA_E_DELTA";
+    case KAMERA_E_PAGE: return "KAMERA_E_PAGE";
+    case KAMERA_E_OVERLAP: return "KAMERA_E_OVERLAP";
+    case KAMERA_E_ALIGN: return "KAMERA_E_ALIGN";
+    case KAMERA_E_WORKSPACE: return "KAMERA_E_WORKSPACE";
+    case KAMERA_E_UNSUPPORTED: return "KAMERA_E_UNSUPPORTED";
+    case KAMERA_E_HIP: return "KAMERA_E_HIP";
+  }
+  return "KAMERA_E_UNKNOWN";
+}
+
+const char* kamera_last_error(void) { return g_last_error.c_str(); }
+
+const char* kamera_version(void) { return "kamera-gfx950 0.1.0"; }
+
+}  // extern "C"

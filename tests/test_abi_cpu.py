@@ -1,0 +1,194 @@
+"""C-ABI checks that need no GPU: symbols, struct layout, host-side validation.
+
+Validation happens on the host before any HIP call, so every error path below
+returns its status on a machine without a GPU. Device pointers here are fake
+addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from position_free_kv_amd import abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kamera.h")
+FAKE = 0x10_0000_0000  # 256-byte aligned fake device address, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(kamera_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = abi.lib()
+    names = header_functions()
+    assert set(names) == set(abi.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert abi.version().startswith("kamera-gfx950")
+
+
+def test_struct_sizes_match_header():
+    # natural C layout on x86_64 (checked against the header's field order)
+    assert ctypes.sizeof(abi.Layout) == 48
+    assert ctypes.sizeof(abi.Factor) == 40
+    assert ctypes.sizeof(abi.Chunk) == 80 + 4 * 40
+    assert ctypes.sizeof(abi.Pool) == 32
+    assert ctypes.sizeof(abi.Plan) == 64
+
+
+def test_status_strings():
+    L = abi.lib()
+    for i, name in enumerate(abi.STATUS):
+        assert L.kamera_status_string(i).decode() == name
+
+
+def test_workspace_bytes_monotone():
+    a = abi.workspace_bytes(1, 0)
+    b = abi.workspace_bytes(64, 0)
+    c = abi.workspace_bytes(64, 5000)
+    assert 0 < a < b < c and c % 256 == 0
+    assert abi.workspace_bytes(-1, 0) == 0
+
+
+def gqa_layout(**kw):
+    d = dict(num_kv_heads=4, head_dim=128, rope_base=1e6, page_size=16)
+    d.update(kw)
+    return abi.make_layout(abi.GQA, abi.BF16, 2, **d)
+
+
+def chunk(**kw):
+    d = dict(num_tokens=32, delta=100, flags=abi.PATCH, k_src=FAKE, v_src=FAKE + 0x100000, k_dst=FAKE + 0x200000,
+             v_dst=FAKE + 0x300000, factors=[dict(u=FAKE + 0x400000, vt=FAKE + 0x500000, tensor=0, width=512, rank=32)])
+    d.update(kw)
+    return abi.ChunkDesc(**d)
+
+
+WS = (FAKE + 0x1000000, 1 << 20)
+
+
+def status_of(fn):
+    try:
+        fn()
+    except abi.KameraError as e:
+        return e.name, str(e)
+    return "KAMERA_OK", ""
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_layout", "KAMERA_E_NULL"),
+    ("bad_family", "KAMERA_E_UNSUPPORTED"),
+    ("bad_dtype", "KAMERA_E_DTYPE"),
+    ("zero_layers", "KAMERA_E_SHAPE"),
+    ("odd_head_dim", "KAMERA_E_SHAPE"),
+    ("bad_base", "KAMERA_E_SHAPE"),
+    ("bad_pairing", "KAMERA_E_UNSUPPORTED"),
+    ("negative_tokens", "KAMERA_E_SHAPE"),
+    ("unknown_flag", "KAMERA_E_UNSUPPORTED"),
+    ("delta_2_31", "KAMERA_E_DELTA"),
+    ("rank_too_big", "KAMERA_E_RANK"),
+    ("factor_cols_outside", "KAMERA_E_SHAPE"),
+    ("factor_null", "KAMERA_E_NULL"),
+    ("factor_bad_tensor", "KAMERA_E_SHAPE"),
+    ("null_src", "KAMERA_E_NULL"),
+    ("null_dst", "KAMERA_E_NULL"),
+    ("misaligned_src", "KAMERA_E_ALIGN"),
+    ("page_out_of_range", "KAMERA_E_PAGE"),
+    ("slot0_out_of_page", "KAMERA_E_PAGE"),
+    ("pages_overlap", "KAMERA_E_OVERLAP"),
+    ("pool_missing", "KAMERA_E_NULL"),
+    ("workspace_small", "KAMERA_E_WORKSPACE"),
+    ("workspace_null", "KAMERA_E_WORKSPACE"),
+    ("too_many_factors", "KAMERA_E_SHAPE"),
+])
+def test_validation_errors(case, expect):
+    lay = gqa_layout()
+    pool = abi.make_pool(FAKE + 0x4000000, FAKE + 0x8000000, num_pages=8)
+    run = lambda L=lay, cs=None, p=None, ws=WS: abi.rehydrate_batched(L, cs or [chunk()], p, ws, 0)
+    if case == "null_layout":
+        f = lambda: abi._check(abi.lib().kamera_rehydrate_batched(None, None, 0, None, None, 0, None))
+    elif case == "bad_family":
+        f = lambda: run(L=abi.make_layout(7, abi.BF16, 2, num_kv_heads=4, head_dim=128))
+    elif case == "bad_dtype":
+        f = lambda: run(L=abi.make_layout(abi.GQA, 9, 2, num_kv_heads=4, head_dim=128))
+    elif case == "zero_layers":
+        f = lambda: run(L=abi.make_layout(abi.GQA, abi.BF16, 0, num_kv_heads=4, head_dim=128))
+    elif case == "odd_head_dim":
+        f = lambda: run(L=gqa_layout(head_dim=127))
+    elif case == "bad_base":
+        f = lambda: run(L=gqa_layout(rope_base=-1.0))
+    elif case == "bad_pairing":
+        f = lambda: run(L=gqa_layout(pairing=5))
+    elif case == "negative_tokens":
+        f = lambda: run(cs=[chunk(num_tokens=-1)])
+    elif case == "unknown_flag":
+        f = lambda: run(cs=[chunk(flags=8)])
+    elif case == "delta_2_31":
+        f = lambda: run(cs=[chunk(delta=2 ** 31)])
+    elif case == "rank_too_big":
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, width=512, rank=abi.MAX_RANK + 1)])])
+    elif case == "factor_cols_outside":
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, col0=500, width=64, rank=8)])])
+    elif case == "factor_null":
+        f = lambda: run(cs=[chunk(factors=[dict(u=None, vt=FAKE, width=512, rank=8)])])
+    elif case == "factor_bad_tensor":
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, tensor=2, width=512, rank=8)])])
+    elif case == "null_src":
+        f = lambda: run(cs=[chunk(v_src=None)])
+    elif case == "null_dst":
+        f = lambda: run(cs=[chunk(k_dst=None)])
+    elif case == "misaligned_src":
+        f = lambda: run(cs=[chunk(k_src=FAKE + 1)])
+    elif case == "page_out_of_range":
+        f = lambda: run(cs=[chunk(block_table=np.array([0, 8]), k_dst=None, v_dst=None)], p=pool)
+    elif case == "slot0_out_of_page":
+        f = lambda: run(cs=[chunk(block_table=np.array([0, 1, 2]), slot0=16, k_dst=None, v_dst=None)], p=pool)
+    elif case == "pages_overlap":
+        f = lambda: run(cs=[chunk(block_table=np.array([0, 1]), k_dst=None, v_dst=None),
+                            chunk(num_tokens=20, block_table=np.array([3, 1]), k_dst=None, v_dst=None)], p=pool)
+    elif case == "pool_missing":
+        f = lambda: run(cs=[chunk(block_table=np.array([0, 1]), k_dst=None, v_dst=None)], p=None)
+    elif case == "workspace_small":
+        f = lambda: run(ws=(WS[0], 64))
+    elif case == "workspace_null":
+        f = lambda: run(ws=(0, 1 << 20))
+    elif case == "too_many_factors":
+        c = chunk()
+        c.c.num_factors = 5
+        f = lambda: run(cs=[c])
+    name, msg = status_of(f)
+    assert name == expect, (case, name, msg)
+
+
+def test_partial_page_sharing_is_not_an_overlap():
+    """Two chunks may share a page when their slots do not collide: validation passes and
+    the call proceeds to the HIP upload (which fails here only for want of a GPU)."""
+    pool = abi.make_pool(FAKE + 0x4000000, FAKE + 0x8000000, num_pages=8)
+    a = chunk(num_tokens=10, block_table=np.array([2]), slot0=0, k_dst=None, v_dst=None)
+    b = chunk(num_tokens=6, block_table=np.array([2]), slot0=10, k_dst=None, v_dst=None)
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, b], pool, WS, 0))
+    assert name in ("KAMERA_OK", "KAMERA_E_HIP"), msg
+
+
+def test_empty_batches_need_no_gpu():
+    abi.rehydrate_batched(gqa_layout(), [], None, WS, 0)
+    abi.rehydrate_batched(gqa_layout(), [chunk(num_tokens=0)], None, WS, 0)
+    pool = abi.make_pool(FAKE, FAKE + 0x100000, num_pages=4)
+    abi.relocate(gqa_layout(), pool, None, 0, 0, 5, WS, 0)
+
+
+def test_relocate_validates_pages():
+    pool = abi.make_pool(FAKE, FAKE + 0x100000, num_pages=2)
+    name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, None, 0, 40, 5, WS, 0))   # needs 3 pages
+    assert name == "KAMERA_E_PAGE"
+    name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, np.array([0, 5]), 0, 20, 5, WS, 0))
+    assert name == "KAMERA_E_PAGE"
+
+
+def test_plan_struct_roundtrip_empty():
+    plan = abi.plan_upload(gqa_layout(), [], None, WS, 0)
+    assert plan.num_tasks == 0 and plan.kernel == 0
+    abi.plan_launch(plan, 0)

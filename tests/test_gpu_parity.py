@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element (small sizes).
+
+Bar (Kamera preprint §6, "within one bf16 ULP of recompute"): every bf16 output
+is within one bf16 step of the once-rounded fp64 result (P1) or within the fp32
+accumulation bound (P2); fp32 outputs meet P3. Indexing, untouched bytes and the
+identity case are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import (check_all, custom_workload, factor, gqa_chunks, pool_untouched_ok, say,
+                            touched_tensors)
+from workloads import make_workload
+from workloads.configs import BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, ChunkSpec, LayoutSpec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from position_free_kv_amd import abi
+    abi.lib()   # fails loudly when the HIP library is missing
+    yield
+
+
+def run_dw(wl):
+    from workloads.device import DeviceWorkload
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    return dw
+
+
+def assert_parity(dw, **kw):
+    tot = check_all(dw, **kw)
+    say(f"  compared {tot['n']} elements: fail={tot['fail']} p2_only={tot['p2_only']} exact={tot['exact']}")
+    assert tot["fail"] == 0, tot["bad"][:3]
+    return tot
+
+
+# ---------------------------------------------------------------- the five configs, shrunk
+@pytest.mark.parametrize("name,kw", [
+    ("C1", {}),                                                        # full size (fp32, generic kernel)
+    ("C2", dict(num_layers=2, num_chunks=3, tokens=200)),
+    ("C3", dict(num_layers=2, num_chunks=2, tokens=150)),
+    ("C4", dict(num_layers=1, tokens=48)),
+    ("C5", dict(num_layers=2, num_chunks=8, max_tokens=300)),
+])
+def test_config_parity_small(name, kw):
+    say(f"[parity-small] {name} {kw}")
+    wl = make_workload(name, **kw)
+    dw = run_dw(wl)
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
+    if name == "C5":   # survivors: V pages untouched, byte for byte
+        for ch in wl.chunks:
+            if ch.role == "survivor":
+                for layer in range(dw.L):
+                    assert np.array_equal(dw.out_rows(ch, layer, 1), wl.pool_rows(ch, layer, 1))
+
+
+# ---------------------------------------------------------------- bit-exact identity
+@pytest.mark.parametrize("family", ["gqa128", "gqa64", "mla", "gqa_f32"])
+def test_identity_delta0_nopatch(family):
+    say(f"[identity] {family}")
+    if family == "mla":
+        lay = LayoutSpec(MLA, BF16, 2, latent_dim=512, rope_dim=64)
+        chunks = [ChunkSpec(index=0, num_tokens=77, delta=0, flags=0, canon_id=0, dst_buffer=0)]
+    else:
+        hd = 64 if family == "gqa64" else 128
+        dt = F32 if family == "gqa_f32" else BF16
+        lay = LayoutSpec(GQA, dt, 2, num_kv_heads=3, head_dim=hd)
+        chunks = gqa_chunks(2, [77, 16], 0, 3, hd, 0, patch=False)
+    wl = custom_workload(lay, chunks)
+    dw = run_dw(wl)
+    for ch in wl.chunks:
+        for layer in range(2):
+            for t in touched_tensors(wl, ch):
+                assert np.array_equal(dw.out_rows(ch, layer, t), wl.canonical(ch.canon_id, layer, t))
+
+
+def test_mla_cache_passthrough_bytes():
+    """Preprint §3 / Fig. 2: c_KV is reused byte for byte; only k_rope rotates."""
+    wl = make_workload("C3", num_layers=2, num_chunks=3, tokens=70, patch=False)
+    dw = run_dw(wl)
+    for ch in wl.chunks:
+        for layer in range(2):
+            g = dw.out_rows(ch, layer, 0)
+            assert np.array_equal(g[:, :512], wl.canonical(ch.canon_id, layer, 0)[:, :512])
+    assert_parity(dw)
+
+
+# ---------------------------------------------------------------- shapes and ranks
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 129, 300])
+def test_ragged_token_counts(T):
+    say(f"[ragged] T={T}")
+    lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6)
+    wl = custom_workload(lay, gqa_chunks(2, T, [513, -77], 2, 128, 32))
+    assert_parity(run_dw(wl))
+
+
+@pytest.mark.parametrize("rank", [1, 5, 8, 13, 32, 40, 64, 96, 128])
+def test_ranks(rank):
+    say(f"[rank] m={rank}")
+    lay = LayoutSpec(GQA, BF16, 1, num_kv_heads=2, head_dim=128, rope_base=1e4)
+    wl = custom_workload(lay, gqa_chunks(2, 70, [1000, 31], 2, 128, rank))
+    assert_parity(run_dw(wl))
+
+
+@pytest.mark.parametrize("delta", [1, -1, -65536, 2 ** 31 - 1, -(2 ** 31 - 1), 123457])
+def test_deltas(delta):
+    say(f"[delta] {delta}")
+    lay = LayoutSpec(GQA, BF16, 1, num_kv_heads=1, head_dim=128, rope_base=1e6)
+    wl = custom_workload(lay, gqa_chunks(1, 40, delta, 1, 128, 8))
+    assert_parity(run_dw(wl))
+
+
+@pytest.mark.parametrize("variant", ["gqa64", "gptj128", "gptj64", "mla_gptj", "gqa96_generic", "mla_f32",
+                                     "mla_latent_odd_generic"])
+def test_layout_variants(variant):
+    say(f"[layout] {variant}")
+    if variant.startswith("mla"):
+        dt = F32 if variant == "mla_f32" else BF16
+        lat = 200 if variant == "mla_latent_odd_generic" else 512
+        lay = LayoutSpec(MLA, dt, 2, latent_dim=lat, rope_dim=64, pairing=GPTJ if "gptj" in variant else NEOX)
+        F = lat + 64
+        chunks = [ChunkSpec(index=i, num_tokens=45 + 20 * i, delta=9000 * (i + 1), flags=PATCH, canon_id=i,
+                            factors=[factor(i, 0, 0, 0, F, 16), factor(i, 1, 0, lat, 64, 8)], dst_buffer=i)
+                  for i in range(2)]
+    else:
+        hd = {"gqa64": 64, "gptj128": 128, "gptj64": 64, "gqa96_generic": 96}[variant]
+        lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=3, head_dim=hd, pairing=GPTJ if "gptj" in variant else NEOX)
+        chunks = gqa_chunks(2, [50, 33], [4000, -250], 3, hd, 16)
+    wl = custom_workload(lay, chunks)
+    assert_parity(run_dw(wl))
+
+
+def test_partial_and_per_head_factors():
+    """Factors covering a head each, and one covering an unaligned column range."""
+    say("[factors] per-head + unaligned")
+    lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=4, head_dim=128, rope_base=1e6)
+    facs = [factor(0, h, 0, 128 * h, 128, 8) for h in range(3)] + [factor(0, 3, 1, 40, 100, 24)]
+    ch = ChunkSpec(index=0, num_tokens=90, delta=777, flags=PATCH, canon_id=0, factors=facs, dst_buffer=0)
+    assert_parity(run_dw(custom_workload(lay, [ch])))
+
+
+def test_layer_sparse_patch():
+    """A factor with layer0 > 0 patches only the deeper layers (deep-half patches)."""
+    say("[layer0]")
+    lay = LayoutSpec(GQA, BF16, 4, num_kv_heads=2, head_dim=128, rope_base=1e6)
+    ch = ChunkSpec(index=0, num_tokens=64, delta=321, flags=PATCH, canon_id=0,
+                   factors=[factor(0, 0, 0, 0, 256, 32, layer0=2), factor(0, 1, 1, 0, 256, 32, layer0=3)],
+                   dst_buffer=0)
+    assert_parity(run_dw(custom_workload(lay, [ch])))
+
+
+# ---------------------------------------------------------------- paged pool
+@pytest.mark.parametrize("slot0", [0, 5, 15])
+def test_paged_slot0(slot0):
+    say(f"[paged] slot0={slot0}")
+    P = 16
+    lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=P)
+    rng = np.random.default_rng(slot0)
+    chunks, pages = [], rng.permutation(40).astype(np.int32)
+    cur = 0
+    for i, T in enumerate([37, 16, 5]):
+        n = -(-(slot0 + T) // P)
+        chunks.append(ChunkSpec(index=i, num_tokens=T, delta=100 * i + 7, flags=PATCH, canon_id=i,
+                                factors=[factor(i, 0, 0, 0, 256, 32), factor(i, 1, 1, 0, 256, 32)],
+                                block_table=pages[cur:cur + n].copy(), slot0=slot0))
+        cur += n
+    wl = custom_workload(lay, chunks, dense_rows=[], num_pages=40)
+    dw = run_dw(wl)
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
+
+
+def test_in_place_with_patch_mla_and_gqa():
+    """In place with a patch: re-conditioning a resident chunk (rotate + add)."""
+    say("[in-place+patch]")
+    for lay, facs in [(LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6),
+                       [factor(0, 0, 0, 0, 256, 32), factor(0, 1, 1, 0, 256, 32)]),
+                      (LayoutSpec(MLA, BF16, 2, latent_dim=512, rope_dim=64),
+                       [factor(0, 0, 0, 0, 576, 32), factor(0, 1, 0, 512, 64, 32)])]:
+        ch = ChunkSpec(index=0, num_tokens=50, delta=-4096, flags=IN_PLACE | PATCH, canon_id=0, factors=facs,
+                       block_table=np.array([3, 0, 7, 1], np.int32), slot0=2, role="survivor")
+        wl = custom_workload(lay, [ch], dense_rows=[], num_pages=8)
+        dw = run_dw(wl)
+        assert_parity(dw)
+        assert pool_untouched_ok(dw)
+
+
+def test_mla_survivor_in_place_touches_rope_only():
+    lay = LayoutSpec(MLA, BF16, 3, latent_dim=512, rope_dim=64)
+    ch = ChunkSpec(index=0, num_tokens=40, delta=-3000, flags=IN_PLACE, canon_id=0,
+                   block_table=np.array([5, 2, 0], np.int32), slot0=0, role="survivor")
+    wl = custom_workload(lay, [ch], dense_rows=[], num_pages=6)
+    dw = run_dw(wl)
+    assert_parity(dw)
+    for layer in range(3):
+        assert np.array_equal(dw.out_rows(ch, layer, 0)[:, :512], wl.pool_rows(ch, layer, 0)[:, :512])
+    assert pool_untouched_ok(dw)
+
+
+# ---------------------------------------------------------------- determinism, composition, plan reuse
+def test_run_twice_bitwise_identical_and_plan_reuse():
+    from position_free_kv_amd import abi
+    wl = make_workload("C2", num_layers=2, num_chunks=2, tokens=130)
+    from workloads.device import DeviceWorkload
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    first = [t.clone() for buf in dw.dense for t in buf]
+    plan = dw.plan()
+    for _ in range(3):
+        abi.plan_launch(plan)
+    torch.cuda.synchronize()
+    again = [t for buf in dw.dense for t in buf]
+    assert all(torch.equal(a, b) for a, b in zip(first, again))
+
+
+def test_reorder_same_slot_identical():
+    """Two orderings that put the same chunk at the same slot (same delta, same stored
+    patch) give bit-identical rows."""
+    wl = make_workload("C4", num_layers=1, tokens=32)
+    dw = run_dw(wl)
+    seen = {}
+    for ch in wl.chunks:
+        key = (ch.canon_id, ch.dst_row0)
+        rows = dw.out_rows(ch, 0, 0)
+        if key in seen:
+            assert np.array_equal(rows, seen[key])
+        seen[key] = rows
+
+
+def test_relocation_composes_on_gpu():
+    """R(d2) R(d1) in place vs R(d1 + d2) at once (preprint §1: R(d)R(p) = R(p+d)).
+    The two-step result carries one extra bf16 rounding of the intermediate pair, which
+    the second rotation mixes across the pair, so the bound is in units of the pair's
+    norm: |a - b| <= 2 ulp_bf16(|(x_p, x_q)|) per element."""
+    from position_free_kv_amd import abi
+    from oracle.tolerance import bf16_value, ulp_bf16
+    lay = abi.make_layout(abi.GQA, abi.BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=16)
+    x = torch.randn(2, 4, 16, 256, device="cuda").to(torch.bfloat16).view(torch.int16)
+    a, b = x.clone(), x.clone()
+    ws = torch.empty(abi.workspace_bytes(1, 8), dtype=torch.uint8, device="cuda")
+    pa, pb = abi.make_pool(a, None, 4), abi.make_pool(b, None, 4)
+    abi.relocate(lay, pa, None, 0, 64, 3000, ws)
+    abi.relocate(lay, pa, None, 0, 64, -1234, ws)
+    abi.relocate(lay, pb, None, 0, 64, 3000 - 1234, ws)
+    torch.cuda.synchronize()
+    va = bf16_value(a.cpu().numpy().view(np.uint16)).reshape(-1, 2, 2, 64)   # [row][head][half][pair]
+    vb = bf16_value(b.cpu().numpy().view(np.uint16)).reshape(-1, 2, 2, 64)
+    vx = bf16_value(x.cpu().numpy().view(np.uint16)).reshape(-1, 2, 2, 64)
+    norm = np.sqrt(vx[:, :, 0] ** 2 + vx[:, :, 1] ** 2)[:, :, None, :]
+    assert np.all(np.abs(va - vb) <= 2 * ulp_bf16(norm))

@@ -168,7 +168,10 @@ class Workload:
     def _factor_fp64(self, f: FactorSpec, T: int, layer: int):
         rng = np.random.default_rng([self.root, _P_FACTOR, f.key, layer, f.slot])
         def orth(n, m):
-            q, r = np.linalg.qr(rng.standard_normal((n, m)))
+            g = rng.standard_normal((n, m))
+            if n < m:   # no n x m matrix has orthonormal columns: keep the scaled Gaussian
+                return g / np.sqrt(n)
+            q, r = np.linalg.qr(g)
             return q * np.sign(np.diag(r))[None, :]
         q1 = orth(T, f.rank)
         q2 = orth(f.width, f.rank)
