@@ -110,6 +110,7 @@ def main() -> int:
     ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-units", type=int, default=224, help="(chunk, layer) units timed on the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
@@ -166,6 +167,24 @@ def main() -> int:
     torch.cuda.synchronize()
     kernel_us = e2.elapsed_time(e3) / args.steps * 1e3
 
+    # ---- a plain device copy of known size: practical read+write ceiling, and the
+    # reference kernel for scaling the HBM byte counters
+    copy_gbps = None
+    if not args.no_copy:
+        n = 1 << 30
+        src = torch.empty(n // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e4, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e4.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e5.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * n / (e4.elapsed_time(e5) / 10 * 1e-3) / 1e9
+        del src, dst
+
     ms_per_step = wall_s / args.steps * 1e3
     tokens = wl.total_tokens
     alg_bytes = dw.algorithmic_bytes()
@@ -193,6 +212,8 @@ def main() -> int:
         "call_us_gpu": call_ms_gpu * 1e3,
         "algorithmic_bytes": alg_bytes,
         "kernel_tokens_per_s": tokens / (kernel_us * 1e-6),
+        "copy_ceiling_GBps": copy_gbps,
+        "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }

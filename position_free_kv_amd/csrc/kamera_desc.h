@@ -13,10 +13,11 @@ constexpr int kSlab = 64;          // columns per slab of the MFMA path
 constexpr int kTileTokens = 16;    // tokens per MFMA tile (the N dimension)
 constexpr int kMaxFactors = 4;
 
-// MFMA path: per-wave register budget of (slab x k-step) operand sets.
-// Variant v holds up to kBudget[v] sets of 8 bf16 x 4 tiles per lane.
-constexpr int kNumVariants = 3;
-constexpr int kBudget[kNumVariants] = {2, 4, 8};
+// MFMA path: a wave task covers a column group of 1 or 2 slabs and holds up to
+// kMaxKSteps 32-wide k-steps of V^T operands in registers. Kernel variant
+// v = (slabs - 1) * 4 + log2(k-step capacity), capacity in {1, 2, 4, 8}.
+constexpr int kMaxKSteps = 8;
+constexpr int kMfmaRangeTokens = 128;  // tokens per wave task (8 tiles)
 
 struct alignas(16) DevFactor {
   const void* u;        // [L - layer0][T][rank]
@@ -30,7 +31,7 @@ struct alignas(16) DevFactor {
 };
 static_assert(sizeof(DevFactor) == 48, "DevFactor layout");
 
-// Per-chunk record. Task space of a chunk (both kernels):
+// Per-chunk record. Task space of a chunk (MFMA path: one task = one wave; generic: one workgroup):
 //   task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
 // stream indexes the tensors this chunk touches (stream_tensor[]), tb the token
 // block, g the column group (MFMA path: head or slab; generic path: unused = 1).

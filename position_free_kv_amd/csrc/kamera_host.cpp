@@ -178,7 +178,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
 
   // -------------------------------------------------------------- per-chunk checks
   bool mfma = mfma_layout_ok(L);
-  int need_budget = 0;
+  int need_ksteps = 0;  // MFMA path: most 32-wide k-steps covering any column group
   std::vector<uint8_t> slot_used;
   if (any_paged) slot_used.assign((size_t)pool->num_pages * P, 0);
 
@@ -258,7 +258,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
         if (!aligned(fa.u, es) || !aligned(fa.vt, es))
           return fail(KAMERA_E_ALIGN, "chunk %d factor %d: factor pointers must be aligned to %zu bytes", i, f, es);
       }
-      // MFMA register budget: slabs per group x k-steps of the factors covering it
+      // MFMA path: k-steps of the factors covering each column group
       if (mfma) {
         const int gcols = L->family == KAMERA_GQA ? L->head_dim : kSlab;
         const int ngroups = F / gcols;
@@ -271,12 +271,14 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
                 continue;
               ks += (fa.rank + 31) / 32;
             }
-            need_budget = std::max(need_budget, ks * (gcols / kSlab));
+            need_ksteps = std::max(need_ksteps, ks);
           }
       }
     }
   }
-  if (mfma && need_budget > kBudget[kNumVariants - 1]) mfma = false;
+  // 128-wide groups keep at most 4 k-steps of V^T operands in registers
+  if (mfma && need_ksteps > (L->family == KAMERA_GQA && L->head_dim == 128 ? kMaxKSteps / 2 : kMaxKSteps))
+    mfma = false;
 
   // -------------------------------------------------------------- pack
   out.bytes = ws_bytes(n, total_pages);
@@ -301,7 +303,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   hd->group_cols = mfma ? (L->family == KAMERA_GQA ? L->head_dim : kSlab) : F;
   hd->rope_group = (mfma && L->family == KAMERA_MLA) ? L->latent_dim / kSlab : -1;
 
-  const int tb_tokens = mfma ? 128 : 16;
+  const int tb_tokens = mfma ? kMfmaRangeTokens : 16;
   int64_t task = 0;
   int64_t page_cursor = 0;
   out.page_off.assign((size_t)n, -1);
@@ -389,8 +391,11 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   out.tasks = task;
   out.kernel = task == 0 ? 0 : (mfma ? 1 : 2);
   out.variant = 0;
-  if (mfma)
-    while (out.variant < kNumVariants - 1 && kBudget[out.variant] < need_budget) ++out.variant;
+  if (mfma) {
+    int cap_log2 = 0;
+    while ((1 << cap_log2) < need_ksteps) ++cap_log2;
+    out.variant = (hd->group_cols / kSlab - 1) * 4 + cap_log2;
+  }
   return KAMERA_OK;
 }
 

@@ -6,11 +6,14 @@
 // paged KV pool (preprint §6).
 //
 // Two kernels read the same packed batch (kamera_desc.h):
-//   rehydrate_mfma<V>  bf16, head_dim 64/128 or MLA with a 64-wide rope band.
-//     One wave = 16 tokens x one column group (a 128-column head = 2 slabs, or
-//     one 64-column slab) of one tensor, looping over a block of token tiles.
-//     The patch contraction (16 tokens x m) . (m x 16 columns) runs on
+//   rehydrate_mfma<S,K>  bf16, head_dim 64/128 or MLA with a 64-wide rope band.
+//     One wave = one column group (a 128-column head = 2 slabs, or one
+//     64-column slab) of one tensor over a block of 16-token tiles. The patch
+//     contraction (16 tokens x m) . (m x 16 columns) runs on
 //     v_mfma_f32_16x16x32_bf16 with the rotated rows as the accumulator input.
+//     Rows stream through HBM in whole-line order with nontemporal loads and
+//     stores and are transposed to and from the MFMA layout in a per-wave LDS
+//     tile.
 //   rehydrate_generic  any dtype/shape; plain fp32 VALU, one workgroup per
 //     (chunk, tensor, layer, token block).
 //
@@ -24,7 +27,7 @@
 //   The MFMA result layout gives lane (lg, c) rows M = 4lg + [0,4) of column c.
 //   Tile q of slab s maps row M to column 64s + 32(q>>1) + 8(M>>2) + 4(q&1) + (M&3),
 //   so the 4 tiles x 4 values of a lane are exactly its two loaded runs. The
-//   V^T operand is loaded once per task with that same column map.
+//   V^T operand is staged once per workgroup with that same column map.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,39 +89,69 @@ __device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ pages,
 // ============================================================================
 // MFMA path
 // ============================================================================
-struct TaskCtx {
-  const uint16_t* src;   // layer base of the source tensor
-  uint16_t* dst;         // layer base of the destination tensor
-  const int32_t* pages;
-  int slot0, P, F, T;
-  int colbase;           // first column of the group
-  int tok0, ntiles;
-  bool in_place, paged;
+// A wave task is (chunk, tensor, layer, token block, column group). Rows move
+// between HBM and registers in "line" layout: a load or store instruction covers
+// whole rows of the group (4 rows x 256 B for a 128-column group), so every
+// 128-byte line is touched by one instruction and the stream can bypass the
+// caches (nontemporal). A per-wave LDS tile (rows padded by 16 B so both
+// layouts are bank-conflict free) turns line layout into the MFMA layout and
+// back. V^T operands and cos/sin stay in registers for the whole task.
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id b runs on XCD b % 8).
+// Give each XCD a contiguous run of task ids, so that tasks sharing a head's V^T
+// (consecutive token blocks) and a block's U (consecutive groups) meet in one
+// L2. Only locality depends on this; any mapping is correct.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
+  const int64_t q = n / 8, r = n % 8;
+  const int64_t x = b % 8, l = b / 8;
+  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  // LDS traffic of one wave is processed in order; this only stops the compiler
+  // from moving LDS accesses across the hand-off between the two layouts.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NSLAB>
+struct Geo {
+  static constexpr int GC = 64 * NSLAB;        // columns per group
+  static constexpr int CPR = GC / 8;           // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;         // rows per line-layout instruction
+  static constexpr int NI = 16 / RPI;          // line-layout instructions per tile (= 2 * NSLAB)
+  static constexpr int RS = 2 * GC + 16;       // LDS row stride in bytes
+  static constexpr int LDS = 16 * RS;          // bytes per wave
 };
 
 template <int NSLAB, int NK>
-__device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& ch, const TaskCtx& tc,
-                                          int layer, int tensor, int rot, const int* kfac,
-                                          const int* kstep, int lane) {
+__device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& ch, int layer, int tensor,
+                                          int colbase, int tok0, int ntiles, int rot, const int* kfac,
+                                          const int* kstep, int lane, unsigned char* lds) {
+  using G = Geo<NSLAB>;
   const int lg = lane >> 4;
   const int c = lane & 15;
+  const int lrow = lane / G::CPR;   // line layout: row inside an instruction's rows
+  const int lchunk = lane % G::CPR; // line layout: 16-byte chunk of the row
+  const bool in_place = (ch.flags & 2u) != 0;
+  const int P = hd.page_size, F = hd.F, T = ch.T;
+  const int32_t* pages = ch.pages;
+  const uint16_t* src = (const uint16_t*)ch.src[tensor] + (int64_t)layer * ch.src_ls + colbase + 8 * lchunk;
+  uint16_t* dst = (uint16_t*)ch.dst[tensor] + (int64_t)layer * ch.dst_ls + colbase + 8 * lchunk;
 
-  // ---- rotation coefficients for the pairs this lane holds
+  // ---- rotation coefficients for the pairs this lane holds (MFMA layout)
   float cs[NSLAB * 8], sn[NSLAB * 8];
   if (rot != ROT_NONE) {
     float cl = 1.f, sl = 0.f;
-    const int npairs = hd.d_rot >> 1;
-    if (lane < npairs) phase_fp64(hd.rope_base, hd.d_rot, ch.delta, lane, cl, sl);
+    if (lane < (hd.d_rot >> 1)) phase_fp64(hd.rope_base, hd.d_rot, ch.delta, lane, cl, sl);
 #pragma unroll
     for (int j = 0; j < NSLAB * 8; ++j) {
       int p;
-      if (rot == ROT_NEOX_SLABS) {          // j in [0,16): slab 0 element j
-        p = 32 * (j >> 3) + 8 * lg + (j & 7);
-      } else if (rot == ROT_NEOX_RUNS) {    // j in [0,8): run 0 element j
-        p = 8 * lg + j;
-      } else {                              // GPT-J: element pair (2j, 2j+1)
-        const int e2 = 2 * j;               // element index inside the lane's 16*NSLAB
-        const int s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;
+      if (rot == ROT_NEOX_SLABS) p = 32 * (j >> 3) + 8 * lg + (j & 7);   // slab-0 element j
+      else if (rot == ROT_NEOX_RUNS) p = 8 * lg + (j & 7);               // run-0 element j
+      else {                                                              // GPT-J pair (2j, 2j+1)
+        const int e2 = 2 * j, s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;
         p = (64 * s + 32 * r + 8 * lg + e) >> 1;
       }
       cs[j] = __shfl(cl, p, 64);
@@ -128,24 +161,24 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
 
   // ---- V^T operands: A[M][k] = Vt[k][col(M)] for every slab, tile and k-step
   bf16x8 av[NK > 0 ? NSLAB * 4 * NK : 1];
-  bool uvec[NK > 0 ? NK : 1];
   const uint16_t* ubase[NK > 0 ? NK : 1];
-  int urank[NK > 0 ? NK : 1];
+  int urank[NK > 0 ? NK : 1], ustride[NK > 0 ? NK : 1];
+  bool uvec[NK > 0 ? NK : 1];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const DevFactor& f = ch.fac[kfac[j]];
-    const int lrel = layer - f.layer0;
-    const uint16_t* vt = (const uint16_t*)f.vt + (int64_t)lrel * f.rank * f.width;
-    ubase[j] = (const uint16_t*)f.u + (int64_t)lrel * ch.T * f.rank + 32 * kstep[j] + 8 * lg;
-    urank[j] = f.rank - 32 * kstep[j] - 8 * lg;   // valid k entries from this lane's offset
+    const int64_t lrel = layer - f.layer0;
+    const uint16_t* vt = (const uint16_t*)f.vt + lrel * f.rank * f.width;
+    ubase[j] = (const uint16_t*)f.u + lrel * T * f.rank + 32 * kstep[j] + 8 * lg;
+    urank[j] = f.rank - 32 * kstep[j] - 8 * lg;
+    ustride[j] = f.rank;
     uvec[j] = f.pad[0] != 0;
-    const int mrow = lane & 15;
-    const int kg = lane >> 4;
+    const int mrow = lane & 15, kg = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < NSLAB; ++s) {
+    for (int s = 0; s < NSLAB; ++s)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = tc.colbase + 64 * s + 32 * (q >> 1) + 8 * (mrow >> 2) + 4 * (q & 1) + (mrow & 3);
+        const int col = colbase + 64 * s + 32 * (q >> 1) + 8 * (mrow >> 2) + 4 * (q & 1) + (mrow & 3);
         const int rel = col - f.col0;
         const bool in = rel >= 0 && rel < f.width;
         bf16x8 a;
@@ -157,40 +190,31 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
         }
         av[(s * 4 + q) * NK + j] = a;
       }
-    }
   }
 
   const bool compute = (rot != ROT_NONE) || (NK > 0);
-
-  auto src_row = [&](int t) -> const uint16_t* {
-    return tc.src + row_offset(tc.in_place ? tc.pages : nullptr, tc.slot0, tc.P, tc.F, t);
-  };
-  auto dst_row = [&](int t) -> uint16_t* {
-    return tc.dst + row_offset(tc.pages, tc.slot0, tc.P, tc.F, t);
-  };
-
-  u32x4 cur[NSLAB][2], nxt[NSLAB][2];
+  u32x4 cur[G::NI], nxt[G::NI];
   bf16x8 ucur[NK > 0 ? NK : 1], unxt[NK > 0 ? NK : 1];
 
-  auto load_tile = [&](int tile, u32x4 (&raw)[NSLAB][2], bf16x8 (&ub)[NK > 0 ? NK : 1]) {
-    const int t = tc.tok0 + tile * kTileTokens + c;
-    const bool valid = t < tc.T;
-    const uint16_t* row = valid ? src_row(t) : nullptr;
+  auto load_tile = [&](int tile, u32x4 (&raw)[G::NI], bf16x8 (&ub)[NK > 0 ? NK : 1]) {
+    const int tt = tok0 + tile * kTileTokens;
 #pragma unroll
-    for (int s = 0; s < NSLAB; ++s)
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        raw[s][r] = valid ? *(const u32x4*)(row + tc.colbase + 64 * s + 32 * r + 8 * lg) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < G::NI; ++i) {
+      const int t = tt + i * G::RPI + lrow;
+      raw[i] = t < T ? __builtin_nontemporal_load(
+                           (const u32x4*)(src + row_offset(in_place ? pages : nullptr, ch.slot0, P, F, t)))
+                     : u32x4{0, 0, 0, 0};
+    }
+    const int t = tt + c;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       bf16x8 b;
-      if (valid && uvec[j] && urank[j] >= 8) {
-        b = *(const bf16x8*)(ubase[j] + (int64_t)t * (ch.fac[kfac[j]].rank));
+      if (t < T && uvec[j] && urank[j] >= 8) {
+        b = *(const bf16x8*)(ubase[j] + (int64_t)t * ustride[j]);
       } else {
-        const int rk = ch.fac[kfac[j]].rank;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint16_t h = (valid && e < urank[j]) ? ubase[j][(int64_t)t * rk + e] : (uint16_t)0;
+          const uint16_t h = (t < T && e < urank[j]) ? ubase[j][(int64_t)t * ustride[j] + e] : (uint16_t)0;
           b[e] = __builtin_bit_cast(__bf16, h);
         }
       }
@@ -199,18 +223,24 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   };
 
   load_tile(0, cur, ucur);
-  for (int tile = 0; tile < tc.ntiles; ++tile) {
-    if (tile + 1 < tc.ntiles) load_tile(tile + 1, nxt, unxt);
-    const int t = tc.tok0 + tile * kTileTokens + c;
-    const bool valid = t < tc.T;
-
-    u32x4 out[NSLAB][2];
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if (tile + 1 < ntiles) load_tile(tile + 1, nxt, unxt);
+    const int tt = tok0 + tile * kTileTokens;
+    u32x4 out[G::NI];
     if (!compute) {
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) out[i] = cur[i];  // line layout in, line layout out
+    } else {
+      // line layout -> LDS -> MFMA layout (lane (lg, c): row c, chunks 8s + 4r + lg)
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i)
+        *(u32x4*)(lds + (i * G::RPI + lrow) * G::RS + 16 * lchunk) = cur[i];
+      wave_lds_fence();
+      u32x4 m[NSLAB][2];
 #pragma unroll
       for (int s = 0; s < NSLAB; ++s)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) out[s][r] = cur[s][r];
-    } else {
+        for (int r = 0; r < 2; ++r) m[s][r] = *(const u32x4*)(lds + c * G::RS + 16 * (8 * s + 4 * r + lg));
       float x[NSLAB * 16];
 #pragma unroll
       for (int s = 0; s < NSLAB; ++s)
@@ -218,26 +248,24 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
         for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            x[16 * s + 8 * r + 2 * w] = bf_lo(cur[s][r][w]);
-            x[16 * s + 8 * r + 2 * w + 1] = bf_hi(cur[s][r][w]);
+            x[16 * s + 8 * r + 2 * w] = bf_lo(m[s][r][w]);
+            x[16 * s + 8 * r + 2 * w + 1] = bf_hi(m[s][r][w]);
           }
-      if (rot == ROT_NEOX_SLABS) {
+      if (NSLAB == 2 && rot == ROT_NEOX_SLABS) {  // pair (i, i + 64): slabs 0 and 1, same position
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float a = x[j], b = x[16 + (j & 15)];
+          const float a = x[j], b = x[(NSLAB - 1) * 16 + j];
           x[j] = fmaf(a, cs[j], -(b * sn[j]));
-          x[16 + (j & 15)] = fmaf(a, sn[j], b * cs[j]);
+          x[(NSLAB - 1) * 16 + j] = fmaf(a, sn[j], b * cs[j]);
         }
-      } else if (rot == ROT_NEOX_RUNS) {
+      } else if (rot == ROT_NEOX_RUNS) {          // pair (i, i + 32): runs 0 and 1 of slab 0
 #pragma unroll
-        for (int s = 0; s < NSLAB; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float a = x[16 * s + j], b = x[16 * s + 8 + j];
-            x[16 * s + j] = fmaf(a, cs[j], -(b * sn[j]));
-            x[16 * s + 8 + j] = fmaf(a, sn[j], b * cs[j]);
-          }
-      } else if (rot == ROT_GPTJ) {
+        for (int j = 0; j < 8; ++j) {
+          const float a = x[j], b = x[8 + j];
+          x[j] = fmaf(a, cs[j], -(b * sn[j]));
+          x[8 + j] = fmaf(a, sn[j], b * cs[j]);
+        }
+      } else if (rot == ROT_GPTJ) {               // pair (2i, 2i + 1): neighbours in a run
 #pragma unroll
         for (int j = 0; j < NSLAB * 8; ++j) {
           const float a = x[2 * j], b = x[2 * j + 1];
@@ -247,73 +275,79 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
       }
       if constexpr (NK > 0) {
 #pragma unroll
-        for (int s = 0; s < NSLAB; ++s)
+        for (int set = 0; set < NSLAB * 4; ++set) {
+          f32x4 acc = {x[4 * set], x[4 * set + 1], x[4 * set + 2], x[4 * set + 3]};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 acc = {x[16 * s + 4 * q], x[16 * s + 4 * q + 1], x[16 * s + 4 * q + 2], x[16 * s + 4 * q + 3]};
-#pragma unroll
-            for (int j = 0; j < NK; ++j)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[(s * 4 + q) * NK + j], ucur[j], acc, 0, 0, 0);
-            x[16 * s + 4 * q] = acc[0];
-            x[16 * s + 4 * q + 1] = acc[1];
-            x[16 * s + 4 * q + 2] = acc[2];
-            x[16 * s + 4 * q + 3] = acc[3];
-          }
+          for (int j = 0; j < NK; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[set * NK + j], ucur[j], acc, 0, 0, 0);
+          x[4 * set] = acc[0];
+          x[4 * set + 1] = acc[1];
+          x[4 * set + 2] = acc[2];
+          x[4 * set + 3] = acc[3];
+        }
       }
+      // MFMA layout -> LDS -> line layout
 #pragma unroll
       for (int s = 0; s < NSLAB; ++s)
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < 2; ++r) {
+          u32x4 o;
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            out[s][r][w] = pack2(x[16 * s + 8 * r + 2 * w], x[16 * s + 8 * r + 2 * w + 1]);
+          for (int w = 0; w < 4; ++w) o[w] = pack2(x[16 * s + 8 * r + 2 * w], x[16 * s + 8 * r + 2 * w + 1]);
+          *(u32x4*)(lds + c * G::RS + 16 * (8 * s + 4 * r + lg)) = o;
+        }
+      wave_lds_fence();
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) out[i] = *(const u32x4*)(lds + (i * G::RPI + lrow) * G::RS + 16 * lchunk);
+      wave_lds_fence();
     }
-    if (valid) {
-      uint16_t* row = dst_row(t);
 #pragma unroll
-      for (int s = 0; s < NSLAB; ++s)
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          *(u32x4*)(row + tc.colbase + 64 * s + 32 * r + 8 * lg) = out[s][r];
+    for (int i = 0; i < G::NI; ++i) {
+      const int t = tt + i * G::RPI + lrow;
+      if (t < T) __builtin_nontemporal_store(out[i], (u32x4*)(dst + row_offset(pages, ch.slot0, P, F, t)));
     }
-    if (tile + 1 < tc.ntiles) {
+    if (tile + 1 < ntiles) {
 #pragma unroll
-      for (int s = 0; s < NSLAB; ++s)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) cur[s][r] = nxt[s][r];
+      for (int i = 0; i < G::NI; ++i) cur[i] = nxt[i];
 #pragma unroll
       for (int j = 0; j < NK; ++j) ucur[j] = unxt[j];
     }
   }
 }
 
-template <int NSLAB, int BUDGET>
-__device__ __forceinline__ void mfma_dispatch_nk(int nk, const DevHeader& hd, const DevChunk& ch,
-                                                 const TaskCtx& tc, int layer, int tensor, int rot,
-                                                 const int* kfac, const int* kstep, int lane) {
-  // NK must satisfy NSLAB * NK <= BUDGET; the host guarantees it.
+template <int NSLAB, int NKMAX>
+__device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const DevChunk& ch, int layer,
+                                              int tensor, int colbase, int tok0, int ntiles, int rot,
+                                              const int* kfac, const int* kstep, int lane, unsigned char* lds) {
+#define KAMERA_NK_CASE(N)                                                                                   \
+  case N:                                                                                                  \
+    if constexpr (N <= NKMAX)                                                                              \
+      mfma_task<NSLAB, N>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds);       \
+    break;
   switch (nk) {
-    case 0: mfma_task<NSLAB, 0>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 1: if constexpr (NSLAB * 1 <= BUDGET) mfma_task<NSLAB, 1>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 2: if constexpr (NSLAB * 2 <= BUDGET) mfma_task<NSLAB, 2>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 3: if constexpr (NSLAB * 3 <= BUDGET) mfma_task<NSLAB, 3>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 4: if constexpr (NSLAB * 4 <= BUDGET) mfma_task<NSLAB, 4>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 5: if constexpr (NSLAB * 5 <= BUDGET) mfma_task<NSLAB, 5>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 6: if constexpr (NSLAB * 6 <= BUDGET) mfma_task<NSLAB, 6>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 7: if constexpr (NSLAB * 7 <= BUDGET) mfma_task<NSLAB, 7>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
-    case 8: if constexpr (NSLAB * 8 <= BUDGET) mfma_task<NSLAB, 8>(hd, ch, tc, layer, tensor, rot, kfac, kstep, lane); break;
+    KAMERA_NK_CASE(0)
+    KAMERA_NK_CASE(1)
+    KAMERA_NK_CASE(2)
+    KAMERA_NK_CASE(3)
+    KAMERA_NK_CASE(4)
+    KAMERA_NK_CASE(5)
+    KAMERA_NK_CASE(6)
+    KAMERA_NK_CASE(7)
+    KAMERA_NK_CASE(8)
     default: break;
   }
+#undef KAMERA_NK_CASE
 }
 
-template <int BUDGET>
+template <int NSLAB, int NKMAX>
 __global__ __launch_bounds__(kBlockThreads) void rehydrate_mfma(const DevHeader* __restrict__ hdr,
                                                                 const DevChunk* __restrict__ chunks) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerBlock * Geo<NSLAB>::LDS];
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const DevHeader& hd = *hdr;
-  const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (task >= hd.total_tasks) return;
+  const int64_t task = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
   const DevChunk& ch = chunks[find_chunk(chunks, hd.nchunks, task)];
 
   int64_t r = task - ch.task0;
@@ -322,52 +356,33 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_mfma(const DevHeader*
   const int tb = (int)(r % ch.ntb);
   r /= ch.ntb;
   const int layer = (int)(r % hd.L);
-  const int stream = (int)(r / hd.L);
-  const int tensor = ch.stream_tensor[stream];
+  const int tensor = ch.stream_tensor[(int)(r / hd.L)];
+  const int colbase = g * hd.group_cols;
+  const int tok0 = tb * ch.tb_tokens;
+  const int ntiles = (min(ch.tb_tokens, ch.T - tok0) + kTileTokens - 1) / kTileTokens;
 
-  TaskCtx tc;
-  tc.in_place = (ch.flags & 2u) != 0;
-  tc.pages = ch.pages;
-  tc.paged = ch.pages != nullptr;
-  tc.slot0 = ch.slot0;
-  tc.P = hd.page_size;
-  tc.F = hd.F;
-  tc.T = ch.T;
-  tc.colbase = g * hd.group_cols;
-  tc.tok0 = tb * ch.tb_tokens;
-  const int ntok = min(ch.tb_tokens, ch.T - tc.tok0);
-  tc.ntiles = (ntok + kTileTokens - 1) / kTileTokens;
-  tc.src = (const uint16_t*)ch.src[tensor] + (int64_t)layer * ch.src_ls;
-  tc.dst = (uint16_t*)ch.dst[tensor] + (int64_t)layer * ch.dst_ls;
-
-  const int nslab = hd.group_cols / kSlab;
-  // Does this task rotate? K (GQA) or the rope group (MLA), and only for delta != 0.
   int rot = ROT_NONE;
   const bool band = hd.family == 0 ? (tensor == 0) : (g == hd.rope_group);
-  if (band && ch.delta != 0) {
-    if (hd.pairing == 1) rot = ROT_GPTJ;
-    else rot = (hd.d_rot == 128) ? ROT_NEOX_SLABS : ROT_NEOX_RUNS;
-  }
-  // k-steps of the factors covering this group's columns
-  int kfac[8], kstep[8];
+  if (band && ch.delta != 0) rot = hd.pairing == 1 ? ROT_GPTJ : (hd.d_rot == 128 ? ROT_NEOX_SLABS : ROT_NEOX_RUNS);
+
+  // 32-wide k-steps of the factors covering this group's columns
+  int kfac[kMaxKSteps], kstep[kMaxKSteps];
   int nk = 0;
   if (ch.flags & 1u) {
     for (int f = 0; f < ch.nfac; ++f) {
       const DevFactor& fa = ch.fac[f];
       if (fa.tensor != tensor || fa.rank <= 0 || layer < fa.layer0) continue;
-      if (fa.col0 >= tc.colbase + hd.group_cols || fa.col0 + fa.width <= tc.colbase) continue;
-      for (int k = 0; k * 32 < fa.rank && nk < 8; ++k) {
+      if (fa.col0 >= colbase + hd.group_cols || fa.col0 + fa.width <= colbase) continue;
+      for (int k = 0; k * 32 < fa.rank && nk < kMaxKSteps; ++k) {
         kfac[nk] = f;
         kstep[nk] = k;
         ++nk;
       }
     }
   }
-  // In place, a group with nothing to do is left untouched.
-  if (tc.in_place && rot == ROT_NONE && nk == 0) return;
-
-  if (nslab == 2) mfma_dispatch_nk<2, BUDGET>(nk, hd, ch, tc, layer, tensor, rot, kfac, kstep, lane);
-  else mfma_dispatch_nk<1, BUDGET>(nk, hd, ch, tc, layer, tensor, rot, kfac, kstep, lane);
+  if ((ch.flags & 2u) && rot == ROT_NONE && nk == 0) return;  // in place and nothing changes
+  mfma_dispatch<NSLAB, NKMAX>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
+                              lds_all + wave * Geo<NSLAB>::LDS);
 }
 
 // ============================================================================
@@ -496,16 +511,25 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
 // ============================================================================
 // Launchers
 // ============================================================================
+template <int NSLAB, int NKMAX>
+static void launch_one(dim3 grid, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
+  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX>), grid, dim3(kBlockThreads), 0, stream, hdr, chunks);
+}
+
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                        hipStream_t stream) {
   const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kBlockThreads);
-  switch (variant) {
-    case 0: hipLaunchKernelGGL(rehydrate_mfma<2>, grid, block, 0, stream, hdr, chunks); break;
-    case 1: hipLaunchKernelGGL(rehydrate_mfma<4>, grid, block, 0, stream, hdr, chunks); break;
-    case 2: hipLaunchKernelGGL(rehydrate_mfma<8>, grid, block, 0, stream, hdr, chunks); break;
+  const dim3 grid((unsigned)blocks);
+  switch (variant) {  // variant = (nslab - 1) * 4 + log2(nk_max)
+    case 0: launch_one<1, 1>(grid, stream, hdr, chunks); break;
+    case 1: launch_one<1, 2>(grid, stream, hdr, chunks); break;
+    case 2: launch_one<1, 4>(grid, stream, hdr, chunks); break;
+    case 3: launch_one<1, 8>(grid, stream, hdr, chunks); break;
+    case 4: launch_one<2, 1>(grid, stream, hdr, chunks); break;
+    case 5: launch_one<2, 2>(grid, stream, hdr, chunks); break;
+    case 6: launch_one<2, 4>(grid, stream, hdr, chunks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
