@@ -42,7 +42,8 @@
  *   - `stream` is a hipStream_t (NULL: the null stream). Work is enqueued
  *     asynchronously; nothing is synchronised.
  *   - The library never allocates device memory. It keeps a small ring of
- *     pinned host staging buffers per device for the descriptor upload.
+ *     pinned, device-mapped host staging buffers per device; a small copy-in
+ *     kernel on `stream` moves each packed batch into the workspace.
  *
  * Errors
  *   Every entry point returns a kamera_status. Arguments are validated on the

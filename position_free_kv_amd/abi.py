@@ -218,6 +218,30 @@ def rehydrate_batched(layout: Layout, chunks: Sequence, pool: Optional[Pool], wo
                                           wp, wb, _stream(stream)))
 
 
+class PreparedBatch:
+    """The marshalled arguments of one kamera_rehydrate_batched call, built once.
+
+    `call()` re-issues the same batch (validation, upload and launch all happen
+    again in the library) with no per-call Python marshalling.
+    """
+
+    def __init__(self, layout: Layout, chunks: Sequence, pool: Optional[Pool], workspace, stream=None):
+        self._chunks = list(chunks)          # keeps block tables alive
+        self._layout = layout
+        self._pool = pool
+        self._arr, self._n = _chunk_array(self._chunks)
+        self._wp, self._wb = _ws(workspace)
+        self._stream = _stream(stream)
+        self._args = (ctypes.byref(layout), self._arr, self._n, ctypes.byref(pool) if pool else None,
+                      self._wp, self._wb, self._stream)
+        self._fn = lib().kamera_rehydrate_batched
+
+    def call(self) -> None:
+        st = self._fn(*self._args)
+        if st:
+            _check(st)
+
+
 def plan_upload(layout: Layout, chunks: Sequence, pool: Optional[Pool], workspace, stream=None) -> Plan:
     arr, n = _chunk_array(chunks)
     wp, wb = _ws(workspace)

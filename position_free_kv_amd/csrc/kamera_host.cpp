@@ -19,6 +19,7 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
                        hipStream_t stream);
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                           hipStream_t stream);
+hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
 }  // namespace kamera
 
 using namespace kamera;
@@ -48,10 +49,13 @@ size_t ws_bytes(int64_t nchunks, int64_t pages) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ------------------------------------------------------------------ staging ring
-// Pinned host buffers used as the source of the stream-ordered descriptor copy.
-// A slot is reused only after the copy that last read it has completed.
+// Pinned, device-mapped host buffers holding packed batches. A small copy-in
+// kernel on the caller's stream moves a batch into the device workspace (a
+// copy-engine transfer would add a cross-engine handoff to every call). A slot
+// is reused only after the copy-in that last read it has completed.
 struct Slot {
   void* host = nullptr;
+  void* dev = nullptr;  // device view of `host`
   size_t cap = 0;
   hipEvent_t done = nullptr;
   bool pending = false;
@@ -79,18 +83,23 @@ kamera_status upload(const void* src, size_t bytes, void* dst, hipStream_t strea
   }
   if (s.cap < bytes) {
     if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
+    s.host = s.dev = nullptr;
     s.cap = 0;
     const size_t cap = std::max(round_up(bytes, 64 * 1024), (size_t)64 * 1024);
-    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
+    if (hipHostMalloc(&s.host, cap, hipHostMallocMapped) != hipSuccess)
       return fail(KAMERA_E_HIP, "hipHostMalloc(%zu) failed", cap);
+    if (hipHostGetDevicePointer(&s.dev, s.host, 0) != hipSuccess) {
+      (void)hipHostFree(s.host);
+      s.host = nullptr;
+      return fail(KAMERA_E_HIP, "hipHostGetDevicePointer failed");
+    }
     s.cap = cap;
   }
   if (!s.done && hipEventCreateWithFlags(&s.done, hipEventDisableTiming) != hipSuccess)
     return fail(KAMERA_E_HIP, "hipEventCreate failed");
   std::memcpy(s.host, src, bytes);
-  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return fail(KAMERA_E_HIP, "hipMemcpyAsync of %zu descriptor bytes failed", bytes);
+  const hipError_t e = launch_copy_in(dst, s.dev, bytes, stream);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "descriptor copy-in launch failed: %s", hipGetErrorString(e));
   if (hipEventRecord(s.done, stream) != hipSuccess) return fail(KAMERA_E_HIP, "hipEventRecord failed");
   s.pending = true;
   return KAMERA_OK;
@@ -128,8 +137,8 @@ int row_width(const kamera_layout* L) {
 }
 
 struct Packed {
-  std::vector<unsigned char> blob;  // header | chunks | pages
-  std::vector<int64_t> page_off;    // per chunk: offset (entries) of its page table, -1 if dense
+  std::vector<unsigned char>& blob;  // header | chunks | pages (thread-local, reused across calls)
+  std::vector<int64_t>& page_off;    // per chunk: offset (entries) of its page table, -1 if dense
   size_t bytes = 0;
   int64_t tasks = 0;
   int kernel = 0;   // 0 none, 1 mfma, 2 generic
@@ -179,8 +188,15 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   // -------------------------------------------------------------- per-chunk checks
   bool mfma = mfma_layout_ok(L);
   int need_ksteps = 0;  // MFMA path: most 32-wide k-steps covering any column group
-  std::vector<uint8_t> slot_used;
-  if (any_paged) slot_used.assign((size_t)pool->num_pages * P, 0);
+  // Pool slots written by this batch: one bit per slot, kept per page as a mask
+  // (pages of up to 64 slots), so the overlap check costs O(pages), not O(tokens).
+  thread_local std::vector<uint64_t> page_mask;
+  thread_local std::vector<uint8_t> slot_used;
+  const bool mask_mode = P <= 64;
+  if (any_paged) {
+    if (mask_mode) page_mask.assign((size_t)pool->num_pages, 0);
+    else slot_used.assign((size_t)pool->num_pages * P, 0);
+  }
 
   for (int i = 0; i < n; ++i) {
     const kamera_chunk& c = chunks[i];
@@ -218,13 +234,26 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
           return fail(KAMERA_E_PAGE, "chunk %d: block_table[%lld] = %d outside [0, %d)", i, (long long)k, pg,
                       pool->num_pages);
       }
-      for (int64_t t = 0; t < T; ++t) {
-        const int64_t s = c.slot0 + t;
-        const size_t slot = (size_t)c.block_table[s / P] * P + (size_t)(s % P);
-        if (slot_used[slot])
-          return fail(KAMERA_E_OVERLAP, "chunk %d token %lld: pool page %d offset %lld already written in this batch",
-                      i, (long long)t, c.block_table[s / P], (long long)(s % P));
-        slot_used[slot] = 1;
+      if (mask_mode) {
+        for (int64_t k = 0; k < np; ++k) {
+          const int64_t lo = std::max<int64_t>(c.slot0 - k * P, 0);
+          const int64_t hi = std::min<int64_t>(c.slot0 + T - k * P, P);
+          const uint64_t m = (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)) << lo;
+          uint64_t& pm = page_mask[(size_t)c.block_table[k]];
+          if (pm & m)
+            return fail(KAMERA_E_OVERLAP, "chunk %d: pool page %d has slots already written in this batch", i,
+                        c.block_table[k]);
+          pm |= m;
+        }
+      } else {
+        for (int64_t t = 0; t < T; ++t) {
+          const int64_t s = c.slot0 + t;
+          const size_t slot = (size_t)c.block_table[s / P] * P + (size_t)(s % P);
+          if (slot_used[slot])
+            return fail(KAMERA_E_OVERLAP, "chunk %d token %lld: pool page %d offset %lld already written in this batch",
+                        i, (long long)t, c.block_table[s / P], (long long)(s % P));
+          slot_used[slot] = 1;
+        }
       }
       if (mfma && (!aligned(pool->k_pool, 16) || (pool->v_pool && !aligned(pool->v_pool, 16)) ||
                    pool->layer_stride % 8))
@@ -401,7 +430,9 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
 
 kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
                           void* ws, size_t ws_size, void* stream, kamera_plan* plan) {
-  Packed pk;
+  thread_local std::vector<unsigned char> blob;
+  thread_local std::vector<int64_t> page_off;
+  Packed pk{blob, page_off};
   kamera_status st = pack_batch(L, chunks, n, pool, pk);
   if (st != KAMERA_OK) return st;
   if (!ws) return fail(KAMERA_E_WORKSPACE, "workspace is NULL");

@@ -97,16 +97,6 @@ __device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ pages,
 // layouts are bank-conflict free) turns line layout into the MFMA layout and
 // back. V^T operands and cos/sin stay in registers for the whole task.
 
-// Workgroups are dispatched round-robin over the 8 XCDs (id b runs on XCD b % 8).
-// Give each XCD a contiguous run of task ids, so that tasks sharing a head's V^T
-// (consecutive token blocks) and a block's U (consecutive groups) meet in one
-// L2. Only locality depends on this; any mapping is correct.
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
-  const int64_t q = n / 8, r = n % 8;
-  const int64_t x = b % 8, l = b / 8;
-  return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
-}
-
 __device__ __forceinline__ void wave_lds_fence() {
   // LDS traffic of one wave is processed in order; this only stops the compiler
   // from moving LDS accesses across the hand-off between the two layouts.
@@ -346,7 +336,8 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_mfma(const DevHeader*
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const DevHeader& hd = *hdr;
-  const int64_t task = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  // plain dispatch order: waves running together stream neighbouring rows
+  const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
   const DevChunk& ch = chunks[find_chunk(chunks, hd.nchunks, task)];
 
@@ -509,8 +500,26 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
 }
 
 // ============================================================================
+// Descriptor copy-in: packed batch from mapped pinned host memory to the workspace
+// ============================================================================
+__global__ __launch_bounds__(kBlockThreads) void copy_in(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+// ============================================================================
 // Launchers
 // ============================================================================
+hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);  // packed batches are multiples of 256 bytes
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = (n16 + kBlockThreads - 1) / kBlockThreads;
+  hipLaunchKernelGGL(copy_in, dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream, (const u32x4*)src,
+                     (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
 template <int NSLAB, int NKMAX>
 static void launch_one(dim3 grid, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
   hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX>), grid, dim3(kBlockThreads), 0, stream, hdr, chunks);

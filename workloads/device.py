@@ -164,6 +164,10 @@ class DeviceWorkload:
         descs = self.descs if chunks is None else [self.descs[i] for i in chunks]
         abi.rehydrate_batched(self.layout, descs, self.pool_desc, self.workspace, stream)
 
+    def prepared(self, stream=None) -> abi.PreparedBatch:
+        """The whole batch marshalled once; .call() issues it again."""
+        return abi.PreparedBatch(self.layout, self.descs, self.pool_desc, self.workspace, stream)
+
     def plan(self, stream=None) -> abi.Plan:
         return abi.plan_upload(self.layout, self.descs, self.pool_desc, self.workspace, stream)
 
