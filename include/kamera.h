@@ -10,9 +10,11 @@
  *   R(delta)   exact RoPE phase re-rotation of the stored keys' rotary band by
  *              delta = p1 - p0 (preprint §3 "Relocate"); V and the MLA latent
  *              c_KV are never rotated.
- *   U_m V_m^T  rank-m conditioning patch, stored as U*Sigma [T][m] and
- *              V^T [m][width] (preprint App. A compile listing; Fig. 2(d)),
- *              added after the rotation (preprint App. A serve listing).
+ *   U_m V_m^T  rank-m conditioning patch, stored as the two tall factors
+ *              U*Sigma [T][m] and V [width][m] (preprint App. A: the compile
+ *              listing keeps U[:, :m]*S[:m] and the top-m right singular
+ *              vectors; the serve listing applies U @ V^T), added after the
+ *              rotation (preprint App. A serve listing).
  *
  * Layout families (preprint §3, Fig. 2):
  *   KAMERA_GQA  rows of K and of V, F = num_kv_heads * head_dim; every key head
@@ -103,10 +105,12 @@ typedef struct kamera_layout {
   double rope_base;      /* RoPE base (> 0, finite), e.g. 1e4 or 1e6                      */
 } kamera_layout;
 
-/* One stored factor pair of a chunk (preprint App. A: U[:, :m]*S[:m], Vt[:m]). */
+/* One stored factor pair of a chunk (preprint App. A: U[:, :m]*S[:m] and V_m; the
+ * patch added to the rows is U V^T). Both factors keep a row's m coefficients
+ * contiguous: V is the transpose of the V^T [m][width] of Fig. 2(d). */
 typedef struct kamera_factor {
   const void* u;         /* device [L - layer0][T][rank]: U*Sigma, row-major               */
-  const void* vt;        /* device [L - layer0][rank][width]: V^T, row-major               */
+  const void* v;         /* device [L - layer0][width][rank]: V, row-major                 */
   int32_t tensor;        /* 0: K (GQA) or the MLA row; 1: V (GQA only)                     */
   int32_t col0;          /* first patched column of that tensor's row                     */
   int32_t width;         /* patched columns [col0, col0 + width), within the row          */

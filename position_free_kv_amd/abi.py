@@ -37,7 +37,7 @@ class Layout(ctypes.Structure):
 
 
 class Factor(ctypes.Structure):
-    _fields_ = [("u", ctypes.c_void_p), ("vt", ctypes.c_void_p), ("tensor", ctypes.c_int32),
+    _fields_ = [("u", ctypes.c_void_p), ("v", ctypes.c_void_p), ("tensor", ctypes.c_int32),
                 ("col0", ctypes.c_int32), ("width", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("layer0", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
@@ -156,7 +156,7 @@ class ChunkDesc:
             raise ValueError(f"at most {MAX_FACTORS} factors per chunk")
         c.num_factors = len(factors)
         for i, f in enumerate(factors):
-            c.factors[i] = Factor(_ptr(f["u"]), _ptr(f["vt"]), int(f.get("tensor", 0)), int(f.get("col0", 0)),
+            c.factors[i] = Factor(_ptr(f["u"]), _ptr(f["v"]), int(f.get("tensor", 0)), int(f.get("col0", 0)),
                                   int(f["width"]), int(f["rank"]), int(f.get("layer0", 0)), 0)
         self.c = c
 

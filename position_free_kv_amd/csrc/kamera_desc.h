@@ -14,20 +14,22 @@ constexpr int kTileTokens = 16;    // tokens per MFMA tile (the N dimension)
 constexpr int kMaxFactors = 4;
 
 // MFMA path: a wave task covers a column group of 1 or 2 slabs and holds up to
-// kMaxKSteps 32-wide k-steps of V^T operands in registers. Kernel variant
+// kMaxKSteps 32-wide k-steps of V operands in registers. Kernel variant
 // v = (slabs - 1) * 4 + log2(k-step capacity), capacity in {1, 2, 4, 8}.
 constexpr int kMaxKSteps = 8;
 constexpr int kMfmaRangeTokens = 128;  // tokens per wave task (8 tiles)
 
 struct alignas(16) DevFactor {
   const void* u;        // [L - layer0][T][rank]
-  const void* vt;       // [L - layer0][rank][width]
+  const void* v;        // [L - layer0][width][rank]
   int32_t tensor;
   int32_t col0;
   int32_t width;
   int32_t rank;
   int32_t layer0;
-  int32_t pad[3];
+  int32_t uvec;         // rank % 8 == 0 and u 16-byte aligned: 16-byte loads of U rows
+  int32_t vvec;         // rank % 8 == 0 and v 16-byte aligned: 16-byte loads of V rows
+  int32_t pad;
 };
 static_assert(sizeof(DevFactor) == 48, "DevFactor layout");
 

@@ -283,8 +283,8 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
                       fa.col0 + fa.width, F);
         if (fa.layer0 < 0 || fa.layer0 >= L->num_layers)
           return fail(KAMERA_E_SHAPE, "chunk %d factor %d: layer0 outside [0, L)", i, f);
-        if (!fa.u || !fa.vt) return fail(KAMERA_E_NULL, "chunk %d factor %d: u or vt is NULL", i, f);
-        if (!aligned(fa.u, es) || !aligned(fa.vt, es))
+        if (!fa.u || !fa.v) return fail(KAMERA_E_NULL, "chunk %d factor %d: u or v is NULL", i, f);
+        if (!aligned(fa.u, es) || !aligned(fa.v, es))
           return fail(KAMERA_E_ALIGN, "chunk %d factor %d: factor pointers must be aligned to %zu bytes", i, f, es);
       }
       // MFMA path: k-steps of the factors covering each column group
@@ -305,7 +305,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
       }
     }
   }
-  // 128-wide groups keep at most 4 k-steps of V^T operands in registers
+  // 128-wide groups keep at most 4 k-steps of V operands in registers
   if (mfma && need_ksteps > (L->family == KAMERA_GQA && L->head_dim == 128 ? kMaxKSteps / 2 : kMaxKSteps))
     mfma = false;
 
@@ -380,13 +380,14 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
       const kamera_factor& fa = c.factors[f];
       DevFactor& df = d.fac[f];
       df.u = fa.u;
-      df.vt = fa.vt;
+      df.v = fa.v;
       df.tensor = fa.tensor;
       df.col0 = fa.col0;
       df.width = fa.width;
       df.rank = fa.rank;
       df.layer0 = fa.layer0;
-      df.pad[0] = (fa.rank % 8 == 0 && aligned(fa.u, 16)) ? 1 : 0;
+      df.uvec = (fa.rank % 8 == 0 && aligned(fa.u, 16)) ? 1 : 0;
+      df.vvec = (fa.rank % 8 == 0 && aligned(fa.v, 16)) ? 1 : 0;
       if (fa.tensor == 1 && fa.rank > 0) v_factor = true;
     }
     // streams: tensors this chunk touches

@@ -27,7 +27,8 @@
 //   The MFMA result layout gives lane (lg, c) rows M = 4lg + [0,4) of column c.
 //   Tile q of slab s maps row M to column 64s + 32(q>>1) + 8(M>>2) + 4(q&1) + (M&3),
 //   so the 4 tiles x 4 values of a lane are exactly its two loaded runs. The
-//   V^T operand is staged once per workgroup with that same column map.
+//   V operand (one 16-byte read of a V row per tile and k-step) is loaded once
+//   per task with that same column map.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,7 +96,7 @@ __device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ pages,
 // 128-byte line is touched by one instruction and the stream can bypass the
 // caches (nontemporal). A per-wave LDS tile (rows padded by 16 B so both
 // layouts are bank-conflict free) turns line layout into the MFMA layout and
-// back. V^T operands and cos/sin stay in registers for the whole task.
+// back. V operands and cos/sin stay in registers for the whole task.
 
 __device__ __forceinline__ void wave_lds_fence() {
   // LDS traffic of one wave is processed in order; this only stops the compiler
@@ -149,7 +150,7 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
     }
   }
 
-  // ---- V^T operands: A[M][k] = Vt[k][col(M)] for every slab, tile and k-step
+  // ---- V operands: A[M][k] = V[col(M)][k] for every slab, tile and k-step
   bf16x8 av[NK > 0 ? NSLAB * 4 * NK : 1];
   const uint16_t* ubase[NK > 0 ? NK : 1];
   int urank[NK > 0 ? NK : 1], ustride[NK > 0 ? NK : 1];
@@ -158,12 +159,13 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   for (int j = 0; j < NK; ++j) {
     const DevFactor& f = ch.fac[kfac[j]];
     const int64_t lrel = layer - f.layer0;
-    const uint16_t* vt = (const uint16_t*)f.vt + lrel * f.rank * f.width;
+    const uint16_t* vf = (const uint16_t*)f.v + lrel * f.width * f.rank;
     ubase[j] = (const uint16_t*)f.u + lrel * T * f.rank + 32 * kstep[j] + 8 * lg;
     urank[j] = f.rank - 32 * kstep[j] - 8 * lg;
     ustride[j] = f.rank;
-    uvec[j] = f.pad[0] != 0;
+    uvec[j] = f.uvec != 0;
     const int mrow = lane & 15, kg = lane >> 4;
+    const int k0 = 32 * kstep[j] + 8 * kg;   // first k of this lane's 8
 #pragma unroll
     for (int s = 0; s < NSLAB; ++s)
 #pragma unroll
@@ -172,11 +174,14 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
         const int rel = col - f.col0;
         const bool in = rel >= 0 && rel < f.width;
         bf16x8 a;
+        if (in && f.vvec && k0 + 8 <= f.rank) {
+          a = *(const bf16x8*)(vf + (int64_t)rel * f.rank + k0);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 32 * kstep[j] + 8 * kg + e;
-          const uint16_t h = (in && k < f.rank) ? vt[(int64_t)k * f.width + rel] : (uint16_t)0;
-          a[e] = __builtin_bit_cast(__bf16, h);
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t h = (in && k0 + e < f.rank) ? vf[(int64_t)rel * f.rank + k0 + e] : (uint16_t)0;
+            a[e] = __builtin_bit_cast(__bf16, h);
+          }
         }
         av[(s * 4 + q) * NK + j] = a;
       }
@@ -399,8 +404,8 @@ __device__ __forceinline__ float add_patch(const DevChunk& ch, int layer, int te
     if (f.tensor != tensor || layer < f.layer0 || col < f.col0 || col >= f.col0 + f.width) continue;
     const int64_t lrel = layer - f.layer0;
     const int64_t ub = lrel * ch.T * f.rank + (int64_t)t * f.rank;
-    const int64_t vb = lrel * f.rank * f.width + (col - f.col0);
-    for (int j = 0; j < f.rank; ++j) acc = fmaf(ld<T>(f.u, ub + j), ld<T>(f.vt, vb + (int64_t)j * f.width), acc);
+    const int64_t vb = lrel * f.width * f.rank + (int64_t)(col - f.col0) * f.rank;
+    for (int j = 0; j < f.rank; ++j) acc = fmaf(ld<T>(f.u, ub + j), ld<T>(f.v, vb + j), acc);
   }
   return acc;
 }

@@ -1,0 +1,120 @@
+"""Summarise rocprofv3 output of bench.py into profiles/ (kernel time and HBM bytes).
+
+Produce the raw output with three runs of the committed bench (one for the
+kernel trace, one per counter, as rocprofv3 collects counters in runs of their
+own), then summarise:
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c2 -- \\
+        python3 bench.py --steps 200 --warmup 20 --no-cpu
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o c2 -- \\
+        python3 bench.py --steps 5 --warmup 1 --no-cpu
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/prof_write -o c2 -- \\
+        python3 bench.py --steps 5 --warmup 1 --no-cpu
+    python3 profile_summary.py OUT C2
+
+HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what
+the same counter reads for bench.py's plain 1 GiB device copy (reads 1 GiB,
+writes 1 GiB), so the figure is in bytes the memory system actually moved.
+"""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL = "kamera::rehydrate_mfma"
+COPY_BYTES = 1 << 30
+
+
+def _rows(path):
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_kernel(rows):
+    agg = defaultdict(list)
+    for r in rows:
+        agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _copy_kib(agg):
+    """Counter of the bench's 1 GiB copy: the copy kernel with the largest grid."""
+    cands = [(g, v) for (k, g), v in agg.items() if "copyBuffer" in k or "copy" in k.lower() and "kamera" not in k]
+    g, v = max(cands, key=lambda x: x[0])
+    return sum(v) / len(v)
+
+
+def _kernel_kib(agg):
+    vals = [v for (k, g), vs in agg.items() if KERNEL in k for v in vs]
+    return sum(vals) / len(vals), len(vals)
+
+
+def main(out: str, cfg: str) -> None:
+    stats = _rows(os.path.join(out, "prof_trace", "c2_kernel_stats.csv"))
+    bench = json.loads(open(os.path.join(out, "prof_trace_bench.json")).read())
+    fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", "c2_counter_collection.csv")))
+    write = _per_kernel(_rows(os.path.join(out, "prof_write", "c2_counter_collection.csv")))
+    f_copy, w_copy = _copy_kib(fetch), _copy_kib(write)
+    f_scale, w_scale = (COPY_BYTES / 1024) / f_copy, (COPY_BYTES / 1024) / w_copy
+    f_k, nf = _kernel_kib(fetch)
+    w_k, nw = _kernel_kib(write)
+    fetch_b = f_k * 1024 * f_scale
+    write_b = w_k * 1024 * w_scale
+    main_row = next(r for r in stats if KERNEL in r["Name"])
+    avg_us = float(main_row["AverageNs"]) / 1e3
+    alg = bench["algorithmic_bytes"]
+
+    lines = [
+        f"# rocprofv3 summary: {KERNEL} on the {cfg} workload",
+        "",
+        f"workload: {bench['config']['workload']}",
+        f"kernel source hash: {bench['kernel_source_hash']}",
+        "",
+        "## kernel trace (rocprofv3 --kernel-trace --stats)",
+        "",
+        "command: rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c2 -- "
+        "python3 bench.py --steps 200 --warmup 20 --no-cpu",
+        "",
+        "| kernel | calls | average us | min us | max us | share of GPU time |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in stats[:6]:
+        name = r["Name"].split("(")[0]
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} "
+                     f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += [
+        "",
+        f"bench.py's own HIP-event figure for the same kernel in the same run: {bench['kernel_us']:.1f} us "
+        f"(rocprofv3 average {avg_us:.1f} us).",
+        "",
+        "## HBM bytes (rocprofv3 --pmc, one counter per run)",
+        "",
+        "commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write -o c2 -- "
+        "python3 bench.py --steps 5 --warmup 1 --no-cpu",
+        "",
+        "| counter | plain 1 GiB copy (KiB/dispatch) | scale to bytes | kernel (KiB/dispatch, mean of n) | kernel bytes |",
+        "|---|---|---|---|---|",
+        f"| FETCH_SIZE | {f_copy:.0f} | x{f_scale:.3f} | {f_k:.0f} (n={nf}) | {fetch_b / 1e6:.1f} MB |",
+        f"| WRITE_SIZE | {w_copy:.0f} | x{w_scale:.3f} | {w_k:.0f} (n={nw}) | {write_b / 1e6:.1f} MB |",
+        "",
+        f"measured HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB; algorithmic: {alg / 1e6:.1f} MB "
+        f"(ratio {(fetch_b + write_b) / alg:.3f})",
+        f"measured bandwidth: {(fetch_b + write_b) / (avg_us * 1e-6) / 1e9:.0f} GB/s; algorithmic: "
+        f"{alg / (avg_us * 1e-6) / 1e9:.0f} GB/s of 8000 ({alg / (avg_us * 1e-6) / 8e12:.1%})",
+    ]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"rehydrate_mfma_{cfg}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", f"traffic_{cfg}.json"), "w") as fh:
+        json.dump({"kernel_source_hash": bench["kernel_source_hash"], "hbm_bytes_per_launch": fetch_b + write_b,
+                   "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
+                   "rocprof_avg_us": avg_us}, fh, indent=1)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else "C2")

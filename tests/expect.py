@@ -37,11 +37,12 @@ def oracle_factors(wl: Workload, ch: ChunkSpec, layer: int, rows: Optional[Seque
     for fi, f in enumerate(ch.factors):
         if layer < f.layer0:
             continue
-        u, vt = wl.factor(ch, fi, layer)
+        u, v = wl.factor(ch, fi, layer)
         u64 = O.upcast(u, wl.layout.dtype)
         if rows is not None:
             u64 = u64[np.asarray(rows)]
-        out.append(O.Factor(f.tensor, f.col0, u64, O.upcast(vt, wl.layout.dtype)))
+        # the oracle takes the right factor as V^T [m][width]
+        out.append(O.Factor(f.tensor, f.col0, u64, O.upcast(v, wl.layout.dtype).T))
     return out
 
 

@@ -62,7 +62,7 @@ def gqa_layout(**kw):
 
 def chunk(**kw):
     d = dict(num_tokens=32, delta=100, flags=abi.PATCH, k_src=FAKE, v_src=FAKE + 0x100000, k_dst=FAKE + 0x200000,
-             v_dst=FAKE + 0x300000, factors=[dict(u=FAKE + 0x400000, vt=FAKE + 0x500000, tensor=0, width=512, rank=32)])
+             v_dst=FAKE + 0x300000, factors=[dict(u=FAKE + 0x400000, v=FAKE + 0x500000, tensor=0, width=512, rank=32)])
     d.update(kw)
     return abi.ChunkDesc(**d)
 
@@ -129,13 +129,13 @@ def test_validation_errors(case, expect):
     elif case == "delta_2_31":
         f = lambda: run(cs=[chunk(delta=2 ** 31)])
     elif case == "rank_too_big":
-        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, width=512, rank=abi.MAX_RANK + 1)])])
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, v=FAKE, width=512, rank=abi.MAX_RANK + 1)])])
     elif case == "factor_cols_outside":
-        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, col0=500, width=64, rank=8)])])
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, v=FAKE, col0=500, width=64, rank=8)])])
     elif case == "factor_null":
-        f = lambda: run(cs=[chunk(factors=[dict(u=None, vt=FAKE, width=512, rank=8)])])
+        f = lambda: run(cs=[chunk(factors=[dict(u=None, v=FAKE, width=512, rank=8)])])
     elif case == "factor_bad_tensor":
-        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, vt=FAKE, tensor=2, width=512, rank=8)])])
+        f = lambda: run(cs=[chunk(factors=[dict(u=FAKE, v=FAKE, tensor=2, width=512, rank=8)])])
     elif case == "null_src":
         f = lambda: run(cs=[chunk(v_src=None)])
     elif case == "null_dst":

@@ -29,10 +29,10 @@ def test_generators_are_deterministic_and_addressable():
     assert [c.delta for c in a.chunks] == [c.delta for c in b.chunks]
     assert np.array_equal(a.canonical(1, 1, 0), b.canonical(1, 1, 0))
     assert not np.array_equal(a.canonical(1, 1, 0), a.canonical(1, 0, 0))
-    u1, vt1 = a.factor(a.chunks[0], 0, 1)
-    u2, vt2 = b.factor(b.chunks[0], 0, 1)
-    assert np.array_equal(u1, u2) and np.array_equal(vt1, vt2)
-    assert u1.dtype == np.uint16 and u1.shape == (64, 32) and vt1.shape == (32, 512)
+    u1, v1 = a.factor(a.chunks[0], 0, 1)
+    u2, v2 = b.factor(b.chunks[0], 0, 1)
+    assert np.array_equal(u1, u2) and np.array_equal(v1, v2)
+    assert u1.dtype == np.uint16 and u1.shape == (64, 32) and v1.shape == (512, 32)
 
 
 def test_outlier_channels_and_orthonormal_factors():
@@ -42,7 +42,8 @@ def test_outlier_channels_and_orthonormal_factors():
     k = w.canonical(0, 0, 0).astype(np.uint32) << 16
     kf = k.view(np.float32)
     assert np.std(kf[:, cols]) > 5 and abs(np.std(np.delete(kf, cols, axis=1)) - 1) < 0.05
-    u, vt = w._factor_fp64(w.chunks[0].factors[0], 1024, 0)
+    u, v = w._factor_fp64(w.chunks[0].factors[0], 1024, 0)
+    vt = v.T
     s = np.linalg.svd(u, compute_uv=False)
     assert np.allclose(s, 0.3 * 0.9 ** np.arange(32), rtol=1e-10)
     assert np.allclose(vt @ vt.T, np.eye(32), atol=1e-12)

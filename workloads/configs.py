@@ -175,14 +175,15 @@ class Workload:
             return q * np.sign(np.diag(r))[None, :]
         q1 = orth(T, f.rank)
         q2 = orth(f.width, f.rank)
-        return q1 * f.sigma[None, :], np.ascontiguousarray(q2.T)
+        return q1 * f.sigma[None, :], q2
 
     def factor(self, chunk: ChunkSpec, fi: int, layer: int):
-        """(U.Sigma [T][m], V^T [m][width]) of factor fi at `layer`, in storage dtype."""
+        """(U.Sigma [T][m], V [width][m]) of factor fi at `layer`, in storage dtype;
+        the patch they encode is U V^T."""
         f = chunk.factors[fi]
-        u, vt = self._factor_fp64(f, chunk.num_tokens, layer)
+        u, v = self._factor_fp64(f, chunk.num_tokens, layer)
         return (self._to_storage(u.astype(np.float32)),
-                self._to_storage(vt.astype(np.float32)))
+                self._to_storage(v.astype(np.float32)))
 
     @property
     def total_tokens(self) -> int:

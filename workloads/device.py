@@ -57,7 +57,7 @@ class DeviceWorkload:
             f = c.factors[fi]
             nl = self.L - f.layer0
             self.factors[key] = (torch.empty((nl, c.num_tokens, f.rank), dtype=self.tdtype, device=self.device),
-                                 torch.empty((nl, f.rank, f.width), dtype=self.tdtype, device=self.device))
+                                 torch.empty((nl, f.width, f.rank), dtype=self.tdtype, device=self.device))
         # dense destinations and pool, sentinel filled
         self.dense = [[_sentinel_fill(torch.empty((self.L, rows, self.F), dtype=self.tdtype, device=self.device),
                                       lay.dtype) for _ in range(nt)] for rows in wl.dense_rows]
@@ -153,8 +153,8 @@ class DeviceWorkload:
         if c.patched:
             fl = []
             for f in c.factors:
-                u, vt = self.factors[(f.key, f.slot)]
-                fl.append(dict(u=u, vt=vt, tensor=f.tensor, col0=f.col0, width=f.width, rank=f.rank,
+                u, v = self.factors[(f.key, f.slot)]
+                fl.append(dict(u=u, v=v, tensor=f.tensor, col0=f.col0, width=f.width, rank=f.rank,
                                layer0=f.layer0))
             kw["factors"] = fl
         return abi.ChunkDesc(**kw)
