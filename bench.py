@@ -13,6 +13,7 @@ launch stream, and the fp64 CPU oracle's throughput on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -86,7 +87,8 @@ def _oracle_units(args):
 def cpu_baseline(cfg: str, wl, sample_units: int):
     import multiprocessing as mp
     cores = max(1, min(16, os.cpu_count() or 1))
-    units = [(ci, layer) for ci in range(len(wl.chunks)) for layer in range(wl.layout.num_layers)][:sample_units]
+    all_units = [(ci, layer) for ci in range(len(wl.chunks)) for layer in range(wl.layout.num_layers)]
+    units = [all_units[i % len(all_units)] for i in range(sample_units)]
     parts = [(cfg, units[i::cores]) for i in range(cores) if units[i::cores]]
     ctx = mp.get_context("fork")
     with ctx.Pool(len(parts)) as pool:
@@ -105,10 +107,11 @@ def cpu_baseline(cfg: str, wl, sample_units: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-units", type=int, default=224, help="(chunk, layer) units timed on the CPU oracle")
+    ap.add_argument("--cpu-units", type=int, default=448,
+                    help="(chunk, layer) units timed on the CPU oracle (the workload repeats past its 224 units)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
     args = ap.parse_args()
@@ -146,6 +149,8 @@ def main() -> int:
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     # ---- whole calls (validation + descriptor upload + kernel): the step
+    gc.collect()
+    gc.disable()   # no collector pauses inside the timed loops
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -167,6 +172,7 @@ def main() -> int:
     e3.record(stream)
     torch.cuda.synchronize()
     kernel_us = e2.elapsed_time(e3) / args.steps * 1e3
+    gc.enable()
 
     # ---- a plain device copy of known size: practical read+write ceiling, and the
     # reference kernel for scaling the HBM byte counters

@@ -20,8 +20,10 @@ LIB = os.path.join(HERE, "libkamera.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = os.environ.get("KAMERA_OFFLOAD_ARCH", "gfx950")
 
-# Packed fp32 VALU forms stay disabled: plain fp32 code only.
-HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms stay disabled: plain fp32 code only. MFMA accumulators stay
+# in ordinary VGPRs, so the independent 16x16 tiles of a task issue back to back
+# instead of being funnelled through one set of accumulation registers.
+HIP_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

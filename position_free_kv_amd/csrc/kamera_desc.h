@@ -7,8 +7,12 @@
 namespace kamera {
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
+constexpr int kBlockThreads = 256;           // generic and copy-in kernels
+// MFMA path: 8 waves per workgroup. Consecutive wave tasks are the heads of one
+// token block and the next block, so a workgroup's waves share U rows (4 heads)
+// and V rows (2 blocks) through the CU's caches; measured faster than 4 or 16.
+constexpr int kWavesPerBlock = 8;
+constexpr int kMfmaBlockThreads = kWaveSize * kWavesPerBlock;
 constexpr int kSlab = 64;          // columns per slab of the MFMA path
 constexpr int kTileTokens = 16;    // tokens per MFMA tile (the N dimension)
 constexpr int kMaxFactors = 4;

@@ -335,7 +335,7 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 }
 
 template <int NSLAB, int NKMAX>
-__global__ __launch_bounds__(kBlockThreads) void rehydrate_mfma(const DevHeader* __restrict__ hdr,
+__global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHeader* __restrict__ hdr,
                                                                 const DevChunk* __restrict__ chunks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerBlock * Geo<NSLAB>::LDS];
   const int lane = threadIdx.x & (kWaveSize - 1);
@@ -527,7 +527,7 @@ hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t 
 
 template <int NSLAB, int NKMAX>
 static void launch_one(dim3 grid, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
-  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX>), grid, dim3(kBlockThreads), 0, stream, hdr, chunks);
+  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX>), grid, dim3(kMfmaBlockThreads), 0, stream, hdr, chunks);
 }
 
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
