@@ -114,6 +114,7 @@ def main() -> int:
                     help="(chunk, layer) units timed on the CPU oracle (the workload repeats past its 224 units)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
+    ap.add_argument("--rank", type=int, default=None, help="override the patch rank m of the workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
@@ -122,7 +123,7 @@ def main() -> int:
         return 2
 
     from workloads import make_workload
-    wl = make_workload(args.config)
+    wl = make_workload(args.config, rank=args.rank)
     # The CPU oracle leg forks worker processes, so it runs before this process
     # touches the GPU (forking a process whose HIP runtime threads are live can deadlock).
     cpu = None
@@ -211,7 +212,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) canonical KV, orthonormal factors with geometric spectra",
-        "config": {"workload": WORKLOADS[args.config], "name": args.config, "chunks": len(wl.chunks),
+        "config": {"workload": WORKLOADS[args.config] + ("" if args.rank is None else f" (rank overridden: m={args.rank})"),
+                   "name": args.config, "chunks": len(wl.chunks),
                    "tokens": tokens, "layers": wl.layout.num_layers, "row_width": wl.layout.row_width},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},

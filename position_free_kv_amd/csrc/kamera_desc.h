@@ -64,6 +64,7 @@ struct alignas(16) DevChunk {
 };
 
 struct alignas(16) DevHeader {
+  uint32_t zeros[4];    // 16 zero bytes: operand reads of lanes with no data point here
   int64_t total_tasks;
   int32_t nchunks;
   int32_t family;
@@ -80,7 +81,8 @@ struct alignas(16) DevHeader {
   int32_t group_cols;   // MFMA path: columns per group (64 or 128)
   int32_t rope_group;   // MFMA path, MLA: group id of the rope band (-1 for GQA)
   double rope_base;
-  int32_t pad[2];
+  int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
+  int32_t pad;
 };
 
 }  // namespace kamera

@@ -328,6 +328,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   hd->d_rot = d_rot;
   hd->pairing = L->pairing;
   hd->page_size = P;
+  hd->page_shift = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
   hd->rope_base = L->rope_base;
   hd->group_cols = mfma ? (L->family == KAMERA_GQA ? L->head_dim : kSlab) : F;
   hd->rope_group = (mfma && L->family == KAMERA_MLA) ? L->latent_dim / kSlab : -1;

@@ -78,6 +78,27 @@ __device__ __forceinline__ int find_chunk(const DevChunk* __restrict__ chunks, i
   return lo;
 }
 
+struct TaskCoord {
+  int chunk, layer, stream, tb, g;
+};
+
+// (chunk, layer, stream, token block, group) of a task:
+//   task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+__device__ __forceinline__ TaskCoord decode_task(const DevHeader& hd, const DevChunk* __restrict__ chunks,
+                                                 int64_t task) {
+  TaskCoord tc;
+  tc.chunk = find_chunk(chunks, hd.nchunks, task);
+  const DevChunk& ch = chunks[tc.chunk];
+  int64_t r = task - ch.task0;
+  tc.g = ch.group0 + (int)(r % ch.ngroups);
+  r /= ch.ngroups;
+  tc.tb = (int)(r % ch.ntb);
+  r /= ch.ntb;
+  tc.layer = (int)(r % hd.L);
+  tc.stream = (int)(r / hd.L);
+  return tc;
+}
+
 // Element offset of token t's row inside one layer of a tensor.
 __device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ pages, int slot0, int P, int F,
                                               int t) {
@@ -160,10 +181,13 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
     const DevFactor& f = ch.fac[kfac[j]];
     const int64_t lrel = layer - f.layer0;
     const uint16_t* vf = (const uint16_t*)f.v + lrel * f.width * f.rank;
-    ubase[j] = (const uint16_t*)f.u + lrel * T * f.rank + 32 * kstep[j] + 8 * lg;
-    urank[j] = f.rank - 32 * kstep[j] - 8 * lg;
-    ustride[j] = f.rank;
     uvec[j] = f.uvec != 0;
+    urank[j] = f.rank - 32 * kstep[j] - 8 * lg;
+    // Vector mode (rank a multiple of 8): every lane reads a whole 16-byte slice;
+    // lanes past the rank read the header's zero block (stride 0).
+    const bool upast = uvec[j] && urank[j] <= 0;
+    ustride[j] = upast ? 0 : f.rank;
+    ubase[j] = upast ? (const uint16_t*)hd.zeros : (const uint16_t*)f.u + lrel * T * f.rank + 32 * kstep[j] + 8 * lg;
     const int mrow = lane & 15, kg = lane >> 4;
     const int k0 = 32 * kstep[j] + 8 * kg;   // first k of this lane's 8
 #pragma unroll
@@ -174,8 +198,8 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
         const int rel = col - f.col0;
         const bool in = rel >= 0 && rel < f.width;
         bf16x8 a;
-        if (in && f.vvec && k0 + 8 <= f.rank) {
-          a = *(const bf16x8*)(vf + (int64_t)rel * f.rank + k0);
+        if (f.vvec) {  // uniform: whole slices, or the zero block outside the factor
+          a = *(const bf16x8*)((in && k0 < f.rank) ? vf + (int64_t)rel * f.rank + k0 : (const uint16_t*)hd.zeros);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -188,28 +212,84 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   }
 
   const bool compute = (rot != ROT_NONE) || (NK > 0);
+
+  // Pool pages. The task's page ids (at most 64) are read once, lane i holding the
+  // i-th; with pages of >= 16 slots a 16-token tile spans at most two of them, which
+  // v_readlane extracts at a uniform index, so no memory read sits on the row
+  // address path. Other page sizes read the table once per row.
+  const int pshift = hd.page_shift;
+  int pg_base = 0, pg_last = 0, pg_reg = 0;
+  bool two_pages = false;
+  if (pages != nullptr) {
+    const int s_first = ch.slot0 + tok0, s_end = ch.slot0 + min(tok0 + ch.tb_tokens, T) - 1;
+    pg_base = pshift >= 0 ? s_first >> pshift : s_first / P;
+    pg_last = pshift >= 0 ? s_end >> pshift : s_end / P;
+    two_pages = P >= kTileTokens && pg_last - pg_base < 64;
+    if (two_pages && lane <= pg_last - pg_base) pg_reg = pages[pg_base + lane];
+  }
+  auto page_row = [&](int tt, int t) -> int64_t {  // element offset of token t's row (tile starting at tt)
+    const int s = ch.slot0 + t;
+    const int pi = pshift >= 0 ? s >> pshift : s / P;
+    const int off = pshift >= 0 ? s & (P - 1) : s - pi * P;
+    int pg;
+    if (two_pages) {
+      const int s0 = ch.slot0 + tt;
+      const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
+      const int pg0 = __builtin_amdgcn_readlane(pg_reg, pi0 - pg_base);
+      const int pg1 = __builtin_amdgcn_readlane(pg_reg, min(pi0 + 1, pg_last) - pg_base);
+      pg = pi == pi0 ? pg0 : pg1;
+    } else {
+      pg = pages[pi];
+    }
+    return ((int64_t)pg * P + off) * F;
+  };
+  // A tile whose 16 rows sit in one page (or in dense rows) is addressed from one
+  // uniform base, like dense rows; only tiles that straddle pages take page_row.
+  auto tile_base = [&](bool paged, int tt, int64_t& base) -> bool {
+    if (!paged) {
+      base = (int64_t)tt * F;
+      return true;
+    }
+    if (!two_pages) return false;
+    const int s0 = ch.slot0 + tt;
+    const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
+    const int off0 = s0 - pi0 * P;
+    if (off0 + kTileTokens > P) return false;
+    base = ((int64_t)__builtin_amdgcn_readlane(pg_reg, pi0 - pg_base) * P + off0) * F;
+    return true;
+  };
+
   u32x4 cur[G::NI], nxt[G::NI];
   bf16x8 ucur[NK > 0 ? NK : 1], unxt[NK > 0 ? NK : 1];
 
   auto load_tile = [&](int tile, u32x4 (&raw)[G::NI], bf16x8 (&ub)[NK > 0 ? NK : 1]) {
+    // Rows past the chunk end load the last row instead (computed, never stored), so
+    // no loaded value is merged with a default and the loads stay in flight.
     const int tt = tok0 + tile * kTileTokens;
+    int64_t base;
+    if (tile_base(in_place && pages, tt, base)) {
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-      const int t = tt + i * G::RPI + lrow;
-      raw[i] = t < T ? __builtin_nontemporal_load(
-                           (const u32x4*)(src + row_offset(in_place ? pages : nullptr, ch.slot0, P, F, t)))
-                     : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = min(tt + i * G::RPI + lrow, T - 1);
+        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + base + (int64_t)(t - tt) * F));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = min(tt + i * G::RPI + lrow, T - 1);
+        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + page_row(tt, t)));
+      }
     }
-    const int t = tt + c;
+    const int t = min(tt + c, T - 1);
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       bf16x8 b;
-      if (t < T && uvec[j] && urank[j] >= 8) {
+      if (uvec[j]) {
         b = *(const bf16x8*)(ubase[j] + (int64_t)t * ustride[j]);
-      } else {
+      } else {  // ranks that are not a multiple of 8: element reads, zero past the rank
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint16_t h = (t < T && e < urank[j]) ? ubase[j][(int64_t)t * ustride[j] + e] : (uint16_t)0;
+          const uint16_t h = e < urank[j] ? ubase[j][(int64_t)t * ustride[j] + e] : (uint16_t)0;
           b[e] = __builtin_bit_cast(__bf16, h);
         }
       }
@@ -296,10 +376,19 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
       for (int i = 0; i < G::NI; ++i) out[i] = *(const u32x4*)(lds + (i * G::RPI + lrow) * G::RS + 16 * lchunk);
       wave_lds_fence();
     }
+    int64_t obase;
+    if (tile_base(pages != nullptr, tt, obase)) {
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-      const int t = tt + i * G::RPI + lrow;
-      if (t < T) __builtin_nontemporal_store(out[i], (u32x4*)(dst + row_offset(pages, ch.slot0, P, F, t)));
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = tt + i * G::RPI + lrow;
+        if (t < T) __builtin_nontemporal_store(out[i], (u32x4*)(dst + obase + (int64_t)(t - tt) * F));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = tt + i * G::RPI + lrow;
+        if (t < T) __builtin_nontemporal_store(out[i], (u32x4*)(dst + page_row(tt, t)));
+      }
     }
     if (tile + 1 < ntiles) {
 #pragma unroll
@@ -344,15 +433,10 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
   // plain dispatch order: waves running together stream neighbouring rows
   const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
-  const DevChunk& ch = chunks[find_chunk(chunks, hd.nchunks, task)];
-
-  int64_t r = task - ch.task0;
-  const int g = ch.group0 + (int)(r % ch.ngroups);
-  r /= ch.ngroups;
-  const int tb = (int)(r % ch.ntb);
-  r /= ch.ntb;
-  const int layer = (int)(r % hd.L);
-  const int tensor = ch.stream_tensor[(int)(r / hd.L)];
+  const TaskCoord tcd = decode_task(hd, chunks, task);
+  const DevChunk& ch = chunks[tcd.chunk];
+  const int g = tcd.g, tb = tcd.tb, layer = tcd.layer;
+  const int tensor = ch.stream_tensor[tcd.stream];
   const int colbase = g * hd.group_cols;
   const int tok0 = tb * ch.tb_tokens;
   const int ntiles = (min(ch.tb_tokens, ch.T - tok0) + kTileTokens - 1) / kTileTokens;
@@ -417,13 +501,10 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
   const DevHeader& hd = *hdr;
   const int64_t task = blockIdx.x;
   if (task >= hd.total_tasks) return;  // uniform over the block
-  const DevChunk& ch = chunks[find_chunk(chunks, hd.nchunks, task)];
-  int64_t r = task - ch.task0;
-  const int tb = (int)(r % ch.ntb);
-  r /= ch.ntb;
-  const int layer = (int)(r % hd.L);
-  const int stream = (int)(r / hd.L);
-  const int tensor = ch.stream_tensor[stream];
+  const TaskCoord tcd = decode_task(hd, chunks, task);
+  const DevChunk& ch = chunks[tcd.chunk];
+  const int tb = tcd.tb, layer = tcd.layer;
+  const int tensor = ch.stream_tensor[tcd.stream];
   const bool in_place = (ch.flags & 2u) != 0;
   const bool patch = (ch.flags & 1u) != 0;
   const bool rotate = tensor == 0 && ch.delta != 0;
