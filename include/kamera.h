@@ -191,6 +191,31 @@ kamera_status kamera_plan_upload(const kamera_layout* layout, const kamera_chunk
                                  size_t workspace_bytes, void* stream, kamera_plan* plan);
 kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream);
 
+/* Patch builder (the compile step; preprint §2 Eq. 2 and App. A): forms the deficit
+ *     Delta = x_cond - R(delta) x_canon
+ * on columns [col0, col0 + width) of one layer's rows of one tensor and returns its
+ * top-`rank` truncated SVD as the factors a kamera_factor takes: u_out = U[:, :m] Sigma
+ * [num_tokens][rank] and v_out = V[:, :m] [width][rank], both in layout->dtype, and
+ * sigma_out[rank] (fp64; may be NULL). The rotation is the operator's R(delta): the K
+ * heads' bands (GQA, tensor 0) or the k_rope band (MLA); tensor 1 (GQA V) is not
+ * rotated. x_cond and x_canon are [num_tokens][F] rows (F the layout's row width).
+ * Everything is computed in fp64 on the device: Delta, G = Delta^T Delta, a
+ * randomized range finder for G on a block of p = min(KAMERA_BUILD_MAX_SUBSPACE,
+ * width, num_tokens) vectors followed by `iterations` power (subspace-iteration)
+ * steps, and a Rayleigh-Ritz step. The result is the exact truncated SVD when
+ * p = min(width, num_tokens); otherwise its residual approaches the Eckart-Young
+ * optimum at a rate set by the gap sigma_{p+1}/sigma_m (16 is a good default). rank in [1, min(KAMERA_BUILD_MAX_RANK, width, num_tokens)], iterations in
+ * [0, 64]. The workspace (256-byte aligned, kamera_build_workspace_bytes bytes) and the
+ * outputs must not overlap the inputs. The call is stream-ordered and does not
+ * synchronise; the library allocates nothing. */
+enum { KAMERA_BUILD_MAX_RANK = 64, KAMERA_BUILD_MAX_SUBSPACE = 80 };
+size_t kamera_build_workspace_bytes(int64_t num_tokens, int32_t width, int32_t rank);
+kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, const void* x_cond,
+                                 const void* x_canon, int64_t num_tokens, int64_t delta, int32_t col0,
+                                 int32_t width, int32_t rank, int32_t iterations, void* u_out,
+                                 void* v_out, double* sigma_out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kamera_status_string(kamera_status status);
 /* Detail of the last error on the calling thread ("" if none). */

@@ -20,13 +20,15 @@ NEOX, GPTJ = 0, 1
 PATCH, IN_PLACE = 1, 2
 MAX_FACTORS = 4
 MAX_RANK = 256
+BUILD_MAX_RANK = 64
+BUILD_MAX_SUBSPACE = 80
 
 STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAMERA_E_RANK",
           "KAMERA_E_DELTA", "KAMERA_E_PAGE", "KAMERA_E_OVERLAP", "KAMERA_E_ALIGN",
           "KAMERA_E_WORKSPACE", "KAMERA_E_UNSUPPORTED", "KAMERA_E_HIP"]
 EXPORTED = ["kamera_workspace_bytes", "kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
             "kamera_plan_upload", "kamera_plan_launch", "kamera_status_string", "kamera_last_error",
-            "kamera_version"]
+            "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch"]
 
 
 class Layout(ctypes.Structure):
@@ -88,8 +90,12 @@ def lib() -> ctypes.CDLL:
         L.kamera_plan_upload.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), i32, ctypes.POINTER(Pool),
                                          vp, sz, vp, ctypes.POINTER(Plan)]
         L.kamera_plan_launch.argtypes = [ctypes.POINTER(Plan), vp]
+        L.kamera_build_workspace_bytes.argtypes = [i64, i32, i32]
+        L.kamera_build_workspace_bytes.restype = sz
+        L.kamera_build_patch.argtypes = [ctypes.POINTER(Layout), i32, vp, vp, i64, i64, i32, i32, i32, i32,
+                                         vp, vp, vp, vp, sz, vp]
         for fn in ("kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched", "kamera_plan_upload",
-                   "kamera_plan_launch"):
+                   "kamera_plan_launch", "kamera_build_patch"):
             getattr(L, fn).restype = ctypes.c_int
         L.kamera_status_string.argtypes = [ctypes.c_int]
         L.kamera_status_string.restype = ctypes.c_char_p
@@ -193,6 +199,20 @@ def _ws(workspace):
     if isinstance(workspace, tuple):
         return int(workspace[0]), int(workspace[1])
     return int(workspace.data_ptr()), int(workspace.numel() * workspace.element_size())
+
+
+def build_workspace_bytes(num_tokens: int, width: int, rank: int) -> int:
+    return int(lib().kamera_build_workspace_bytes(int(num_tokens), int(width), int(rank)))
+
+
+def build_patch(layout: Layout, tensor: int, x_cond, x_canon, num_tokens: int, delta: int, col0: int, width: int,
+                rank: int, iterations: int, u_out, v_out, sigma_out, workspace, stream=None) -> None:
+    """Top-`rank` factors of x_cond - R(delta) x_canon on columns [col0, col0 + width)."""
+    wp, wb = _ws(workspace)
+    _check(lib().kamera_build_patch(ctypes.byref(layout), int(tensor), _ptr(x_cond), _ptr(x_canon),
+                                    int(num_tokens), int(delta), int(col0), int(width), int(rank),
+                                    int(iterations), _ptr(u_out), _ptr(v_out), _ptr(sigma_out), wp, wb,
+                                    _stream(stream)))
 
 
 def relocate(layout: Layout, pool: Pool, block_table, slot0: int, num_tokens: int, delta: int, workspace,

@@ -3,7 +3,8 @@
     python -m position_free_kv_amd.build
 
 The library is the C ABI of include/kamera.h: host validation and packing
-(csrc/kamera_host.cpp) plus the gfx950 kernels (csrc/kamera_kernels.hip).
+(csrc/kamera_host.cpp) plus the gfx950 kernels: the operator
+(csrc/kamera_kernels.hip) and the patch builder (csrc/kamera_builder.hip).
 """
 from __future__ import annotations
 
@@ -44,13 +45,16 @@ def build(verbose_asm: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     kobj = os.path.join(objdir, "kamera_kernels.o")
+    bobj = os.path.join(objdir, "kamera_builder.o")
     hobj = os.path.join(objdir, "kamera_host.o")
     _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
           os.path.join(CSRC, "kamera_kernels.hip"), "-o", kobj])
+    _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
+          os.path.join(CSRC, "kamera_builder.hip"), "-o", bobj])
     _run([cc, "-x", "c++", *COMMON, "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-c",
           os.path.join(CSRC, "kamera_host.cpp"), "-o", hobj])
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", tmp])
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, bobj, hobj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose_asm:
         _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "--cuda-device-only", "-S",

@@ -1,0 +1,425 @@
+// Patch builder (the compile step) for gfx950: top-m factors of the deficit
+//     Delta = KV(B|A) - R(delta) . KV(B|empty)
+// Kamera preprint, §2 Eq. 2 (the deficit) and App. A (compile step: conditioned
+// rows minus the relocated canonical, truncated SVD stored as U*Sigma and V).
+//
+// Method: randomized subspace iteration with a Rayleigh-Ritz step (Halko,
+// Martinsson & Tropp, SIAM Review 2011, §4.5 and §5.3) on the Gram matrix
+// G = Delta^T Delta, everything in fp64:
+//   delta_k   Delta [T][W] for the patched columns [col0, col0 + W)
+//   gram_k    G [W][W] (upper 32 x 32 tiles, mirrored)
+//   start_k   a deterministic pseudo-random start block Z0 [p][W]
+//   orth_k    Q = CGS2-orthonormalised rows of Z (one workgroup)
+//   zt_k      Z = Q G (rows of Q times the symmetric G); Q = orth(Z) once for
+//             the range finder and once per power step
+//   rr_k      H = Q Z^T = Q G Q^T (p x p)
+//   jacobi_k  eigenpairs of H: parallel cyclic Jacobi (Brent & Luk 1985
+//             round-robin ordering) in one workgroup's LDS, sorted descending
+//   finish_k  V_m = Q^T E[:, :m], sigma = sqrt(lambda)
+//   usig_k    U*Sigma = Delta V_m
+// U*Sigma and V are rounded once from fp64 to the storage dtype.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kamera_builder.h"
+
+namespace kamera {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kOrthThreads = 1024;
+constexpr int kOrthWaves = kOrthThreads / 64;
+
+__device__ __forceinline__ double load_x(const void* p, int dtype, int64_t i) {
+  if (dtype == 1) return (double)__uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+  return (double)((const float*)p)[i];
+}
+
+// fp64 -> bf16, round to nearest even, without double rounding: round to odd
+// into fp32 first (an exact sticky bit, 16 spare bits), then to nearest even.
+__device__ __forceinline__ uint16_t bf16_from_f64(double v) {
+  float f = (float)v;
+  if ((double)f != v && f == f && !__builtin_isinf(f)) {
+    if (fabs((double)f) > fabs(v)) f = __uint_as_float(__float_as_uint(f) - 1u);  // toward zero
+    f = __uint_as_float(__float_as_uint(f) | 1u);                                // sticky
+  }
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7f800000u) == 0x7f800000u) return (uint16_t)((b >> 16) | ((b & 0xffffu) ? 0x40u : 0u));
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ void store_x(void* p, int dtype, int64_t i, double v) {
+  if (dtype == 1)
+    ((uint16_t*)p)[i] = bf16_from_f64(v);
+  else
+    ((float*)p)[i] = (float)v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the result. `red` holds one slot per wave.
+__device__ double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// Counter-based hash (the splitmix64 finaliser) -> uniform in [-1, 1).
+__device__ __forceinline__ double hash_uniform(uint64_t x) {
+  x = x * 0x9E3779B97F4A7C15ull + 0x2545F4914F6CDD1Dull;
+  x ^= x >> 30;
+  x *= 0xBF58476D1CE4E5B9ull;
+  x ^= x >> 27;
+  x *= 0x94D049BB133111EBull;
+  x ^= x >> 31;
+  return (double)(x >> 11) * (2.0 / 9007199254740992.0) - 1.0;
+}
+
+// Delta[t][w] = x_cond[t][c] - (R(delta) x_canon)[t][c], c = col0 + w, in fp64.
+// Rotation as in the relocation operator: theta_i = base^(-2i/d_rot), angle
+// delta*theta_i, NeoX pairs (i, i + d_rot/2) or GPT-J pairs (2i, 2i + 1) per band.
+__global__ __launch_bounds__(kThreads) void delta_k(BuildArgs a) {
+  __shared__ double cs_tab[kBuildMaxPairs], sn_tab[kBuildMaxPairs];
+  const int npairs = a.d_rot / 2;
+  if (a.rotate)
+    for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
+      const double th = pow(a.base, (-2.0 * (double)i) / (double)a.d_rot);
+      double s, c;
+      sincos((double)a.delta_pos * th, &s, &c);
+      cs_tab[i] = c;
+      sn_tab[i] = s;
+    }
+  __syncthreads();
+  const int64_t n = (int64_t)a.T * a.W;
+  const int64_t band_end = a.band0 + (int64_t)a.nbands * a.band_stride;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(e / a.W), w = (int)(e % a.W);
+    const int c = a.col0 + w;
+    const int64_t row = (int64_t)t * a.F;
+    double solo = load_x(a.x_canon, a.dtype, row + c);
+    if (a.rotate && c >= a.band0 && c < band_end) {
+      const int o = a.band0 + ((c - a.band0) / a.band_stride) * a.band_stride;
+      const int i = c - o;
+      if (i < a.d_rot) {
+        int pi, partner;
+        bool first;
+        if (a.pairing == 1) {
+          pi = i >> 1;
+          first = (i & 1) == 0;
+          partner = o + (first ? i + 1 : i - 1);
+        } else {
+          first = i < npairs;
+          pi = first ? i : i - npairs;
+          partner = o + (first ? i + npairs : i - npairs);
+        }
+        const double other = load_x(a.x_canon, a.dtype, row + partner);
+        const double cv = cs_tab[pi], sv = sn_tab[pi];
+        solo = first ? solo * cv - other * sv : other * sv + solo * cv;
+      }
+    }
+    a.delta[e] = load_x(a.x_cond, a.dtype, row + c) - solo;
+  }
+}
+
+// G = Delta^T Delta. One 32 x 32 tile (bi <= bj) per workgroup; the mirror tile is
+// written from the same sums, so G is exactly symmetric.
+__global__ __launch_bounds__(kThreads) void gram_k(BuildArgs a) {
+  __shared__ double ti[32][33], tj[32][33];
+  const int tiles = (a.W + 31) / 32;
+  int bi = 0, rem = blockIdx.x;  // blockIdx.x enumerates the upper triangle row by row
+  while (rem >= tiles - bi) {
+    rem -= tiles - bi;
+    ++bi;
+  }
+  const int bj = bi + rem;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // ty in [0, 8): rows 4ty..4ty+3
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int t0 = 0; t0 < a.T; t0 += 32) {
+    for (int k = threadIdx.x; k < 32 * 32; k += blockDim.x) {
+      const int r = k >> 5, col = k & 31, t = t0 + r;
+      const int ci = bi * 32 + col, cj = bj * 32 + col;
+      ti[r][col] = (t < a.T && ci < a.W) ? a.delta[(int64_t)t * a.W + ci] : 0.0;
+      tj[r][col] = (t < a.T && cj < a.W) ? a.delta[(int64_t)t * a.W + cj] : 0.0;
+    }
+    __syncthreads();
+    for (int r = 0; r < 32; ++r) {
+      const double vj = tj[r][tx];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fma(ti[r][ty * 4 + q], vj, acc[q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = bi * 32 + ty * 4 + q, j = bj * 32 + tx;
+    if (i < a.W && j < a.W) {
+      a.gram[(int64_t)i * a.W + j] = acc[q];
+      a.gram[(int64_t)j * a.W + i] = acc[q];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void start_k(BuildArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < (int64_t)a.p * a.W) a.z[e] = hash_uniform((uint64_t)e);
+}
+
+// Z[k][i] = sum_j Q[k][j] G[j][i], kZRows rows k per thread (G is read p/kZRows times).
+constexpr int kZRows = 8;
+__global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int k0 = blockIdx.y * kZRows;
+  if (i >= a.W) return;
+  double acc[kZRows];
+#pragma unroll
+  for (int r = 0; r < kZRows; ++r) acc[r] = 0.0;
+  const int nr = min(kZRows, a.p - k0);
+  for (int j = 0; j < a.W; ++j) {
+    const double g = a.gram[(int64_t)j * a.W + i];
+#pragma unroll
+    for (int r = 0; r < kZRows; ++r)
+      if (r < nr) acc[r] = fma(a.q[(int64_t)(k0 + r) * a.W + j], g, acc[r]);
+  }
+  for (int r = 0; r < nr; ++r) a.z[(int64_t)(k0 + r) * a.W + i] = acc[r];
+}
+
+// Q = rows of Z orthonormalised by classical Gram-Schmidt with one
+// re-orthogonalisation pass (CGS2). A row that is numerically in the span of
+// the previous ones (rank-deficient Delta, or Delta = 0) is replaced by a fresh
+// pseudo-random row and orthonormalised again.
+__global__ __launch_bounds__(kOrthThreads) void orth_k(BuildArgs a) {
+  __shared__ double red[kOrthWaves];
+  __shared__ double coef[kBuildMaxSubspace];
+  const int W = a.W, p = a.p;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int j = 0; j < p; ++j) {
+    double* qj = a.q + (int64_t)j * W;
+    for (int attempt = 0; attempt < 4; ++attempt) {
+      double n0 = 0.0;
+      for (int i = threadIdx.x; i < W; i += blockDim.x) {
+        const double v = attempt == 0
+                             ? a.z[(int64_t)j * W + i]
+                             : hash_uniform(((uint64_t)(attempt * kBuildMaxSubspace + j) << 32) + (uint64_t)i);
+        qj[i] = v;
+        n0 += v * v;
+      }
+      n0 = block_sum(n0, red);  // its barriers also publish the row written above
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int k = wave; k < j; k += kOrthWaves) {
+          const double* qk = a.q + (int64_t)k * W;
+          double d = 0.0;
+          for (int i = lane; i < W; i += 64) d = fma(qk[i], qj[i], d);
+          d = wave_sum(d);
+          if (lane == 0) coef[k] = d;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < W; i += blockDim.x) {
+          double v = qj[i];
+          for (int k = 0; k < j; ++k) v = fma(-coef[k], a.q[(int64_t)k * W + i], v);
+          qj[i] = v;
+        }
+        __syncthreads();
+      }
+      double nn = 0.0;
+      for (int i = threadIdx.x; i < W; i += blockDim.x) nn += qj[i] * qj[i];
+      nn = block_sum(nn, red);
+      if (n0 > 0.0 && nn > 1e-24 * n0 && nn > 1e-280) {
+        const double inv = 1.0 / sqrt(nn);
+        for (int i = threadIdx.x; i < W; i += blockDim.x) qj[i] *= inv;
+        __syncthreads();
+        break;
+      }
+    }
+  }
+}
+
+// H[r][c] = sum_i Q[r][i] Z[c][i]: one wave per entry.
+__global__ __launch_bounds__(kThreads) void rr_k(BuildArgs a) {
+  const int e = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= a.p * a.p) return;
+  const int r = e / a.p, c = e % a.p;
+  const double* qr = a.q + (int64_t)r * a.W;
+  const double* zc = a.z + (int64_t)c * a.W;
+  double s = 0.0;
+  for (int i = lane; i < a.W; i += 64) s = fma(qr[i], zc[i], s);
+  s = wave_sum(s);
+  if (lane == 0) a.h[e] = s;
+}
+
+// Eigenpairs of the symmetric p x p matrix H by parallel cyclic Jacobi: each
+// round applies p/2 disjoint plane rotations chosen by the round-robin
+// tournament (player n-1 fixed, the rest rotating); a rotation is skipped when
+// its off-diagonal entry is negligible against the geometric mean of the two
+// diagonal entries, and the sweeps stop once a whole sweep skips every pair.
+__global__ __launch_bounds__(kThreads) void jacobi_k(BuildArgs a) {
+  __shared__ double A[kBuildMaxSubspace][kBuildMaxSubspace + 1];
+  __shared__ double E[kBuildMaxSubspace][kBuildMaxSubspace + 1];
+  __shared__ double cs[kBuildMaxSubspace / 2], sn[kBuildMaxSubspace / 2];
+  __shared__ int pp[kBuildMaxSubspace / 2], qq[kBuildMaxSubspace / 2];
+  __shared__ int order[kBuildMaxSubspace];
+  __shared__ int rotated;
+  const int p = a.p;
+  const int n = p + (p & 1);  // an even number of players; index p is a bye when p is odd
+  for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
+    const int r = e / p, c = e % p;
+    A[r][c] = 0.5 * (a.h[r * p + c] + a.h[c * p + r]);
+    E[r][c] = r == c ? 1.0 : 0.0;
+  }
+  for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
+    __syncthreads();
+    if (threadIdx.x == 0) rotated = 0;
+    __syncthreads();
+    for (int round = 0; round < n - 1; ++round) {
+      for (int k = threadIdx.x; k < n / 2; k += blockDim.x) {
+        int x, y;
+        if (k == 0) {
+          x = n - 1;
+          y = round;
+        } else {
+          x = (round + k) % (n - 1);
+          y = (round + n - 1 - k) % (n - 1);
+        }
+        const int lo = min(x, y), hi = max(x, y);
+        double c = 1.0, s = 0.0;
+        if (hi < p) {
+          const double apq = A[lo][hi], app = A[lo][lo], aqq = A[hi][hi];
+          if (fabs(apq) > 1e-300 && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
+            const double th = (aqq - app) / (2.0 * apq);
+            const double t = fabs(th) > 1e150 ? 0.5 / th : (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(1.0 + th * th));
+            c = 1.0 / sqrt(1.0 + t * t);
+            s = t * c;
+            rotated = 1;
+          }
+        }
+        pp[k] = lo;
+        qq[k] = hi;
+        cs[k] = c;
+        sn[k] = s;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < (n / 2) * p; e += blockDim.x) {  // A <- J^T A
+        const int k = e / p, col = e % p;
+        if (qq[k] >= p || sn[k] == 0.0) continue;
+        const double c = cs[k], s = sn[k];
+        const double x = A[pp[k]][col], y = A[qq[k]][col];
+        A[pp[k]][col] = c * x - s * y;
+        A[qq[k]][col] = s * x + c * y;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < (n / 2) * p; e += blockDim.x) {  // A <- A J, E <- E J
+        const int k = e / p, row = e % p;
+        if (qq[k] >= p || sn[k] == 0.0) continue;
+        const double c = cs[k], s = sn[k];
+        const double x = A[row][pp[k]], y = A[row][qq[k]];
+        A[row][pp[k]] = c * x - s * y;
+        A[row][qq[k]] = s * x + c * y;
+        const double u = E[row][pp[k]], v = E[row][qq[k]];
+        E[row][pp[k]] = c * u - s * v;
+        E[row][qq[k]] = s * u + c * v;
+      }
+      __syncthreads();
+    }
+    if (!rotated) break;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p; i += blockDim.x) {  // rank by eigenvalue, descending; ties by index
+    int rank = 0;
+    for (int j = 0; j < p; ++j)
+      if (A[j][j] > A[i][i] || (A[j][j] == A[i][i] && j < i)) ++rank;
+    order[rank] = i;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
+    const int r = e / p, k = e % p;
+    a.evec[r * p + k] = E[r][order[k]];
+  }
+  for (int k = threadIdx.x; k < p; k += blockDim.x) a.lam[k] = A[order[k]][order[k]];
+}
+
+// V_m[i][k] = sum_j Q[j][i] E[j][k]; sigma_k = sqrt(max(lambda_k, 0)).
+__global__ __launch_bounds__(kThreads) void finish_k(BuildArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < a.m && a.sigma) a.sigma[e] = sqrt(fmax(a.lam[e], 0.0));
+  if (e >= (int64_t)a.W * a.m) return;
+  const int i = (int)(e / a.m), k = (int)(e % a.m);
+  double s = 0.0;
+  for (int j = 0; j < a.p; ++j) s = fma(a.q[(int64_t)j * a.W + i], a.evec[j * a.p + k], s);
+  a.vm[e] = s;
+  store_x(a.v_out, a.dtype, e, s);
+}
+
+// (U Sigma)[t][k] = sum_w Delta[t][w] V_m[w][k].
+__global__ __launch_bounds__(kThreads) void usig_k(BuildArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)a.T * a.m) return;
+  const int t = (int)(e / a.m), k = (int)(e % a.m);
+  const double* d = a.delta + (int64_t)t * a.W;
+  double s = 0.0;
+  for (int w = 0; w < a.W; ++w) s = fma(d[w], a.vm[(int64_t)w * a.m + k], s);
+  store_x(a.u_out, a.dtype, e, s);
+}
+
+unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t build_workspace_bytes(int64_t T, int64_t W, int64_t m) {
+  const int64_t p = std::min<int64_t>(kBuildMaxSubspace, std::min(W, T));
+  const size_t d = sizeof(double);
+  return align256(T * W * d) + align256(W * W * d) + 2 * align256(p * W * d) + 2 * align256(p * p * d) +
+         align256(p * d) + align256(W * m * d);
+}
+
+void build_workspace_carve(BuildArgs& a, void* ws) {
+  char* c = (char*)ws;
+  const size_t d = sizeof(double);
+  auto take = [&](int64_t count) {
+    double* r = (double*)c;
+    c += align256((size_t)count * d);
+    return r;
+  };
+  a.delta = take((int64_t)a.T * a.W);
+  a.gram = take((int64_t)a.W * a.W);
+  a.q = take((int64_t)a.p * a.W);
+  a.z = take((int64_t)a.p * a.W);
+  a.h = take((int64_t)a.p * a.p);
+  a.evec = take((int64_t)a.p * a.p);
+  a.lam = take(a.p);
+  a.vm = take((int64_t)a.W * a.m);
+}
+
+hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
+  const dim3 blk(kThreads);
+  const int64_t tw = (int64_t)a.T * a.W;
+  hipLaunchKernelGGL(delta_k, dim3(std::min<unsigned>(blocks_for(tw, kThreads), 8192u)), blk, 0, st, a);
+  const int tiles = (a.W + 31) / 32;
+  hipLaunchKernelGGL(gram_k, dim3(tiles * (tiles + 1) / 2), blk, 0, st, a);
+  hipLaunchKernelGGL(start_k, dim3(blocks_for((int64_t)a.p * a.W, kThreads)), blk, 0, st, a);
+  hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
+  const dim3 zgrid(blocks_for(a.W, kThreads), blocks_for(a.p, kZRows));
+  for (int it = 0; it <= a.iters; ++it) {  // the range finder's product, then `iters` power steps
+    hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
+    hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
+  }
+  hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
+  hipLaunchKernelGGL(rr_k, dim3(blocks_for((int64_t)a.p * a.p, kThreads / 64)), blk, 0, st, a);
+  hipLaunchKernelGGL(jacobi_k, dim3(1), blk, 0, st, a);
+  hipLaunchKernelGGL(finish_k, dim3(blocks_for((int64_t)a.W * a.m, kThreads)), blk, 0, st, a);
+  hipLaunchKernelGGL(usig_k, dim3(blocks_for((int64_t)a.T * a.m, kThreads)), blk, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kamera

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "kamera.h"
+#include "kamera_builder.h"
 #include "kamera_desc.h"
 
 namespace kamera {
@@ -538,6 +539,78 @@ kamera_status kamera_relocate(const kamera_layout* layout, const kamera_pool* po
   c.block_table = block_table;
   c.slot0 = slot0;
   return kamera_rehydrate_batched(layout, &c, 1, pool, workspace, workspace_bytes, stream);
+}
+
+size_t kamera_build_workspace_bytes(int64_t num_tokens, int32_t width, int32_t rank) {
+  if (num_tokens < 1 || width < 1 || rank < 1) return 0;
+  return build_workspace_bytes(num_tokens, width, rank);
+}
+
+kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, const void* x_cond,
+                                 const void* x_canon, int64_t num_tokens, int64_t delta, int32_t col0,
+                                 int32_t width, int32_t rank, int32_t iterations, void* u_out, void* v_out,
+                                 double* sigma_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  kamera_status st = check_layout(layout);
+  if (st != KAMERA_OK) return st;
+  const bool gqa = layout->family == KAMERA_GQA;
+  if (tensor < 0 || tensor > (gqa ? 1 : 0))
+    return fail(KAMERA_E_SHAPE, "tensor %d invalid for this family", tensor);
+  if (!x_cond || !x_canon) return fail(KAMERA_E_NULL, "x_cond or x_canon is NULL");
+  if (!u_out || !v_out) return fail(KAMERA_E_NULL, "u_out or v_out is NULL");
+  const size_t es = layout->dtype == KAMERA_BF16 ? 2 : 4;
+  if (!aligned(x_cond, es) || !aligned(x_canon, es) || !aligned(u_out, es) || !aligned(v_out, es))
+    return fail(KAMERA_E_ALIGN, "row and factor pointers must be aligned to %zu bytes", es);
+  if (sigma_out && !aligned(sigma_out, sizeof(double))) return fail(KAMERA_E_ALIGN, "sigma_out must be 8-byte aligned");
+  if (num_tokens < 1 || num_tokens > (1 << 24)) return fail(KAMERA_E_SHAPE, "num_tokens must be in [1, 2^24]");
+  if (delta <= -(int64_t(1) << 31) || delta >= (int64_t(1) << 31)) return fail(KAMERA_E_DELTA, "|delta| must be < 2^31");
+  const int F = row_width(layout);
+  if (col0 < 0 || width < 1 || (int64_t)col0 + width > F)
+    return fail(KAMERA_E_SHAPE, "columns [%d, %lld) outside the row of %d", col0, (long long)col0 + width, F);
+  const int64_t max_rank = std::min<int64_t>(KAMERA_BUILD_MAX_RANK, std::min<int64_t>(width, num_tokens));
+  if (rank < 1 || rank > max_rank) return fail(KAMERA_E_RANK, "rank %d outside [1, %lld]", rank, (long long)max_rank);
+  if (iterations < 0 || iterations > 64) return fail(KAMERA_E_SHAPE, "iterations must be in [0, 64]");
+  if ((int64_t)num_tokens * width > (int64_t(1) << 31))
+    return fail(KAMERA_E_SHAPE, "num_tokens * width must be <= 2^31");
+  const size_t need = build_workspace_bytes(num_tokens, width, rank);
+  if (!workspace) return fail(KAMERA_E_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(KAMERA_E_ALIGN, "workspace must be %zu-byte aligned", kAlign);
+  if (workspace_bytes < need) return fail(KAMERA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  BuildArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x_cond = x_cond;
+  a.x_canon = x_canon;
+  a.u_out = u_out;
+  a.v_out = v_out;
+  a.sigma = sigma_out;
+  a.delta_pos = delta;
+  a.base = layout->rope_base;
+  a.T = (int)num_tokens;
+  a.F = F;
+  a.W = width;
+  a.col0 = col0;
+  a.m = rank;
+  a.p = (int)std::min<int64_t>(kBuildMaxSubspace, std::min<int64_t>(width, num_tokens));
+  a.iters = iterations;
+  a.dtype = layout->dtype == KAMERA_BF16 ? 1 : 0;
+  a.rotate = tensor == 0;
+  a.pairing = layout->pairing;
+  if (gqa) {
+    a.band0 = 0;
+    a.band_stride = layout->head_dim;
+    a.nbands = layout->num_kv_heads;
+    a.d_rot = layout->head_dim;
+  } else {
+    a.band0 = layout->latent_dim;
+    a.band_stride = layout->rope_dim;
+    a.nbands = 1;
+    a.d_rot = layout->rope_dim;
+  }
+  build_workspace_carve(a, workspace);
+  const hipError_t e = launch_builder(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "builder launch failed: %s", hipGetErrorString(e));
+  return KAMERA_OK;
 }
 
 const char* kamera_status_string(kamera_status s) {

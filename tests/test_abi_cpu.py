@@ -192,3 +192,61 @@ def test_plan_struct_roundtrip_empty():
     plan = abi.plan_upload(gqa_layout(), [], None, WS, 0)
     assert plan.num_tasks == 0 and plan.kernel == 0
     abi.plan_launch(plan, 0)
+
+
+# --------------------------------------------------------------------------- patch builder
+def build_call(layout=None, **kw):
+    lay = layout or gqa_layout()
+    d = dict(tensor=0, x_cond=FAKE, x_canon=FAKE + 0x100000, num_tokens=64, delta=100, col0=0, width=512,
+             rank=32, iterations=16, u_out=FAKE + 0x200000, v_out=FAKE + 0x300000, sigma_out=FAKE + 0x400000)
+    d.update(kw)
+    need = abi.build_workspace_bytes(d["num_tokens"], d["width"], d["rank"]) if d["num_tokens"] > 0 else 0
+    ws = kw.pop("ws", None) if "ws" in kw else (FAKE + 0x1000000, need)
+    d.pop("ws", None)
+    return lambda: abi.build_patch(lay, workspace=ws, **d)
+
+
+def test_build_workspace_bytes():
+    a = abi.build_workspace_bytes(64, 512, 32)
+    b = abi.build_workspace_bytes(1024, 512, 32)
+    # Delta [T][W], G [W][W], Q and Z [p][W], H and E [p][p], lambda [p], V_m [W][m], all fp64
+    p = 64
+    assert a >= 8 * (64 * 512 + 512 * 512 + 2 * p * 512 + 2 * p * p + p + 512 * 32)
+    assert a < b and a % 256 == 0 and b % 256 == 0
+    assert abi.build_workspace_bytes(0, 512, 32) == 0 and abi.build_workspace_bytes(8, 512, 0) == 0
+
+
+MLA_LAYOUT = dict(latent_dim=512, rope_dim=64, rope_base=1e4, page_size=16)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x_cond=None), "KAMERA_E_NULL"),
+    (dict(v_out=None), "KAMERA_E_NULL"),
+    (dict(tensor=2), "KAMERA_E_SHAPE"),
+    (dict(num_tokens=0), "KAMERA_E_SHAPE"),
+    (dict(col0=500, width=13), "KAMERA_E_SHAPE"),
+    (dict(col0=-1), "KAMERA_E_SHAPE"),
+    (dict(rank=0), "KAMERA_E_RANK"),
+    (dict(rank=65), "KAMERA_E_RANK"),
+    (dict(num_tokens=16, rank=17), "KAMERA_E_RANK"),
+    (dict(width=8, rank=9), "KAMERA_E_RANK"),
+    (dict(iterations=-1), "KAMERA_E_SHAPE"),
+    (dict(iterations=65), "KAMERA_E_SHAPE"),
+    (dict(delta=1 << 31), "KAMERA_E_DELTA"),
+    (dict(x_canon=FAKE + 1), "KAMERA_E_ALIGN"),
+    (dict(sigma_out=FAKE + 4), "KAMERA_E_ALIGN"),
+    (dict(ws=(FAKE + 0x1000000, 1024)), "KAMERA_E_WORKSPACE"),
+    (dict(ws=(0, 1 << 30)), "KAMERA_E_WORKSPACE"),
+    (dict(ws=(FAKE + 0x1000008, 1 << 30)), "KAMERA_E_ALIGN"),
+])
+def test_build_patch_validation(kw, expect):
+    name, msg = status_of(build_call(**kw))
+    assert name == expect, msg
+
+
+def test_build_patch_mla_has_one_tensor():
+    lay = abi.make_layout(abi.MLA, abi.BF16, 1, **MLA_LAYOUT)
+    name, _ = status_of(build_call(lay, tensor=1, width=576))
+    assert name == "KAMERA_E_SHAPE"
+    name, _ = status_of(build_call(lay, tensor=0, col0=512, width=65))
+    assert name == "KAMERA_E_SHAPE"
