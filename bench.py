@@ -103,6 +103,96 @@ def cpu_baseline(cfg: str, wl, sample_units: int):
                       f"excluded"}
 
 
+# ----------------------------------------------------------------------------- patch builder
+BUILDER_SHAPES = {
+    # name: (layout kwargs, tokens, patched width, rank, description)
+    "C2": (dict(family=0, num_kv_heads=4, head_dim=128, rope_base=1e6), 1024, 512, 32,
+           "K of one C2 chunk-layer: 1024 tokens x 512 columns (4 heads x 128), bf16, rank 32"),
+    "C3": (dict(family=1, latent_dim=512, rope_dim=64, rope_base=1e4), 1024, 576, 32,
+           "MLA row of one C3 chunk-layer: 1024 tokens x 576 columns, bf16, rank 32"),
+    "C4": (dict(family=0, num_kv_heads=32, head_dim=128, rope_base=1e4), 2048, 4096, 32,
+           "K of one C4 chunk-layer: 2048 tokens x 4096 columns (32 heads x 128), bf16, rank 32"),
+}
+
+
+def _builder_case(cfg: str):
+    from workloads.builder_inputs import BuilderCase
+    from workloads.configs import BF16, LayoutSpec
+    lk, T, W, m, desc = BUILDER_SHAPES[cfg]
+    lay = LayoutSpec(dtype=BF16, num_layers=1, **lk)
+    canon = BuilderCase(lay, tensor=0, num_tokens=T, delta=4096, col0=0, width=W, seed=7).canonical()
+    cond = BuilderCase(lay, tensor=0, num_tokens=T, delta=4096, col0=0, width=W, seed=8).canonical()
+    return lay, T, W, m, desc, canon, cond
+
+
+def builder_cpu_baseline(cfg: str, budget_s: float = 10.0):
+    """LAPACK (gesdd) truncated SVD of the fp64 deficit, the oracle of the builder, on the host."""
+    import oracle.kamera_oracle as O
+    from oracle.builder_oracle import deficit, truncated_svd
+    lay, T, W, m, desc, canon, cond = _builder_case(cfg)
+    bands = O.band_offsets(lay.family, lay.num_kv_heads, lay.head_dim, lay.latent_dim)
+    d_rot = O.rotary_width(lay.family, lay.head_dim, lay.rope_dim)
+    xc, xk = O.upcast(cond, lay.dtype), O.upcast(canon, lay.dtype)
+    n, t0 = 0, time.perf_counter()
+    while n < 200 and time.perf_counter() - t0 < budget_s:
+        d = deficit(xc, xk, 4096, bands=bands, d_rot=d_rot, base=lay.rope_base, pairing=lay.pairing)[:, :W]
+        truncated_svd(d, m)
+        n += 1
+    wall = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    return {"value": n / wall, "unit": "builds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} builds of the same deficit ({desc}): fp64 deficit and LAPACK gesdd; {wall:.1f} s wall"}
+
+
+def builder_main(args) -> int:
+    cpu = None if args.no_cpu else builder_cpu_baseline(args.config)
+    import torch
+    from position_free_kv_amd import abi
+    torch.cuda.set_device(0)
+    abi.lib()
+    lay, T, W, m, desc, canon, cond = _builder_case(args.config)
+    layout = abi.make_layout(lay.family, lay.dtype, 1, num_kv_heads=lay.num_kv_heads, head_dim=lay.head_dim,
+                             latent_dim=lay.latent_dim, rope_dim=lay.rope_dim, pairing=lay.pairing,
+                             rope_base=lay.rope_base)
+    xk = torch.from_numpy(canon.view("int16").copy()).cuda()
+    xc = torch.from_numpy(cond.view("int16").copy()).cuda()
+    u = torch.empty((T, m), dtype=torch.int16, device="cuda")
+    v = torch.empty((W, m), dtype=torch.int16, device="cuda")
+    sig = torch.empty(m, dtype=torch.float64, device="cuda")
+    ws = torch.empty(abi.build_workspace_bytes(T, W, m), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: abi.build_patch(layout, 0, xc, xk, T, 4096, 0, W, m, args.builder_iterations, u, v, sig, ws,
+                                   stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    out = {
+        "metric": "patch builds/s (fp64 deficit and top-m truncated SVD of one chunk-layer tensor), 1 GPU",
+        "value": args.steps / wall, "unit": "builds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic: two independent seeded N(0,1) bf16 row blocks (a full-rank deficit)",
+        "config": {"workload": desc, "name": args.config, "tokens": T, "width": W, "rank": m,
+                   "iterations": args.builder_iterations},
+        "gpu_ms_per_build": ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # ----------------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -115,12 +205,20 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
     ap.add_argument("--rank", type=int, default=None, help="override the patch rank m of the workload")
+    ap.add_argument("--builder", action="store_true",
+                    help="time the patch builder (kamera_build_patch) on one chunk-layer of --config instead")
+    ap.add_argument("--builder-iterations", type=int, default=16)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
                                    "several GPUs would each run their own share (see DESIGN.md); only --gpus 1 "
                                    "is measured"}), flush=True)
         return 2
+    if args.builder:
+        if args.config not in BUILDER_SHAPES:
+            print(json.dumps({"error": f"no builder shape for {args.config}"}), flush=True)
+            return 2
+        return builder_main(args)
 
     from workloads import make_workload
     wl = make_workload(args.config, rank=args.rank)

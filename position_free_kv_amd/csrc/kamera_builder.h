@@ -26,6 +26,9 @@ struct BuildArgs {
   double* evec;         // [p][p]
   double* lam;          // [p]
   double* vm;           // [W][m]
+  double* bz;           // [p][p]  Gram of the block being orthonormalised
+  double* lf;           // [p][p]  its Cholesky factor (lower)
+  int* flag;            // 1: Cholesky QR rejected the block, the CGS2 fallback runs
   int64_t delta_pos;    // the relocation offset
   double base;          // RoPE base
   int T, F, W, col0, m, p, iters;

@@ -9,10 +9,15 @@
 //   delta_k   Delta [T][W] for the patched columns [col0, col0 + W)
 //   gram_k    G [W][W] (upper 32 x 32 tiles, mirrored)
 //   start_k   a deterministic pseudo-random start block Z0 [p][W]
-//   orth_k    Q = CGS2-orthonormalised rows of Z (one workgroup)
-//   zt_k      Z = Q G (rows of Q times the symmetric G); Q = orth(Z) once for
-//             the range finder and once per power step
-//   rr_k      H = Q Z^T = Q G Q^T (p x p)
+//   orthonormalisation of the block Z (p x W) into Q, once for the range
+//   finder and once per power step: shifted CholeskyQR3 (Fukaya, Kannan,
+//   Nakatsukasa, Yamamoto & Yanagisawa, SIAM J. Sci. Comput. 2020): a Cholesky
+//   QR pass on Z Z^T + sI, then two plain passes; each pass is B = X X^T
+//   (dots_k), B = L L^T (chol_k, one workgroup, LDS) and X <- L^-1 X (trsm_k).
+//   A block whose pivots collapse anyway (rank-deficient Z, e.g. Delta = 0)
+//   sets a flag and is orthonormalised by CGS2 instead (orth_k, one workgroup)
+//   zt_k      Z = Q G (rows of Q times the symmetric G)
+//   dots_k    H = Q Z^T = Q G Q^T (p x p)
 //   jacobi_k  eigenpairs of H: parallel cyclic Jacobi (Brent & Luk 1985
 //             round-robin ordering) in one workgroup's LDS, sorted descending
 //   finish_k  V_m = Q^T E[:, :m], sigma = sqrt(lambda)
@@ -174,23 +179,32 @@ __global__ __launch_bounds__(kThreads) void start_k(BuildArgs a) {
   if (e < (int64_t)a.p * a.W) a.z[e] = hash_uniform((uint64_t)e);
 }
 
-// Z[k][i] = sum_j Q[k][j] G[j][i], kZRows rows k per thread (G is read p/kZRows times).
+// Z[k][i] = sum_j Q[k][j] G[j][i]. A workgroup covers 64 columns i and kZRows rows
+// k; its 4 waves split the sum over j and add their partial sums in LDS (fixed
+// order, so the result is deterministic).
 constexpr int kZRows = 8;
 __global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ double part[kThreads / 64][kZRows][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   const int k0 = blockIdx.y * kZRows;
-  if (i >= a.W) return;
+  const int nr = min(kZRows, a.p - k0);
   double acc[kZRows];
 #pragma unroll
   for (int r = 0; r < kZRows; ++r) acc[r] = 0.0;
-  const int nr = min(kZRows, a.p - k0);
-  for (int j = 0; j < a.W; ++j) {
-    const double g = a.gram[(int64_t)j * a.W + i];
+  if (i < a.W)
+    for (int j = wave; j < a.W; j += kThreads / 64) {
+      const double g = a.gram[(int64_t)j * a.W + i];
 #pragma unroll
-    for (int r = 0; r < kZRows; ++r)
-      if (r < nr) acc[r] = fma(a.q[(int64_t)(k0 + r) * a.W + j], g, acc[r]);
-  }
-  for (int r = 0; r < nr; ++r) a.z[(int64_t)(k0 + r) * a.W + i] = acc[r];
+      for (int r = 0; r < kZRows; ++r)
+        if (r < nr) acc[r] = fma(a.q[(int64_t)(k0 + r) * a.W + j], g, acc[r]);
+    }
+#pragma unroll
+  for (int r = 0; r < kZRows; ++r) part[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave == 0 && i < a.W)
+    for (int r = 0; r < nr; ++r)
+      a.z[(int64_t)(k0 + r) * a.W + i] = part[0][r][lane] + part[1][r][lane] + part[2][r][lane] + part[3][r][lane];
 }
 
 // Q = rows of Z orthonormalised by classical Gram-Schmidt with one
@@ -200,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
 __global__ __launch_bounds__(kOrthThreads) void orth_k(BuildArgs a) {
   __shared__ double red[kOrthWaves];
   __shared__ double coef[kBuildMaxSubspace];
+  if (*a.flag == 0) return;  // Cholesky QR succeeded
   const int W = a.W, p = a.p;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int j = 0; j < p; ++j) {
@@ -243,39 +258,152 @@ __global__ __launch_bounds__(kOrthThreads) void orth_k(BuildArgs a) {
   }
 }
 
-// H[r][c] = sum_i Q[r][i] Z[c][i]: one wave per entry.
-__global__ __launch_bounds__(kThreads) void rr_k(BuildArgs a) {
+// out[r][c] = sum_i X[r][i] Y[c][i] for p x W blocks X, Y: one wave per entry.
+__global__ __launch_bounds__(kThreads) void dots_k(BuildArgs a, const double* x, const double* y, double* out) {
   const int e = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (e >= a.p * a.p) return;
   const int r = e / a.p, c = e % a.p;
-  const double* qr = a.q + (int64_t)r * a.W;
-  const double* zc = a.z + (int64_t)c * a.W;
+  const double* xr = x + (int64_t)r * a.W;
+  const double* yc = y + (int64_t)c * a.W;
   double s = 0.0;
-  for (int i = lane; i < a.W; i += 64) s = fma(qr[i], zc[i], s);
+  for (int i = lane; i < a.W; i += 64) s = fma(xr[i], yc[i], s);
   s = wave_sum(s);
-  if (lane == 0) a.h[e] = s;
+  if (lane == 0) out[e] = s;
+}
+
+// Cholesky factor B = L L^T of the p x p Gram of a block (right-looking, in LDS).
+// pass 0 factors B + sI with s = 11 (W p + p (p + 1)) u trace(B), u = 2^-53 (the
+// shift of shifted CholeskyQR, which keeps the factorisation alive up to a
+// condition number of 1/u); passes 1 and 2 factor B itself and reject a pivot
+// below 1e-14 (pass 1) or 1e-6 (pass 2) of its column's squared norm, which
+// CholeskyQR2 could not bring back to orthogonality. A rejection sets the flag
+// (pass 0 sets it, later passes can only add to it) and the CGS2 fallback runs.
+// 16 waves on a 32 x 32 grid: the trailing updates, not the step barriers, dominate.
+constexpr int kCholThreads = 1024;
+__global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
+  __shared__ double Ls[kBuildMaxSubspace][kBuildMaxSubspace + 1];
+  __shared__ double dg[kBuildMaxSubspace];
+  __shared__ double red[kCholThreads / 64];
+  const int p = a.p;
+  double tr = 0.0;
+  for (int i = threadIdx.x; i < p; i += blockDim.x) tr += a.bz[i * p + i];
+  tr = block_sum(tr, red);
+  const double shift = pass == 0 ? 11.0 * ((double)a.W * p + (double)p * (p + 1)) * 0x1p-53 * tr : 0.0;
+  const double ratio = pass == 0 ? 0.0 : (pass == 1 ? 1e-14 : 1e-6);
+  // lower triangle only; 32 x 32 thread grid, loads unrolled so they overlap
+  for (int r0 = 0; r0 < p; r0 += kCholThreads / 32) {
+    const int r = r0 + (threadIdx.x >> 5);
+#pragma unroll
+    for (int cc = 0; cc < kBuildMaxSubspace; cc += 32) {
+      const int c = cc + (threadIdx.x & 31);
+      if (r < p && c <= r) {
+        const double v = 0.5 * (a.bz[r * p + c] + a.bz[c * p + r]) + (r == c ? shift : 0.0);
+        Ls[r][c] = v;
+        if (r == c) dg[r] = v;
+      }
+    }
+  }
+  __syncthreads();
+  int bad = !(tr > 0.0) || !(tr < 1e300);
+  for (int k = 0; k < p && !bad; ++k) {
+    const double d = Ls[k][k];
+    if (!(d > ratio * dg[k]) || !(d > 0.0) || !(d < 1e300)) {  // uniform: every thread reads the same pivot
+      bad = 1;
+      break;
+    }
+    const double rk = sqrt(d);
+    __syncthreads();  // the pivot is read before column k changes
+    for (int i = k + 1 + threadIdx.x; i < p; i += blockDim.x) Ls[i][k] /= rk;
+    if (threadIdx.x == 0) Ls[k][k] = rk;
+    __syncthreads();
+    // trailing lower triangle (i >= j > k); a 32 x 32 thread grid, no index division
+    for (int i = k + 1 + (threadIdx.x >> 5); i < p; i += kCholThreads / 32) {
+      const double lik = Ls[i][k];
+#pragma unroll
+      for (int jj = 0; jj < kBuildMaxSubspace; jj += 32) {  // independent entries: let them overlap
+        const int j = k + 1 + jj + (threadIdx.x & 31);
+        if (j <= i) Ls[i][j] = fma(-lik, Ls[j][k], Ls[i][j]);
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *a.flag = pass == 0 ? bad : (*a.flag | bad);
+  for (int r0 = 0; r0 < p; r0 += kCholThreads / 32) {  // lower triangle; the upper part is never read
+    const int r = r0 + (threadIdx.x >> 5);
+#pragma unroll
+    for (int cc = 0; cc < kBuildMaxSubspace; cc += 32) {
+      const int c = cc + (threadIdx.x & 31);
+      if (r < p && c <= r) a.lf[r * p + c] = Ls[r][c];
+    }
+  }
+}
+
+// Q = L^-1 Z by forward substitution, one wave per column i of the block: lane l
+// holds rows l and l + 64. Step k takes the finished entry q_k from its lane
+// (v_readlane at a uniform index) and removes its contribution from the rows below;
+// L is kept transposed in LDS so the lanes read a contiguous row of it. All of a
+// column is read before any of it is written, so src == dst is allowed.
+constexpr int kTrsmWaves = 8;
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const double* src, double* dst) {
+  __shared__ double Lt[kBuildMaxSubspace][kBuildMaxSubspace + 1];  // Lt[k][r] = L[r][k]
+  __shared__ double inv[kBuildMaxSubspace];
+  if (*a.flag) return;  // uniform: the fallback orthonormalises this block
+  const int p = a.p, W = a.W;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int r = wave; r < p; r += kTrsmWaves)
+    for (int k = lane; k < p; k += 64) Lt[k][r] = k <= r ? a.lf[r * p + k] : 0.0;
+  for (int r = threadIdx.x; r < p; r += blockDim.x) inv[r] = 1.0 / a.lf[r * p + r];
+  __syncthreads();
+  const int i = blockIdx.x * kTrsmWaves + wave;
+  if (i >= W) return;  // uniform over the wave
+  const int r0 = lane, r1 = lane + 64;
+  double acc0 = r0 < p ? src[(int64_t)r0 * W + i] : 0.0;
+  double acc1 = r1 < p ? src[(int64_t)r1 * W + i] : 0.0;
+  for (int k = 0; k < p; ++k) {
+    const double qk = readlane_f64(k < 64 ? acc0 : acc1, k & 63) * inv[k];
+    if (r0 > k) acc0 = fma(-Lt[k][r0], qk, acc0);
+    if (r1 > k && r1 < p) acc1 = fma(-Lt[k][r1], qk, acc1);
+  }
+  if (r0 < p) dst[(int64_t)r0 * W + i] = acc0 * inv[r0];
+  if (r1 < p) dst[(int64_t)r1 * W + i] = acc1 * inv[r1];
 }
 
 // Eigenpairs of the symmetric p x p matrix H by parallel cyclic Jacobi: each
 // round applies p/2 disjoint plane rotations chosen by the round-robin
 // tournament (player n-1 fixed, the rest rotating); a rotation is skipped when
 // its off-diagonal entry is negligible against the geometric mean of the two
-// diagonal entries, and the sweeps stop once a whole sweep skips every pair.
-__global__ __launch_bounds__(kThreads) void jacobi_k(BuildArgs a) {
+// diagonal entries or against 1e-17 ||H||_F, and the sweeps stop once a whole
+// sweep skips every pair.
+constexpr int kJacobiThreads = 1024;
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   __shared__ double A[kBuildMaxSubspace][kBuildMaxSubspace + 1];
   __shared__ double E[kBuildMaxSubspace][kBuildMaxSubspace + 1];
   __shared__ double cs[kBuildMaxSubspace / 2], sn[kBuildMaxSubspace / 2];
   __shared__ int pp[kBuildMaxSubspace / 2], qq[kBuildMaxSubspace / 2];
   __shared__ int order[kBuildMaxSubspace];
   __shared__ int rotated;
+  __shared__ double red[kJacobiThreads / 64];
   const int p = a.p;
   const int n = p + (p & 1);  // an even number of players; index p is a bye when p is odd
+  double ss = 0.0;
   for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
     const int r = e / p, c = e % p;
-    A[r][c] = 0.5 * (a.h[r * p + c] + a.h[c * p + r]);
+    const double v = 0.5 * (a.h[r * p + c] + a.h[c * p + r]);
+    A[r][c] = v;
     E[r][c] = r == c ? 1.0 : 0.0;
+    ss += v * v;
   }
+  // entries below 1e-17 ||H||_F are left alone: rounding noise of that size
+  // reappears with every rotation, so chasing it would never end
+  const double floor_abs = fmax(1e-17 * sqrt(block_sum(ss, red)), 1e-300);
   for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
     __syncthreads();
     if (threadIdx.x == 0) rotated = 0;
@@ -294,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void jacobi_k(BuildArgs a) {
         double c = 1.0, s = 0.0;
         if (hi < p) {
           const double apq = A[lo][hi], app = A[lo][lo], aqq = A[hi][hi];
-          if (fabs(apq) > 1e-300 && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
+          if (fabs(apq) > floor_abs && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
             const double th = (aqq - app) / (2.0 * apq);
             const double t = fabs(th) > 1e150 ? 0.5 / th : (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(1.0 + th * th));
             c = 1.0 / sqrt(1.0 + t * t);
@@ -308,25 +436,31 @@ __global__ __launch_bounds__(kThreads) void jacobi_k(BuildArgs a) {
         sn[k] = s;
       }
       __syncthreads();
-      for (int e = threadIdx.x; e < (n / 2) * p; e += blockDim.x) {  // A <- J^T A
-        const int k = e / p, col = e % p;
+      // the waves take the pairs in turn; the 64 lanes of a wave walk the rows/columns
+      const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+      for (int k = wv; k < n / 2; k += kJacobiThreads / 64) {  // A <- J^T A
         if (qq[k] >= p || sn[k] == 0.0) continue;
+        const int lo = pp[k], hi = qq[k];
         const double c = cs[k], s = sn[k];
-        const double x = A[pp[k]][col], y = A[qq[k]][col];
-        A[pp[k]][col] = c * x - s * y;
-        A[qq[k]][col] = s * x + c * y;
+        for (int col = ln; col < p; col += 64) {
+          const double x = A[lo][col], y = A[hi][col];
+          A[lo][col] = c * x - s * y;
+          A[hi][col] = s * x + c * y;
+        }
       }
       __syncthreads();
-      for (int e = threadIdx.x; e < (n / 2) * p; e += blockDim.x) {  // A <- A J, E <- E J
-        const int k = e / p, row = e % p;
+      for (int k = wv; k < n / 2; k += kJacobiThreads / 64) {  // A <- A J, E <- E J
         if (qq[k] >= p || sn[k] == 0.0) continue;
+        const int lo = pp[k], hi = qq[k];
         const double c = cs[k], s = sn[k];
-        const double x = A[row][pp[k]], y = A[row][qq[k]];
-        A[row][pp[k]] = c * x - s * y;
-        A[row][qq[k]] = s * x + c * y;
-        const double u = E[row][pp[k]], v = E[row][qq[k]];
-        E[row][pp[k]] = c * u - s * v;
-        E[row][qq[k]] = s * u + c * v;
+        for (int row = ln; row < p; row += 64) {
+          const double x = A[row][lo], y = A[row][hi];
+          A[row][lo] = c * x - s * y;
+          A[row][hi] = s * x + c * y;
+          const double u = E[row][lo], v = E[row][hi];
+          E[row][lo] = c * u - s * v;
+          E[row][hi] = s * u + c * v;
+        }
       }
       __syncthreads();
     }
@@ -379,8 +513,8 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 size_t build_workspace_bytes(int64_t T, int64_t W, int64_t m) {
   const int64_t p = std::min<int64_t>(kBuildMaxSubspace, std::min(W, T));
   const size_t d = sizeof(double);
-  return align256(T * W * d) + align256(W * W * d) + 2 * align256(p * W * d) + 2 * align256(p * p * d) +
-         align256(p * d) + align256(W * m * d);
+  return align256(T * W * d) + align256(W * W * d) + 2 * align256(p * W * d) + 4 * align256(p * p * d) +
+         align256(p * d) + align256(W * m * d) + 256;
 }
 
 void build_workspace_carve(BuildArgs& a, void* ws) {
@@ -399,6 +533,9 @@ void build_workspace_carve(BuildArgs& a, void* ws) {
   a.evec = take((int64_t)a.p * a.p);
   a.lam = take(a.p);
   a.vm = take((int64_t)a.W * a.m);
+  a.bz = take((int64_t)a.p * a.p);
+  a.lf = take((int64_t)a.p * a.p);
+  a.flag = (int*)c;
 }
 
 hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
@@ -408,15 +545,28 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
   const int tiles = (a.W + 31) / 32;
   hipLaunchKernelGGL(gram_k, dim3(tiles * (tiles + 1) / 2), blk, 0, st, a);
   hipLaunchKernelGGL(start_k, dim3(blocks_for((int64_t)a.p * a.W, kThreads)), blk, 0, st, a);
-  hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
-  const dim3 zgrid(blocks_for(a.W, kThreads), blocks_for(a.p, kZRows));
+  const dim3 dgrid(blocks_for((int64_t)a.p * a.p, kThreads / 64));
+  const dim3 tgrid(blocks_for(a.W, kTrsmWaves));
+  auto orthonormalise = [&]() {  // a.z -> a.q
+    hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.z, (const double*)a.z, a.bz);
+    hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, 0);
+    hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.z, a.q);
+    for (int pass = 1; pass <= 2; ++pass) {
+      hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.q, a.bz);
+      hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, pass);
+      hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.q, a.q);
+    }
+    hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
+  };
+  orthonormalise();
+  const dim3 zgrid(blocks_for(a.W, 64), blocks_for(a.p, kZRows));
   for (int it = 0; it <= a.iters; ++it) {  // the range finder's product, then `iters` power steps
     hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
-    hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
+    orthonormalise();
   }
   hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
-  hipLaunchKernelGGL(rr_k, dim3(blocks_for((int64_t)a.p * a.p, kThreads / 64)), blk, 0, st, a);
-  hipLaunchKernelGGL(jacobi_k, dim3(1), blk, 0, st, a);
+  hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.z, a.h);
+  hipLaunchKernelGGL(jacobi_k, dim3(1), dim3(kJacobiThreads), 0, st, a);
   hipLaunchKernelGGL(finish_k, dim3(blocks_for((int64_t)a.W * a.m, kThreads)), blk, 0, st, a);
   hipLaunchKernelGGL(usig_k, dim3(blocks_for((int64_t)a.T * a.m, kThreads)), blk, 0, st, a);
   return hipGetLastError();

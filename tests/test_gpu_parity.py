@@ -118,12 +118,14 @@ def test_deltas(delta):
 
 
 @pytest.mark.parametrize("variant", ["gqa64", "gptj128", "gptj64", "mla_gptj", "gqa96_generic", "mla_f32",
-                                     "mla_latent_odd_generic"])
+                                     "mla_latent_odd_generic", "mla_latent448", "mla_rope_only"])
 def test_layout_variants(variant):
     say(f"[layout] {variant}")
     if variant.startswith("mla"):
         dt = F32 if variant == "mla_f32" else BF16
-        lat = 200 if variant == "mla_latent_odd_generic" else 512
+        # 512: 128-column latent groups + a half group for the band; 448: 64-column groups;
+        # 0: the band alone (one half group); 200: not a multiple of 64 (generic kernel)
+        lat = {"mla_latent_odd_generic": 200, "mla_latent448": 448, "mla_rope_only": 0}.get(variant, 512)
         lay = LayoutSpec(MLA, dt, 2, latent_dim=lat, rope_dim=64, pairing=GPTJ if "gptj" in variant else NEOX)
         F = lat + 64
         chunks = [ChunkSpec(index=i, num_tokens=45 + 20 * i, delta=9000 * (i + 1), flags=PATCH, canon_id=i,
