@@ -94,13 +94,14 @@ def cpu_baseline(cfg: str, wl, sample_units: int):
     with ctx.Pool(len(parts)) as pool:
         res = pool.map(_oracle_units, parts)
     wall = max(r[0] for r in res)
+    cpu_s = sum(r[0] for r in res)
     n_units = sum(r[1] for r in res)
     T = wl.chunks[0].num_tokens
     tokens = n_units * T / wl.layout.num_layers     # a token is rehydrated once all its layers are done
     return {"value": tokens / wall, "unit": "tokens/s", "cores": len(parts), "kind": "oracle",
             "sample": f"{n_units} (chunk, layer) units of {T} tokens (K and V, fp64, rounded to bf16) of the "
-                      f"{cfg} workload, spread over {len(parts)} processes; {wall:.1f} s wall, input drawing "
-                      f"excluded"}
+                      f"{cfg} workload, spread over {len(parts)} processes; {wall:.1f} s wall, {cpu_s:.1f} CPU-s, "
+                      f"input drawing excluded"}
 
 
 # ----------------------------------------------------------------------------- patch builder
@@ -271,6 +272,33 @@ def main() -> int:
     e3.record(stream)
     torch.cuda.synchronize()
     kernel_us = e2.elapsed_time(e3) / args.steps * 1e3
+
+    # ---- per-launch spread: each launch between its own pair of events
+    n_dist = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for ea, eb in evs:
+        ea.record(stream)
+        abi.plan_launch(plan, stream)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+    pct = lambda q: per_launch[min(len(per_launch) - 1, int(q * len(per_launch)))]
+
+    # ---- the same chunks at delta 0 without a patch: a plain copy through the
+    # kernel's own access pattern, the practical ceiling for this workload's layout
+    pattern_gbps = None
+    cbytes = dw.copy_bytes()
+    if cbytes > 0:
+        cplan = abi.plan_upload(dw.layout, dw.copy_descs(), dw.pool_desc, dw.workspace, stream)
+        for _ in range(5):
+            abi.plan_launch(cplan, stream)
+        e6, e7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e6.record(stream)
+        for _ in range(n_dist):
+            abi.plan_launch(cplan, stream)
+        e7.record(stream)
+        torch.cuda.synchronize()
+        pattern_gbps = cbytes / (e6.elapsed_time(e7) / n_dist * 1e-3) / 1e9
     gc.enable()
 
     # ---- a plain device copy of known size: practical read+write ceiling, and the
@@ -316,11 +344,13 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "kernel_us": kernel_us,
+        "kernel_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "pattern_copy_GBps": pattern_gbps,
+        "frac_of_pattern_copy": (achieved / pattern_gbps) if pattern_gbps else None,
         "call_us_gpu": call_ms_gpu * 1e3,
         "algorithmic_bytes": alg_bytes,
         "kernel_tokens_per_s": tokens / (kernel_us * 1e-6),
-        "copy_ceiling_GBps": copy_gbps,
-        "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
+        "torch_copy_GBps": copy_gbps,
         "kernel_source_hash": kernel_source_hash(),
         "cpu_baseline": cpu,
     }

@@ -240,11 +240,26 @@ def pin_builder_planted(b):
     assert np.allclose(s[:r], sig, rtol=1e-12, atol=1e-15)
     res = b.residual_energy(delta, us, vt)
     assert abs(res - np.sum(sig[m:] ** 2)) <= 1e-12 * np.sum(sig ** 2)
-    # the compile-step deficit subtracts the relocated canonical (App. A)
+    # storage convention (Fig. 2(d), App. A): sigma folded into U, V^T with orthonormal rows
+    assert np.allclose(np.linalg.norm(us, axis=0), sig[:m], rtol=1e-12)
+    assert np.allclose(vt @ vt.T, np.eye(m), atol=1e-12)
+    # the compile-step deficit subtracts the relocated canonical (App. A): conditioned
+    # rows equal to the canonical rotated by delta (as a complex multiply, NeoX halves)
+    # plus a known matrix P give back exactly P
     x = rng.standard_normal((T, 128))
     cond = x + 0.0
     d = b.deficit(cond, x, 0, bands=[0], d_rot=128, base=1e4, pairing=0)
     assert np.all(d == 0)
+    delta, base = 777, 1e4
+    th = base ** (-2.0 * np.arange(64) / 128)
+    z = (x[:, :64] + 1j * x[:, 64:]) * np.exp(1j * delta * th)[None, :]
+    P = 0.01 * rng.standard_normal((T, 128))
+    cond = np.concatenate([z.real, z.imag], axis=1) + P
+    d = b.deficit(cond, x, delta, bands=[0], d_rot=128, base=base, pairing=0)
+    assert np.max(np.abs(d - P)) <= 1e-12
+    # ... and only for the rotated tensor: V's deficit is a plain difference
+    dv = b.deficit(x + P, x, delta, bands=[0], d_rot=128, base=base, pairing=0, rotate_this=False)
+    assert np.max(np.abs(dv - P)) <= 1e-15
 
 
 ORACLE_PINS = [pin_theta_geometric, pin_pairs_from_pages, pin_complex_multiply, pin_composition,

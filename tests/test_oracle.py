@@ -132,6 +132,55 @@ def test_pins_catch_planted_mistake(mutate):
     assert caught, f"no pin caught mutation {mutate.__name__}"
 
 
+BUILDER_PATH = os.path.join(os.path.dirname(builder.__file__), "builder_oracle.py")
+
+
+def _fresh_builder():
+    spec = importlib.util.spec_from_file_location("oracle.builder_oracle_mutant", BUILDER_PATH)
+    m = importlib.util.module_from_spec(spec)
+    m.__package__ = "oracle"
+    spec.loader.exec_module(m)
+    return m
+
+
+def _bmut_unrotated(m):
+    m.rotate = lambda x, *a, **k: np.asarray(x, dtype=np.float64)
+
+
+def _bmut_sigma_in_v(m):
+    orig = m.truncated_svd
+
+    def f(d, k):
+        us, vt, s = orig(d, k)
+        return us / s[:k][None, :], vt * s[:k][:, None], s
+    m.truncated_svd = f
+
+
+def _bmut_smallest(m):
+    def f(d, k):
+        u, s, vt = np.linalg.svd(d, full_matrices=False)
+        return u[:, -k:] * s[-k:][None, :], vt[-k:], s
+    m.truncated_svd = f
+
+
+def _bmut_rank_minus_one(m):
+    orig = m.truncated_svd
+
+    def f(d, k):
+        us, vt, s = orig(d, k)
+        return us[:, : k - 1], vt[: k - 1], s
+    m.truncated_svd = f
+
+
+@pytest.mark.parametrize("mutate", [_bmut_unrotated, _bmut_sigma_in_v, _bmut_smallest, _bmut_rank_minus_one],
+                         ids=lambda f: f.__name__[6:])
+def test_builder_pin_catches_planted_mistake(mutate):
+    m = _fresh_builder()
+    mutate(m)
+    with pytest.raises(AssertionError):
+        pin_builder_planted(m)
+
+
 # ---------------------------------------------------------------- tolerance predicate
 def test_tolerance_predicate():
     y = np.array([1.0, -2.5, 3.0e-3, 100.0])

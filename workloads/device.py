@@ -159,6 +159,23 @@ class DeviceWorkload:
             kw["factors"] = fl
         return abi.ChunkDesc(**kw)
 
+    def copy_descs(self) -> list:
+        """The same chunks with delta 0 and no patch: the operator then copies each
+        out-of-place chunk through its own access pattern (in-place chunks do nothing)."""
+        out = []
+        for c in self.wl.chunks:
+            d = self._desc(c)
+            d.c.delta = 0
+            d.c.flags = d.c.flags & ~abi.PATCH
+            d.c.num_factors = 0
+            out.append(d)
+        return out
+
+    def copy_bytes(self) -> int:
+        """Bytes moved by copy_descs(): each out-of-place row read once and written once."""
+        return sum(self.L * self.lay.num_tensors * 2 * c.num_tokens * self.F * self.es
+                   for c in self.wl.chunks if not c.in_place)
+
     # ------------------------------------------------------------------ running
     def run(self, stream=None, chunks: Optional[Sequence[int]] = None) -> None:
         descs = self.descs if chunks is None else [self.descs[i] for i in chunks]
