@@ -82,7 +82,7 @@ struct alignas(16) DevHeader {
   int32_t rope_group;   // MFMA path, MLA: group id of the rope band (-1 for GQA)
   double rope_base;
   int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
-  int32_t pad;
+  int32_t xcd_window_log2;  // MFMA path: log2 of the workgroups an XCD takes in a row (0: plain order)
 };
 
 }  // namespace kamera

@@ -333,6 +333,14 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   hd->rope_base = L->rope_base;
   hd->group_cols = mfma ? (L->family == KAMERA_GQA ? L->head_dim : kSlab) : F;
   hd->rope_group = (mfma && L->family == KAMERA_MLA) ? L->latent_dim / kSlab : -1;
+  // XCD window (measured on MI355X): rows of more than 8 column groups (e.g. 32 heads x
+  // 128) span several workgroups and gain 19% from keeping a row's workgroups on one
+  // XCD (W = 16); rows of exactly 8 groups gain ~1% with W = 4; narrower rows, where a
+  // workgroup already covers whole rows, are fastest in plain order.
+  if (mfma) {
+    const int ngroups = F / hd->group_cols;
+    hd->xcd_window_log2 = ngroups > kWavesPerBlock ? 4 : (ngroups == kWavesPerBlock ? 2 : 0);
+  }
 
   const int tb_tokens = mfma ? kMfmaRangeTokens : 16;
   int64_t task = 0;

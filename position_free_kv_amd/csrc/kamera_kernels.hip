@@ -430,8 +430,23 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const DevHeader& hd = *hdr;
-  // plain dispatch order: waves running together stream neighbouring rows
-  const int64_t task = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  // Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8).
+  // For rows wider than one workgroup's heads, windows of 8*W workgroups are
+  // remapped so that XCD x runs W consecutive logical workgroups: whole rows of a
+  // token block, and the V operands they share, stay in one XCD's L2. Narrow rows
+  // keep the plain order (W = 1), where neighbouring workgroups already stream
+  // neighbouring rows. The map is a bijection; a partial last window is unchanged.
+  int64_t blk = blockIdx.x;
+  if (hd.xcd_window_log2 > 0) {
+    const int wl = hd.xcd_window_log2;
+    const int64_t win = (int64_t)8 << wl;
+    const int64_t nfull = ((int64_t)gridDim.x >> (3 + wl)) << (3 + wl);
+    if (blk < nfull) {
+      const int64_t x = blk & 7, j = blk >> 3;
+      blk = (j >> wl) * win + (x << wl) + (j & ((1 << wl) - 1));
+    }
+  }
+  const int64_t task = blk * kWavesPerBlock + wave;
   if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
   const TaskCoord tcd = decode_task(hd, chunks, task);
   const DevChunk& ch = chunks[tcd.chunk];
