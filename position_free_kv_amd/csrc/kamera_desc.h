@@ -38,7 +38,8 @@ struct alignas(16) DevFactor {
 static_assert(sizeof(DevFactor) == 48, "DevFactor layout");
 
 // Per-chunk record. Task space of a chunk (MFMA path: one task = one wave; generic: one workgroup):
-//   task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+//   chunk-major:  task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+//   layer-major:  task = layer * layer_tasks + task0 + (stream * ntb + tb) * ngroups + g
 // stream indexes the tensors this chunk touches (stream_tensor[]), tb the token
 // block, g the column group (MFMA path: head or slab; generic path: unused = 1).
 struct alignas(16) DevChunk {
@@ -83,6 +84,8 @@ struct alignas(16) DevHeader {
   double rope_base;
   int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
   int32_t xcd_window_log2;  // MFMA path: log2 of the workgroups an XCD takes in a row (0: plain order)
+  int64_t layer_tasks;  // > 0: layer-major task order, this many tasks per layer (task0 within a layer)
+  int64_t pad2;
 };
 
 }  // namespace kamera

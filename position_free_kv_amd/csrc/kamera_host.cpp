@@ -146,6 +146,12 @@ struct Packed {
   int variant = 0;
 };
 
+// Task order of batches with paged destinations (see the kernel's decode_task):
+// layer-major keeps the workgroups in flight inside one layer's slice of the pool
+// (a pool layer is ~180 MB at 36-layer deque sizes); measured 1.5% faster on the
+// 16-token random-page deque than chunk-major.
+constexpr bool kLayerMajorPaged = true;
+
 // Is the bf16 MFMA kernel able to run this layout at all?
 bool mfma_layout_ok(const kamera_layout* L) {
   if (L->dtype != KAMERA_BF16) return false;
@@ -343,6 +349,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   }
 
   const int tb_tokens = mfma ? kMfmaRangeTokens : 16;
+  const bool layer_major = kLayerMajorPaged && mfma && any_paged;
   int64_t task = 0;
   int64_t page_cursor = 0;
   out.page_off.assign((size_t)n, -1);
@@ -425,7 +432,11 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
       d.group0 = 0;
       d.ngroups = 1;
     }
-    task += (int64_t)d.nstreams * L->num_layers * d.ntb * d.ngroups;
+    task += (int64_t)d.nstreams * (layer_major ? 1 : L->num_layers) * d.ntb * d.ngroups;
+  }
+  if (layer_major) {
+    hd->layer_tasks = task;
+    task *= L->num_layers;
   }
   hd->total_tasks = task;
   out.tasks = task;

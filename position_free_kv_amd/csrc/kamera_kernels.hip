@@ -83,13 +83,27 @@ struct TaskCoord {
 };
 
 // (chunk, layer, stream, token block, group) of a task:
-//   task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+//   chunk-major:  task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
+//   layer-major:  task = layer * layer_tasks + task0 + (stream * ntb + tb) * ngroups + g
 __device__ __forceinline__ TaskCoord decode_task(const DevHeader& hd, const DevChunk* __restrict__ chunks,
                                                  int64_t task) {
   TaskCoord tc;
+  int64_t r;
+  if (hd.layer_tasks > 0) {
+    tc.layer = (int)(task / hd.layer_tasks);
+    const int64_t in_layer = task - (int64_t)tc.layer * hd.layer_tasks;
+    tc.chunk = find_chunk(chunks, hd.nchunks, in_layer);
+    const DevChunk& ch = chunks[tc.chunk];
+    r = in_layer - ch.task0;
+    tc.g = ch.group0 + (int)(r % ch.ngroups);
+    r /= ch.ngroups;
+    tc.tb = (int)(r % ch.ntb);
+    tc.stream = (int)(r / ch.ntb);
+    return tc;
+  }
   tc.chunk = find_chunk(chunks, hd.nchunks, task);
   const DevChunk& ch = chunks[tc.chunk];
-  int64_t r = task - ch.task0;
+  r = task - ch.task0;
   tc.g = ch.group0 + (int)(r % ch.ngroups);
   r /= ch.ngroups;
   tc.tb = (int)(r % ch.ntb);

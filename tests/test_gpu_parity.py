@@ -179,6 +179,28 @@ def test_paged_slot0(slot0):
     assert pool_untouched_ok(dw)
 
 
+def test_mixed_dense_paged_and_in_place_batch():
+    """One batch mixing dense destinations, paged destinations, an in-place survivor and an
+    empty chunk: a batch with any paged chunk runs in layer-major task order, so every
+    chunk type is decoded from within-layer offsets."""
+    say("[mixed batch]")
+    P = 16
+    lay = LayoutSpec(GQA, BF16, 3, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=P)
+    pages = np.random.default_rng(5).permutation(48).astype(np.int32)
+    facs = lambda i: [factor(i, 0, 0, 0, 256, 32), factor(i, 1, 1, 0, 256, 32)]
+    chunks = [ChunkSpec(index=0, num_tokens=150, delta=900, flags=PATCH, canon_id=0, factors=facs(0), dst_buffer=0),
+              ChunkSpec(index=1, num_tokens=0, delta=5, flags=PATCH, canon_id=1, factors=facs(1), dst_buffer=1),
+              ChunkSpec(index=2, num_tokens=70, delta=-300, flags=PATCH, canon_id=2, factors=facs(2),
+                        block_table=pages[0:5].copy(), slot0=3),
+              ChunkSpec(index=3, num_tokens=200, delta=-1234, flags=IN_PLACE, canon_id=3,
+                        block_table=pages[5:18].copy(), slot0=0, role="survivor"),
+              ChunkSpec(index=4, num_tokens=33, delta=77, flags=0, canon_id=4, dst_buffer=2)]
+    wl = custom_workload(lay, chunks, dense_rows=[150, 1, 33], num_pages=48)
+    dw = run_dw(wl)
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
+
+
 def test_in_place_with_patch_mla_and_gqa():
     """In place with a patch: re-conditioning a resident chunk (rotate + add)."""
     say("[in-place+patch]")
