@@ -262,6 +262,33 @@ def pin_builder_planted(b):
     assert np.max(np.abs(dv - P)) <= 1e-15
 
 
+def pin_orbit_mean(b):
+    """Orbit deficit (preprint §5, reorder): with conditioned blocks built as the
+    canonical rotated to each ordering's offset (complex multiply, NeoX halves) plus a
+    common matrix P and per-ordering parts N_k that sum to zero, the orbit deficit is
+    exactly P. One ordering reduces to the single deficit; the order of the orderings
+    does not matter."""
+    rng = np.random.default_rng(21)
+    T, d, base = 40, 64, 1e6
+    x = rng.standard_normal((T, d))
+    P = 0.1 * rng.standard_normal((T, d))
+    deltas = [0, 2048, -4096, 6144, 123457]
+    N = rng.standard_normal((len(deltas), T, d))
+    N -= N.mean(axis=0, keepdims=True)
+    th = base ** (-2.0 * np.arange(d // 2) / d)
+    conds = []
+    for k, dl in enumerate(deltas):
+        z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * dl * th)[None, :]
+        conds.append(np.concatenate([z.real, z.imag], axis=1) + P + N[k])
+    kw = dict(bands=[0], d_rot=d, base=base, pairing=0)
+    got = b.orbit_deficit(conds, x, deltas, **kw)
+    assert np.max(np.abs(got - P)) <= 1e-12
+    assert np.max(np.abs(b.orbit_deficit(conds[:1], x, deltas[:1], **kw) - b.deficit(conds[0], x, deltas[0], **kw))) == 0
+    perm = [3, 0, 4, 2, 1]
+    rev = b.orbit_deficit([conds[i] for i in perm], x, [deltas[i] for i in perm], **kw)
+    assert np.max(np.abs(rev - got)) <= 1e-14
+
+
 ORACLE_PINS = [pin_theta_geometric, pin_pairs_from_pages, pin_complex_multiply, pin_composition,
                pin_norm_and_inverse, pin_identity, pin_large_delta_phase, pin_patch_is_matmul,
                pin_full_rank_reconstructs, pin_survivor_rotation_only, pin_paging_bruteforce,

@@ -8,7 +8,7 @@ import pytest
 import oracle.builder_oracle as builder
 import oracle.kamera_oracle as O
 from oracle import tolerance as tol
-from tests.oracle_pins import ORACLE_PINS, pin_builder_planted
+from tests.oracle_pins import ORACLE_PINS, pin_builder_planted, pin_orbit_mean
 
 ORACLE_PATH = os.path.join(os.path.dirname(O.__file__), "kamera_oracle.py")
 
@@ -20,6 +20,10 @@ def test_oracle_pin(pin):
 
 def test_builder_pin():
     pin_builder_planted(builder)
+
+
+def test_orbit_pin():
+    pin_orbit_mean(builder)
 
 
 # ---------------------------------------------------------------- planted mistakes
@@ -179,6 +183,34 @@ def test_builder_pin_catches_planted_mistake(mutate):
     mutate(m)
     with pytest.raises(AssertionError):
         pin_builder_planted(m)
+
+
+def _omut_sum_not_mean(m):
+    orig = m.orbit_deficit
+    m.orbit_deficit = lambda xs, x, ds, **kw: orig(xs, x, ds, **kw) * len(xs)
+
+
+def _omut_first_delta(m):
+    orig = m.orbit_deficit
+    m.orbit_deficit = lambda xs, x, ds, **kw: orig(xs, x, [ds[0]] * len(ds), **kw)
+
+
+def _omut_unrotated(m):
+    m.rotate = lambda x, *a, **k: np.asarray(x, dtype=np.float64)
+
+
+def _omut_drop_last(m):
+    orig = m.orbit_deficit
+    m.orbit_deficit = lambda xs, x, ds, **kw: orig(xs[:-1], x, ds[:-1], **kw) if len(xs) > 1 else orig(xs, x, ds, **kw)
+
+
+@pytest.mark.parametrize("mutate", [_omut_sum_not_mean, _omut_first_delta, _omut_unrotated, _omut_drop_last],
+                         ids=lambda f: f.__name__[6:])
+def test_orbit_pin_catches_planted_mistake(mutate):
+    m = _fresh_builder()
+    mutate(m)
+    with pytest.raises(AssertionError):
+        pin_orbit_mean(m)
 
 
 # ---------------------------------------------------------------- tolerance predicate
