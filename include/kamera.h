@@ -208,13 +208,28 @@ kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream);
  * [0, 64]. The workspace (256-byte aligned, kamera_build_workspace_bytes bytes) and the
  * outputs must not overlap the inputs. The call is stream-ordered and does not
  * synchronise; the library allocates nothing. */
-enum { KAMERA_BUILD_MAX_RANK = 64, KAMERA_BUILD_MAX_SUBSPACE = 80 };
+enum { KAMERA_BUILD_MAX_RANK = 64, KAMERA_BUILD_MAX_SUBSPACE = 80, KAMERA_BUILD_MAX_ORBIT = 32 };
 size_t kamera_build_workspace_bytes(int64_t num_tokens, int32_t width, int32_t rank);
 kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, const void* x_cond,
                                  const void* x_canon, int64_t num_tokens, int64_t delta, int32_t col0,
                                  int32_t width, int32_t rank, int32_t iterations, void* u_out,
                                  void* v_out, double* sigma_out, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* Orbit patch (preprint §5, reorder): one patch for every ordering of a cached set. The
+ * chunk sat at offset deltas[k] in ordering k and x_conds[k] holds its conditioned rows
+ * there; the factors are those of the mean deficit
+ *     (1/K) sum_k (x_conds[k] - R(deltas[k]) x_canon)
+ * (the ordering held out for evaluation is simply not passed). x_conds and deltas are
+ * HOST arrays of num_orderings entries in [1, KAMERA_BUILD_MAX_ORBIT], read during the
+ * call; each x_conds[k] is a device pointer laid out like x_canon. Everything else is
+ * as kamera_build_patch (which is this call with one ordering). */
+kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tensor, int32_t num_orderings,
+                                       const void* const* x_conds, const int64_t* deltas,
+                                       const void* x_canon, int64_t num_tokens, int32_t col0,
+                                       int32_t width, int32_t rank, int32_t iterations, void* u_out,
+                                       void* v_out, double* sigma_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* kamera_status_string(kamera_status status);

@@ -22,13 +22,14 @@ MAX_FACTORS = 4
 MAX_RANK = 256
 BUILD_MAX_RANK = 64
 BUILD_MAX_SUBSPACE = 80
+BUILD_MAX_ORBIT = 32
 
 STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAMERA_E_RANK",
           "KAMERA_E_DELTA", "KAMERA_E_PAGE", "KAMERA_E_OVERLAP", "KAMERA_E_ALIGN",
           "KAMERA_E_WORKSPACE", "KAMERA_E_UNSUPPORTED", "KAMERA_E_HIP"]
 EXPORTED = ["kamera_workspace_bytes", "kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
             "kamera_plan_upload", "kamera_plan_launch", "kamera_status_string", "kamera_last_error",
-            "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch"]
+            "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch", "kamera_build_orbit_patch"]
 
 
 class Layout(ctypes.Structure):
@@ -94,8 +95,11 @@ def lib() -> ctypes.CDLL:
         L.kamera_build_workspace_bytes.restype = sz
         L.kamera_build_patch.argtypes = [ctypes.POINTER(Layout), i32, vp, vp, i64, i64, i32, i32, i32, i32,
                                          vp, vp, vp, vp, sz, vp]
+        L.kamera_build_orbit_patch.argtypes = [ctypes.POINTER(Layout), i32, i32, ctypes.POINTER(vp),
+                                               ctypes.POINTER(i64), vp, i64, i32, i32, i32, i32, vp, vp, vp, vp,
+                                               sz, vp]
         for fn in ("kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched", "kamera_plan_upload",
-                   "kamera_plan_launch", "kamera_build_patch"):
+                   "kamera_plan_launch", "kamera_build_patch", "kamera_build_orbit_patch"):
             getattr(L, fn).restype = ctypes.c_int
         L.kamera_status_string.argtypes = [ctypes.c_int]
         L.kamera_status_string.restype = ctypes.c_char_p
@@ -213,6 +217,19 @@ def build_patch(layout: Layout, tensor: int, x_cond, x_canon, num_tokens: int, d
                                     int(num_tokens), int(delta), int(col0), int(width), int(rank),
                                     int(iterations), _ptr(u_out), _ptr(v_out), _ptr(sigma_out), wp, wb,
                                     _stream(stream)))
+
+
+def build_orbit_patch(layout: Layout, tensor: int, x_conds: Sequence, deltas: Sequence[int], x_canon,
+                      num_tokens: int, col0: int, width: int, rank: int, iterations: int, u_out, v_out, sigma_out,
+                      workspace, stream=None) -> None:
+    """Top-`rank` factors of the mean deficit over the orderings (x_conds[k], deltas[k])."""
+    k = len(x_conds)
+    conds = (ctypes.c_void_p * max(k, 1))(*[_ptr(x) for x in x_conds])
+    ds = (ctypes.c_int64 * max(len(deltas), 1))(*[int(d) for d in deltas])
+    wp, wb = _ws(workspace)
+    _check(lib().kamera_build_orbit_patch(ctypes.byref(layout), int(tensor), k, conds, ds, _ptr(x_canon),
+                                          int(num_tokens), int(col0), int(width), int(rank), int(iterations),
+                                          _ptr(u_out), _ptr(v_out), _ptr(sigma_out), wp, wb, _stream(stream)))
 
 
 def relocate(layout: Layout, pool: Pool, block_table, slot0: int, num_tokens: int, delta: int, workspace,

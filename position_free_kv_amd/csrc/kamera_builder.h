@@ -11,9 +11,12 @@ constexpr int kBuildMaxSubspace = 80;   // iterated subspace p = min(80, width, 
 constexpr int kBuildMaxPairs = 256;     // d_rot <= 512
 constexpr int kBuildMaxSweeps = 40;     // Jacobi sweeps (quadratic convergence: ~6-10 needed)
 constexpr double kBuildJacobiTol = 2.220446049250313e-16;
+constexpr int kBuildMaxOrbit = 32;      // orderings averaged by an orbit patch
 
 struct BuildArgs {
-  const void* x_cond;   // [T][F] storage dtype
+  const void* x_cond[kBuildMaxOrbit];     // per ordering: [T][F] storage dtype
+  int64_t delta_k[kBuildMaxOrbit];        // per ordering: the relocation offset
+  int norbit;                             // orderings averaged (1: a single deficit)
   const void* x_canon;  // [T][F]
   void* u_out;          // [T][m]
   void* v_out;          // [W][m]
@@ -29,7 +32,6 @@ struct BuildArgs {
   double* bz;           // [p][p]  Gram of the block being orthonormalised
   double* lf;           // [p][p]  its Cholesky factor (lower)
   int* flag;            // 1: Cholesky QR rejected the block, the CGS2 fallback runs
-  int64_t delta_pos;    // the relocation offset
   double base;          // RoPE base
   int T, F, W, col0, m, p, iters;
   int dtype;            // 0 fp32, 1 bf16

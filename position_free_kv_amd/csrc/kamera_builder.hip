@@ -1,7 +1,8 @@
 // Patch builder (the compile step) for gfx950: top-m factors of the deficit
 //     Delta = KV(B|A) - R(delta) . KV(B|empty)
 // Kamera preprint, §2 Eq. 2 (the deficit) and App. A (compile step: conditioned
-// rows minus the relocated canonical, truncated SVD stored as U*Sigma and V).
+// rows minus the relocated canonical, truncated SVD stored as U*Sigma and V), or of
+// the mean deficit over a set of orderings (§5, reorder: the orbit patch).
 //
 // Method: randomized subspace iteration with a Rayleigh-Ritz step (Halko,
 // Martinsson & Tropp, SIAM Review 2011, §4.5 and §5.3) on the Gram matrix
@@ -90,19 +91,28 @@ __device__ __forceinline__ double hash_uniform(uint64_t x) {
   return (double)(x >> 11) * (2.0 / 9007199254740992.0) - 1.0;
 }
 
-// Delta[t][w] = x_cond[t][c] - (R(delta) x_canon)[t][c], c = col0 + w, in fp64.
-// Rotation as in the relocation operator: theta_i = base^(-2i/d_rot), angle
-// delta*theta_i, NeoX pairs (i, i + d_rot/2) or GPT-J pairs (2i, 2i + 1) per band.
+// Delta[t][w] = mean_k x_cond_k[t][c] - (Rbar x_canon)[t][c], c = col0 + w, in fp64,
+// where Rbar = mean_k R(delta_k) acts on each rotary pair as [[cbar, -sbar], [sbar, cbar]]
+// (cbar, sbar the means of cos and sin of delta_k theta_i). By linearity this is the
+// mean of the per-ordering deficits x_cond_k - R(delta_k) x_canon (one ordering: the
+// plain deficit). Rotation as in the relocation operator: theta_i = base^(-2i/d_rot),
+// NeoX pairs (i, i + d_rot/2) or GPT-J pairs (2i, 2i + 1) per band.
 __global__ __launch_bounds__(kThreads) void delta_k(BuildArgs a) {
   __shared__ double cs_tab[kBuildMaxPairs], sn_tab[kBuildMaxPairs];
   const int npairs = a.d_rot / 2;
+  const double inv_k = 1.0 / (double)a.norbit;
   if (a.rotate)
     for (int i = threadIdx.x; i < npairs; i += blockDim.x) {
       const double th = pow(a.base, (-2.0 * (double)i) / (double)a.d_rot);
-      double s, c;
-      sincos((double)a.delta_pos * th, &s, &c);
-      cs_tab[i] = c;
-      sn_tab[i] = s;
+      double cm = 0.0, sm = 0.0;
+      for (int k = 0; k < a.norbit; ++k) {
+        double s, c;
+        sincos((double)a.delta_k[k] * th, &s, &c);
+        cm += c;
+        sm += s;
+      }
+      cs_tab[i] = cm * inv_k;
+      sn_tab[i] = sm * inv_k;
     }
   __syncthreads();
   const int64_t n = (int64_t)a.T * a.W;
@@ -132,7 +142,9 @@ __global__ __launch_bounds__(kThreads) void delta_k(BuildArgs a) {
         solo = first ? solo * cv - other * sv : other * sv + solo * cv;
       }
     }
-    a.delta[e] = load_x(a.x_cond, a.dtype, row + c) - solo;
+    double cond = 0.0;
+    for (int k = 0; k < a.norbit; ++k) cond += load_x(a.x_cond[k], a.dtype, row + c);
+    a.delta[e] = cond * inv_k - solo;
   }
 }
 

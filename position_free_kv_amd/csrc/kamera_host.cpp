@@ -230,7 +230,12 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
         mfma = false;
     }
     // destination
-    const bool touches_v = ntensors == 2 && !(in_place && !patch);
+    // V is touched out of place always, in place only by a patch with a V factor (the
+    // packing below streams the same tensors)
+    bool v_factor = false;
+    for (int f = 0; patch && f < c.num_factors; ++f)
+      if (c.factors[f].tensor == 1 && c.factors[f].rank > 0) v_factor = true;
+    const bool touches_v = ntensors == 2 && (!in_place || v_factor);
     if (paged) {
       if (touches_v && !pool->v_pool) return fail(KAMERA_E_NULL, "chunk %d: pool.v_pool is NULL", i);
       if (c.slot0 < 0 || c.slot0 >= P) return fail(KAMERA_E_PAGE, "chunk %d: slot0 must be in [0, page_size)", i);
@@ -565,24 +570,39 @@ size_t kamera_build_workspace_bytes(int64_t num_tokens, int32_t width, int32_t r
   return build_workspace_bytes(num_tokens, width, rank);
 }
 
-kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, const void* x_cond,
-                                 const void* x_canon, int64_t num_tokens, int64_t delta, int32_t col0,
-                                 int32_t width, int32_t rank, int32_t iterations, void* u_out, void* v_out,
-                                 double* sigma_out, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+static_assert(KAMERA_BUILD_MAX_ORBIT == kBuildMaxOrbit, "orbit limit of the ABI and the builder");
+static_assert(KAMERA_BUILD_MAX_RANK == kBuildMaxRank, "rank limit of the ABI and the builder");
+static_assert(KAMERA_BUILD_MAX_SUBSPACE == kBuildMaxSubspace, "subspace size of the ABI and the builder");
+
+kamera_status build_impl(const kamera_layout* layout, int32_t tensor, int32_t norbit, const void* const* x_conds,
+                         const int64_t* deltas, const void* x_canon, int64_t num_tokens, int32_t col0,
+                         int32_t width, int32_t rank, int32_t iterations, void* u_out, void* v_out,
+                         double* sigma_out, void* workspace, size_t workspace_bytes, void* stream) {
   kamera_status st = check_layout(layout);
   if (st != KAMERA_OK) return st;
   const bool gqa = layout->family == KAMERA_GQA;
   if (tensor < 0 || tensor > (gqa ? 1 : 0))
     return fail(KAMERA_E_SHAPE, "tensor %d invalid for this family", tensor);
-  if (!x_cond || !x_canon) return fail(KAMERA_E_NULL, "x_cond or x_canon is NULL");
-  if (!u_out || !v_out) return fail(KAMERA_E_NULL, "u_out or v_out is NULL");
+  if (norbit < 1 || norbit > KAMERA_BUILD_MAX_ORBIT)
+    return fail(KAMERA_E_SHAPE, "num_orderings must be in [1, %d] (got %d)", KAMERA_BUILD_MAX_ORBIT, norbit);
+  if (!x_conds || !deltas) return fail(KAMERA_E_NULL, "x_conds or deltas is NULL");
   const size_t es = layout->dtype == KAMERA_BF16 ? 2 : 4;
-  if (!aligned(x_cond, es) || !aligned(x_canon, es) || !aligned(u_out, es) || !aligned(v_out, es))
+  for (int k = 0; k < norbit; ++k) {
+    if (!x_conds[k]) return fail(KAMERA_E_NULL, "x_cond of ordering %d is NULL", k);
+    if (!aligned(x_conds[k], es)) return fail(KAMERA_E_ALIGN, "x_cond of ordering %d must be aligned to %zu bytes", k, es);
+    if (deltas[k] <= -(int64_t(1) << 31) || deltas[k] >= (int64_t(1) << 31))
+      return fail(KAMERA_E_DELTA, "ordering %d: |delta| must be < 2^31", k);
+  }
+  if (!x_canon) return fail(KAMERA_E_NULL, "x_canon is NULL");
+  if (!u_out || !v_out) return fail(KAMERA_E_NULL, "u_out or v_out is NULL");
+  if (!aligned(x_canon, es) || !aligned(u_out, es) || !aligned(v_out, es))
     return fail(KAMERA_E_ALIGN, "row and factor pointers must be aligned to %zu bytes", es);
   if (sigma_out && !aligned(sigma_out, sizeof(double))) return fail(KAMERA_E_ALIGN, "sigma_out must be 8-byte aligned");
   if (num_tokens < 1 || num_tokens > (1 << 24)) return fail(KAMERA_E_SHAPE, "num_tokens must be in [1, 2^24]");
-  if (delta <= -(int64_t(1) << 31) || delta >= (int64_t(1) << 31)) return fail(KAMERA_E_DELTA, "|delta| must be < 2^31");
   const int F = row_width(layout);
   if (col0 < 0 || width < 1 || (int64_t)col0 + width > F)
     return fail(KAMERA_E_SHAPE, "columns [%d, %lld) outside the row of %d", col0, (long long)col0 + width, F);
@@ -598,12 +618,15 @@ kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, co
 
   BuildArgs a;
   std::memset(&a, 0, sizeof(a));
-  a.x_cond = x_cond;
+  for (int k = 0; k < norbit; ++k) {
+    a.x_cond[k] = x_conds[k];
+    a.delta_k[k] = deltas[k];
+  }
+  a.norbit = norbit;
   a.x_canon = x_canon;
   a.u_out = u_out;
   a.v_out = v_out;
   a.sigma = sigma_out;
-  a.delta_pos = delta;
   a.base = layout->rope_base;
   a.T = (int)num_tokens;
   a.F = F;
@@ -630,6 +653,32 @@ kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, co
   const hipError_t e = launch_builder(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KAMERA_E_HIP, "builder launch failed: %s", hipGetErrorString(e));
   return KAMERA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kamera_status kamera_build_patch(const kamera_layout* layout, int32_t tensor, const void* x_cond,
+                                 const void* x_canon, int64_t num_tokens, int64_t delta, int32_t col0,
+                                 int32_t width, int32_t rank, int32_t iterations, void* u_out, void* v_out,
+                                 double* sigma_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!x_cond) return fail(KAMERA_E_NULL, "x_cond is NULL");
+  const void* conds[1] = {x_cond};
+  const int64_t deltas[1] = {delta};
+  return build_impl(layout, tensor, 1, conds, deltas, x_canon, num_tokens, col0, width, rank, iterations, u_out,
+                    v_out, sigma_out, workspace, workspace_bytes, stream);
+}
+
+kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tensor, int32_t num_orderings,
+                                       const void* const* x_conds, const int64_t* deltas, const void* x_canon,
+                                       int64_t num_tokens, int32_t col0, int32_t width, int32_t rank,
+                                       int32_t iterations, void* u_out, void* v_out, double* sigma_out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return build_impl(layout, tensor, num_orderings, x_conds, deltas, x_canon, num_tokens, col0, width, rank,
+                    iterations, u_out, v_out, sigma_out, workspace, workspace_bytes, stream);
 }
 
 const char* kamera_status_string(kamera_status s) {

@@ -17,6 +17,19 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ka
 FAKE = 0x10_0000_0000  # 256-byte aligned fake device address, never dereferenced
 
 
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001
+        return False
+
+
+# Every call below is meant to stop in host validation. On a machine with a GPU a
+# validation gap would send fake addresses to a real device, so the module does not run there.
+pytestmark = pytest.mark.skipif(_gpu_present(), reason="host-validation tests use fake device addresses")
+
+
 def header_functions():
     src = open(HEADER).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(kamera_\w+)\s*\(", src, re.M)))
@@ -164,13 +177,18 @@ def test_validation_errors(case, expect):
 
 
 def test_partial_page_sharing_is_not_an_overlap():
-    """Two chunks may share a page when their slots do not collide: validation passes and
-    the call proceeds to the HIP upload (which fails here only for want of a GPU)."""
+    """Two chunks may share a page when their slots do not collide: validation passes the
+    overlap check and stops at the (deliberately too small) workspace, before any upload
+    or launch, so the fake addresses are never touched on any machine."""
     pool = abi.make_pool(FAKE + 0x4000000, FAKE + 0x8000000, num_pages=8)
     a = chunk(num_tokens=10, block_table=np.array([2]), slot0=0, k_dst=None, v_dst=None)
     b = chunk(num_tokens=6, block_table=np.array([2]), slot0=10, k_dst=None, v_dst=None)
-    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, b], pool, WS, 0))
-    assert name in ("KAMERA_OK", "KAMERA_E_HIP"), msg
+    tiny = (WS[0], 1)
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, b], pool, tiny, 0))
+    assert name == "KAMERA_E_WORKSPACE", msg
+    c = chunk(num_tokens=6, block_table=np.array([2]), slot0=8, k_dst=None, v_dst=None)   # slots 8..13 collide
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, c], pool, tiny, 0))
+    assert name == "KAMERA_E_OVERLAP", msg
 
 
 def test_empty_batches_need_no_gpu():
@@ -250,3 +268,44 @@ def test_build_patch_mla_has_one_tensor():
     assert name == "KAMERA_E_SHAPE"
     name, _ = status_of(build_call(lay, tensor=0, col0=512, width=65))
     assert name == "KAMERA_E_SHAPE"
+
+
+def orbit_call(k=3, **kw):
+    lay = kw.pop("layout", None) or gqa_layout()
+    conds = kw.pop("conds", [FAKE + 0x100000 * (i + 1) for i in range(k)])
+    deltas = kw.pop("deltas", [2048 * i for i in range(len(conds))])
+    d = dict(tensor=0, x_canon=FAKE, num_tokens=64, col0=0, width=512, rank=32, iterations=16,
+             u_out=FAKE + 0x4000000, v_out=FAKE + 0x5000000, sigma_out=FAKE + 0x6000000)
+    d.update(kw)
+    ws = (FAKE + 0x10000000, abi.build_workspace_bytes(d["num_tokens"], d["width"], d["rank"]))
+    return lambda: abi.build_orbit_patch(lay, d.pop("tensor"), conds, deltas, workspace=ws, **d)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=0), "KAMERA_E_SHAPE"),
+    (dict(k=33), "KAMERA_E_SHAPE"),
+    (dict(conds=[FAKE, 0, FAKE + 0x200000]), "KAMERA_E_NULL"),
+    (dict(conds=[FAKE, FAKE + 1], deltas=[0, 1]), "KAMERA_E_ALIGN"),
+    (dict(deltas=[0, 1 << 31, 5]), "KAMERA_E_DELTA"),
+    (dict(rank=65), "KAMERA_E_RANK"),
+    (dict(x_canon=None), "KAMERA_E_NULL"),
+])
+def test_build_orbit_patch_validation(kw, expect):
+    name, msg = status_of(orbit_call(**kw))
+    assert name == expect, msg
+
+
+def test_in_place_patch_needs_v_pool_only_for_v_factors():
+    """In place, V is touched only by a V factor: a K-only patch needs no V pool."""
+    pool = abi.make_pool(FAKE + 0x4000000, None, num_pages=8)
+    tiny = (WS[0], 1)
+    kf = dict(u=FAKE + 0x400000, v=FAKE + 0x500000, tensor=0, width=512, rank=32)
+    vf = dict(u=FAKE + 0x600000, v=FAKE + 0x700000, tensor=1, width=512, rank=32)
+    k_only = chunk(num_tokens=20, flags=abi.PATCH | abi.IN_PLACE, block_table=np.array([1, 4]), slot0=0,
+                   k_src=None, v_src=None, k_dst=None, v_dst=None, factors=[kf])
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [k_only], pool, tiny, 0))
+    assert name == "KAMERA_E_WORKSPACE", msg
+    with_v = chunk(num_tokens=20, flags=abi.PATCH | abi.IN_PLACE, block_table=np.array([1, 4]), slot0=0,
+                   k_src=None, v_src=None, k_dst=None, v_dst=None, factors=[kf, vf])
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [with_v], pool, tiny, 0))
+    assert name == "KAMERA_E_NULL" and "v_pool" in msg, msg

@@ -23,9 +23,10 @@ import pytest
 import torch
 
 import oracle.kamera_oracle as O
-from oracle.builder_oracle import deficit, residual_energy, truncated_svd
+from oracle import tolerance as tol
+from oracle.builder_oracle import deficit, orbit_deficit, residual_energy, truncated_svd
 from tests.gpu_util import say
-from workloads.builder_inputs import BuilderCase
+from workloads.builder_inputs import BuilderCase, orbit_parts
 from workloads.configs import BF16, F32, GPTJ, GQA, MLA, NEOX, LayoutSpec
 
 pytestmark = pytest.mark.gpu
@@ -232,3 +233,132 @@ def test_full_rank_patch_reproduces_conditioned_rows():
         err = np.abs(g - want)
         say(f"  max |rehydrated - KV(B|A)| = {err.max():.3e}")
         assert err.max() <= 2e-5 * (1 + np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------------- orbit patch
+def stored_rows(lay: LayoutSpec, canon: np.ndarray, tensor: int, delta: int, col0: int, part: np.ndarray):
+    """Stored KV(B|A) of one ordering: round(R(delta) canonical + part on the patched columns)."""
+    x = O.upcast(canon, lay.dtype)
+    bands, d_rot = _geometry(lay)
+    y = O.rotate(x, delta, bands, d_rot, lay.rope_base, lay.pairing) if tensor == 0 else x.copy()
+    y[:, col0:col0 + part.shape[1]] += part
+    return O.round_to(y, lay.dtype)
+
+
+def run_orbit(case: BuilderCase, conds, deltas, rank: int, iterations: int):
+    from position_free_kv_amd import abi
+    lay = case.layout
+    T, W = case.num_tokens, case.width
+    tdt, fill = (torch.int16, 0x7FA5) if lay.dtype == BF16 else (torch.float32, float("nan"))
+    u = torch.full((T, rank), fill, dtype=tdt, device="cuda")
+    v = torch.full((W, rank), fill, dtype=tdt, device="cuda")
+    sig = torch.full((rank,), float("nan"), dtype=torch.float64, device="cuda")
+    ws = torch.empty(abi.build_workspace_bytes(T, W, rank), dtype=torch.uint8, device="cuda")
+    dconds = [_dev(c) for c in conds]
+    abi.build_orbit_patch(_abi_layout(lay), case.tensor, dconds, deltas, _dev(case.canonical()), T, case.col0, W,
+                          rank, iterations, u, v, sig, ws)
+    torch.cuda.synchronize()
+    un, vn = u.cpu().numpy(), v.cpu().numpy()
+    if lay.dtype == BF16:
+        un, vn = un.view(np.uint16), vn.view(np.uint16)
+    return un, vn, sig.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,K", [(F32, 6), (BF16, 6), (BF16, 24)])
+def test_orbit_patch_matches_lapack(dtype, K):
+    """Orbit patch (preprint §5, reorder): K orderings place the chunk at offsets
+    slot * 512; each ordering's conditioned rows carry a shared planted part plus a
+    per-ordering part that averages to zero. The GPU factors of the mean deficit are
+    checked against LAPACK on the oracle's orbit deficit (Eckart-Young, sigma), and sigma
+    against the planted spectrum within Weyl's bound."""
+    lay = gqa(dtype, 4, 128, base=1e4)
+    case = BuilderCase(lay, tensor=0, num_tokens=512, delta=0, col0=0, width=512, sigma0=6.0, ratio=0.85,
+                       planted_rank=48, seed=31)
+    rank = 32
+    say(f"[orbit] dtype={dtype} K={K}")
+    canon = case.canonical()
+    deltas = [512 * ((3 * k) % 4) + 7 * k for k in range(K)]
+    parts = orbit_parts(case, K, spread=0.05)
+    conds = [stored_rows(lay, canon, 0, d, 0, p) for d, p in zip(deltas, parts)]
+    u, v, sig = run_orbit(case, conds, deltas, rank, 16)
+    bands, d_rot = _geometry(lay)
+    D = orbit_deficit([O.upcast(c, dtype) for c in conds], O.upcast(canon, dtype), deltas, bands=bands,
+                      d_rot=d_rot, base=lay.rope_base, pairing=lay.pairing)
+    _, _, s = truncated_svd(D, rank)
+    opt = float(np.sum(s[rank:] ** 2))
+    U, V = O.upcast(u, dtype), O.upcast(v, dtype)
+    res = residual_energy(D, U, V.T)
+    uu = unit_roundoff(dtype) * (1 + 4 * unit_roundoff(dtype))
+    rnd = uu * (np.linalg.norm(U) * np.linalg.norm(V, 2) * (1 + uu) + np.linalg.norm(U, 2) * np.linalg.norm(V))
+    bound = np.sqrt(opt * (1 + 1e-6)) + rnd + 1e-10 * np.linalg.norm(D)
+    say(f"  res={res:.6e} opt={opt:.6e} excess={np.sqrt(res) - np.sqrt(opt):.3e} allowed={bound - np.sqrt(opt):.3e}")
+    assert res >= opt * (1 - 1e-9) - 1e-13 * np.linalg.norm(D) ** 2
+    assert np.sqrt(res) <= bound
+    assert np.all(np.abs(sig ** 2 - s[:rank] ** 2) <= 1e-4 * s[:rank] ** 2 + 1e-12 * s[0] ** 2), (sig[:4], s[:4])
+    weyl = np.linalg.norm(D - case.deficit(), 2)
+    assert np.all(np.abs(sig - case.sigma[:rank]) <= weyl + 1e-9), (sig[:4], case.sigma[:4], weyl)
+
+
+def test_orbit_of_one_is_the_single_patch():
+    """One ordering: kamera_build_orbit_patch and kamera_build_patch give the same bytes."""
+    case = BuilderCase(gqa(BF16, 2, 128), tensor=0, num_tokens=300, delta=4321, col0=0, width=256, sigma0=4.0,
+                       ratio=0.85, seed=32)
+    say("[orbit] K=1 vs single")
+    canon, cond, u1, v1, s1 = run_builder(case, 16, 8)
+    u2, v2, s2 = run_orbit(case, [cond], [case.delta], 16, 8)
+    assert np.array_equal(u1, u2) and np.array_equal(v1, v2) and np.array_equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------------- removal patch
+def test_removal_patch_in_place():
+    """Removal patch (preprint §5, sliding-window survival): a survivor keeps its conditioned
+    rows X in the pool; re-prefilled without the evicted chunk it would hold
+    Y = R(-E) X + D with D low-rank (rank 48 planted). The builder forms the rank-64 patch
+    of Y - R(-E) X from the stored rows, and the operator applies it in place
+    (IN_PLACE | PATCH): the pool then matches the oracle applying the same factors, and
+    lies within the truncation and rounding error of Y."""
+    from position_free_kv_amd import abi
+    P, H, hd, T, E, rank = 16, 4, 128, 200, 1500, 64
+    lay = LayoutSpec(GQA, BF16, 1, num_kv_heads=H, head_dim=hd, rope_base=1e6, page_size=P)
+    F = H * hd
+    case = BuilderCase(lay, tensor=0, num_tokens=T, delta=-E, col0=0, width=F, sigma0=3.0, ratio=0.9,
+                       planted_rank=48, seed=33)
+    say("[removal] rank-64 removal patch applied in place")
+    kept = case.canonical()                       # the survivor's stored (conditioned) rows
+    target = conditioned_rows(case, kept)         # round(R(-E) kept + D)
+    _, _, u, v, sig = run_builder(case, rank, 16, canon=kept, cond=target)
+    pages = np.random.default_rng(3).permutation(24).astype(np.int32)[: (T + P - 1) // P]
+    pool = torch.full((1, 24, P, F), 0x7FA5, dtype=torch.int16, device="cuda")
+    slots = np.arange(T)
+    flat = torch.from_numpy(pages[slots // P].astype(np.int64) * P + slots % P).cuda()
+    pool.view(-1, F)[flat] = torch.from_numpy(kept.view(np.int16)).cuda()
+    du, dv = _dev(u), _dev(v)
+    ch = abi.ChunkDesc(num_tokens=T, delta=-E, flags=abi.PATCH | abi.IN_PLACE, block_table=pages, slot0=0,
+                       factors=[dict(u=du, v=dv, tensor=0, col0=0, width=F, rank=rank)])
+    lay_abi = _abi_layout(lay)
+    ws = torch.empty(abi.batch_workspace_bytes([ch], P), dtype=torch.uint8, device="cuda")
+    abi.rehydrate(lay_abi, ch, abi.make_pool(pool, None, num_pages=24), ws)
+    torch.cuda.synchronize()
+    got = pool.view(-1, F)[flat].cpu().numpy().view(np.uint16)
+    # the operator against the oracle with the same (GPU-built) factors
+    bands, d_rot = _geometry(lay)
+    x = O.upcast(kept, BF16)
+    fac = [O.Factor(0, 0, O.upcast(u, BF16), O.upcast(v, BF16).T)]
+    kw = dict(tensor=0, delta=-E, rotate_this=True, bands=bands, d_rot=d_rot, base=lay.rope_base,
+              pairing=lay.pairing, factors=fac, patch=True)
+    y = O.rehydrate_tensor(x, family=GQA, **kw)
+    res = tol.check_bf16(got, y, O.round_to(y, BF16), O.abs_terms(x, **kw), rank + 4)
+    assert res["fail"] == 0, res
+    # the pool now holds (close to) the re-prefilled rows
+    err = O.upcast(got, BF16) - O.upcast(target, BF16)
+    D = oracle_deficit(case, kept, target)
+    _, _, s = truncated_svd(D, rank)
+    floor = np.sqrt(np.sum(s[rank:] ** 2))
+    say(f"  ||pool - target||_F = {np.linalg.norm(err):.4e}; Eckart-Young floor {floor:.4e}; "
+        f"||D||_F = {np.linalg.norm(D):.4e}")
+    # the pool is rounded to bf16 once more: allow one bf16 rounding of the result on top of the floor
+    assert np.linalg.norm(err) <= floor + 2.0 ** -8 * np.linalg.norm(O.upcast(target, BF16)) + 1e-6
+    # untouched slots keep their sentinel
+    mask = np.ones(24 * P, bool)
+    mask[flat.cpu().numpy()] = False
+    assert bool((pool.view(-1, F)[torch.from_numpy(np.nonzero(mask)[0]).cuda()] == 0x7FA5).all())

@@ -68,3 +68,17 @@ class BuilderCase:
         q1, _ = np.linalg.qr(rng.standard_normal((T, len(s))))
         q2, _ = np.linalg.qr(rng.standard_normal((W, len(s))))
         return (q1 * s[None, :]) @ q2.T
+
+
+_P_ORBIT = 103
+
+
+def orbit_parts(case: BuilderCase, num_orderings: int, spread: float) -> list:
+    """Per-ordering deficits for an orbit: the case's drawn deficit (the part every
+    ordering shares) plus a per-ordering Gaussian part of scale `spread`, centred so the
+    parts sum to zero over the orderings. Returns num_orderings fp64 [T][width] arrays."""
+    base = case.deficit()
+    rng = np.random.default_rng([case.seed, _P_ORBIT, case.tensor, num_orderings])
+    extra = spread * rng.standard_normal((num_orderings,) + base.shape)
+    extra -= extra.mean(axis=0, keepdims=True)
+    return [base + extra[k] for k in range(num_orderings)]
