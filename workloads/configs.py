@@ -201,8 +201,24 @@ def _gqa_factors(key, F, m, sigma, layer0=0):
 
 def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Optional[int] = None,
                   tokens: Optional[int] = None, rank: Optional[int] = None,
-                  patch: bool = True, max_tokens: Optional[int] = None) -> Workload:
-    """Build config `name` (C1..C5). Keyword overrides shrink it for fast tests."""
+                  patch: bool = True, max_tokens: Optional[int] = None,
+                  patch_layer0: Optional[int] = None) -> Workload:
+    """Build config `name` (C1..C5). Keyword overrides shrink it for fast tests;
+    patch_layer0 makes every factor start at that layer (e.g. L // 2: the deep-half
+    patches of the preprint's Table 2, layers below it carry no patch)."""
+    wl = _make_workload(name, num_layers=num_layers, num_chunks=num_chunks, tokens=tokens, rank=rank,
+                        patch=patch, max_tokens=max_tokens)
+    if patch_layer0 is not None:
+        if not 0 <= patch_layer0 < wl.layout.num_layers:
+            raise ValueError("patch_layer0 outside [0, L)")
+        for c in wl.chunks:
+            for f in c.factors:
+                f.layer0 = patch_layer0
+    return wl
+
+
+def _make_workload(name: str, *, num_layers: Optional[int], num_chunks: Optional[int], tokens: Optional[int],
+                   rank: Optional[int], patch: bool, max_tokens: Optional[int]) -> Workload:
     root = _ROOT[name]
     if name == "C1":
         lay = LayoutSpec(GQA, F32, num_layers or 1, num_kv_heads=2, head_dim=64, rope_base=10000.0)
