@@ -201,6 +201,18 @@ def test_mixed_dense_paged_and_in_place_batch():
     assert pool_untouched_ok(dw)
 
 
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_shared_basis_across_chunks(name):
+    """One per-layer V basis aliased by every chunk's factor of a slot (only U differs):
+    the kernel reads the same V rows for all chunks."""
+    say(f"[shared basis] {name}")
+    wl = make_workload(name, num_layers=2, num_chunks=3, tokens=140, shared_basis=True)
+    dw = run_dw(wl)
+    ptrs = {dw.factors[(f.key, f.slot)][1].data_ptr() for c in wl.chunks for f in c.factors}
+    assert len(ptrs) == len({f.slot for c in wl.chunks for f in c.factors})   # one V buffer per slot
+    assert_parity(dw)
+
+
 def test_in_place_with_patch_mla_and_gqa():
     """In place with a patch: re-conditioning a resident chunk (rotate + add)."""
     say("[in-place+patch]")

@@ -42,7 +42,7 @@ CONFIG_NAMES = ("C1", "C2", "C3", "C4", "C5")
 _ROOT = {"C1": 1001, "C2": 1002, "C3": 1003, "C4": 1004, "C5": 1005}
 
 # draw purposes (second entry of every seed key)
-_P_CANON, _P_OUTLIER, _P_DELTA, _P_LEN, _P_ROLE, _P_FACTOR, _P_TABLE, _P_POOL = range(1, 9)
+_P_CANON, _P_OUTLIER, _P_DELTA, _P_LEN, _P_ROLE, _P_FACTOR, _P_TABLE, _P_POOL, _P_BASIS = range(1, 10)
 
 BF16_SENTINEL = 0x7FA5  # a quiet-NaN bit pattern no real output produces
 F32_SENTINEL = 0x7FC0DEAD
@@ -91,6 +91,7 @@ class FactorSpec:
     key: int          # identifies the factor draw: default_rng([root, FACTOR, key, layer, slot])
     slot: int         # factor slot (0..3), part of the draw key
     layer0: int = 0   # first patched layer (layers below it carry no factor)
+    basis: int = -1   # >= 0: V is the shared per-layer basis default_rng([root, BASIS, basis, layer, slot])
 
 
 @dataclass
@@ -174,6 +175,8 @@ class Workload:
             q, r = np.linalg.qr(g)
             return q * np.sign(np.diag(r))[None, :]
         q1 = orth(T, f.rank)
+        if f.basis >= 0:   # a basis shared by every chunk whose factor names it
+            rng = np.random.default_rng([self.root, _P_BASIS, f.basis, layer, f.slot])
         q2 = orth(f.width, f.rank)
         return q1 * f.sigma[None, :], q2
 
@@ -202,10 +205,12 @@ def _gqa_factors(key, F, m, sigma, layer0=0):
 def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Optional[int] = None,
                   tokens: Optional[int] = None, rank: Optional[int] = None,
                   patch: bool = True, max_tokens: Optional[int] = None,
-                  patch_layer0: Optional[int] = None) -> Workload:
+                  patch_layer0: Optional[int] = None, shared_basis: bool = False) -> Workload:
     """Build config `name` (C1..C5). Keyword overrides shrink it for fast tests;
     patch_layer0 makes every factor start at that layer (e.g. L // 2: the deep-half
-    patches of the preprint's Table 2, layers below it carry no patch)."""
+    patches of the preprint's Table 2, layers below it carry no patch); shared_basis
+    gives every chunk the same per-layer V for a factor slot (the preprint's §4: the
+    deficit's directions are shared across items, only the coefficients U differ)."""
     wl = _make_workload(name, num_layers=num_layers, num_chunks=num_chunks, tokens=tokens, rank=rank,
                         patch=patch, max_tokens=max_tokens)
     if patch_layer0 is not None:
@@ -214,6 +219,10 @@ def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Op
         for c in wl.chunks:
             for f in c.factors:
                 f.layer0 = patch_layer0
+    if shared_basis:
+        for c in wl.chunks:
+            for f in c.factors:
+                f.basis = f.slot
     return wl
 
 

@@ -53,11 +53,19 @@ class DeviceWorkload:
             cid: [torch.empty((self.L, wl.canon_tokens[cid], self.F), dtype=self.tdtype, device=self.device)
                   for _ in range(nt)] for cid in canon_ids}
         self.factors: Dict[Tuple[int, int], Tuple[torch.Tensor, torch.Tensor]] = {}
+        bases: Dict[Tuple[int, int, int, int, int], torch.Tensor] = {}
         for key, (c, fi) in fac_keys.items():
             f = c.factors[fi]
             nl = self.L - f.layer0
-            self.factors[key] = (torch.empty((nl, c.num_tokens, f.rank), dtype=self.tdtype, device=self.device),
-                                 torch.empty((nl, f.width, f.rank), dtype=self.tdtype, device=self.device))
+            vshape = (nl, f.width, f.rank)
+            if f.basis >= 0:   # one V buffer per shared basis, aliased by every chunk that names it
+                bk = (f.basis, f.slot, f.layer0, f.width, f.rank)
+                if bk not in bases:
+                    bases[bk] = torch.empty(vshape, dtype=self.tdtype, device=self.device)
+                v = bases[bk]
+            else:
+                v = torch.empty(vshape, dtype=self.tdtype, device=self.device)
+            self.factors[key] = (torch.empty((nl, c.num_tokens, f.rank), dtype=self.tdtype, device=self.device), v)
         # dense destinations and pool, sentinel filled
         self.dense = [[_sentinel_fill(torch.empty((self.L, rows, self.F), dtype=self.tdtype, device=self.device),
                                       lay.dtype) for _ in range(nt)] for rows in wl.dense_rows]
@@ -206,6 +214,7 @@ class DeviceWorkload:
         written once, factors read once per chunk-layer (survivors move K only)."""
         es, F, L = self.es, self.F, self.L
         total = 0
+        seen_v = set()
         for c in self.wl.chunks:
             T = c.num_tokens
             if c.in_place and not c.patched:
@@ -215,5 +224,9 @@ class DeviceWorkload:
             total += L * self.lay.num_tensors * 2 * T * F * es
             if c.patched:
                 for f in c.factors:
-                    total += (L - f.layer0) * (T * f.rank + f.rank * f.width) * es
+                    total += (L - f.layer0) * T * f.rank * es
+                    vkey = (f.basis, f.slot, f.layer0, f.width, f.rank) if f.basis >= 0 else (id(c), id(f))
+                    if vkey not in seen_v:   # a shared basis is read once per layer
+                        seen_v.add(vkey)
+                        total += (L - f.layer0) * f.rank * f.width * es
         return total
