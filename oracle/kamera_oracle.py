@@ -132,6 +132,48 @@ def rotate(x: np.ndarray, delta: int, band_offsets: Sequence[int], d_rot: int, b
 
 
 # ----------------------------------------------------------------------------
+# Per-token re-anchoring (QV-PIC Eq. 2: model-native M-RoPE applied with request
+# positions; KAMERA §4: a uniform shift of (t, h, w) is the 1-D rotation R(delta))
+# ----------------------------------------------------------------------------
+def pair_sections(d_rot: int, sections: Sequence[int]) -> np.ndarray:
+    """Position component (0 = t, 1 = h, 2 = w) that drives each rotary pair i.
+
+    Sections are blocked: the first sections[0] pairs follow t, the next sections[1]
+    follow h, the rest follow w. All zero means a 1-D rotation (every pair follows
+    component 0)."""
+    n = d_rot // 2
+    sec = np.zeros(n, dtype=np.int64)
+    if any(sections):
+        if sum(sections) != n:
+            raise ValueError("sections must add up to d_rot / 2")
+        sec[sections[0]:sections[0] + sections[1]] = 1
+        sec[sections[0] + sections[1]:] = 2
+    return sec
+
+
+def token_phases(positions: np.ndarray, d_rot: int, base: float, sections: Sequence[int]):
+    """cos and sin of phi[t, i] = positions[t, sec(i)] * theta_i, fp64 ([T][d_rot/2])."""
+    pos = np.asarray(positions, dtype=np.int64).reshape(len(positions), -1)
+    comp = pos[:, pair_sections(d_rot, sections)].astype(np.float64)      # [T][pairs]
+    phi = comp * inv_freq(d_rot, base)[None, :]
+    return np.cos(phi), np.sin(phi)
+
+
+def rotate_positions(x: np.ndarray, positions: np.ndarray, sections: Sequence[int], band_offsets: Sequence[int],
+                     d_rot: int, base: float, pairing: int) -> np.ndarray:
+    """Every rotary band of token t rotated by its own position offsets (t, h, w)."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    c, s = token_phases(positions, d_rot, base, sections)
+    p, q = pair_columns(d_rot, pairing)
+    for o in band_offsets:
+        a = x[:, o + p]
+        b = x[:, o + q]
+        y[:, o + p] = a * c - b * s
+        y[:, o + q] = a * s + b * c
+    return y
+
+
+# ----------------------------------------------------------------------------
 # U_m V_m^T: the rank-m conditioning patch (KAMERA Eq. 1; App. A serve listing)
 # ----------------------------------------------------------------------------
 def add_patch(y: np.ndarray, u: np.ndarray, vt: np.ndarray, col0: int) -> np.ndarray:
@@ -167,13 +209,21 @@ class Factor:
 
 def rehydrate_tensor(x: np.ndarray, *, tensor: int, family: int, delta: int, rotate_this: bool,
                      bands: Sequence[int], d_rot: int, base: float, pairing: int,
-                     factors: Iterable[Factor] = (), patch: bool = True) -> np.ndarray:
+                     factors: Iterable[Factor] = (), patch: bool = True, positions=None,
+                     sections: Sequence[int] = (0, 0, 0)) -> np.ndarray:
     """Eq. 1 for one tensor of one chunk at one layer, fp64, before output rounding.
 
     x: rows of the stored tensor ([T][F], fp64). `rotate_this` says whether this
     tensor carries the rope band (K for GQA/MHA, the 576-row for MLA; never V).
+    With `positions` ([T][3] integer offsets), token t is rotated by its own offsets
+    (per-token re-anchoring) and delta is not used.
     """
-    y = rotate(x, delta, bands, d_rot, base, pairing) if rotate_this else np.array(x, dtype=np.float64)
+    if not rotate_this:
+        y = np.array(x, dtype=np.float64)
+    elif positions is not None:
+        y = rotate_positions(x, positions, sections, bands, d_rot, base, pairing)
+    else:
+        y = rotate(x, delta, bands, d_rot, base, pairing)
     if patch:
         for f in factors:
             if f.tensor == tensor:
@@ -183,7 +233,7 @@ def rehydrate_tensor(x: np.ndarray, *, tensor: int, family: int, delta: int, rot
 
 def abs_terms(x: np.ndarray, *, tensor: int, delta: int, rotate_this: bool, bands: Sequence[int],
               d_rot: int, base: float, pairing: int, factors: Iterable[Factor] = (),
-              patch: bool = True) -> np.ndarray:
+              patch: bool = True, positions=None, sections: Sequence[int] = (0, 0, 0)) -> np.ndarray:
     """S = sum of |terms| of every output element (fp64), for rounding-error bounds.
 
     Rotated pair: |a||c| + |b||s| and |a||s| + |b||c|; unrotated: |x|; plus
@@ -192,7 +242,10 @@ def abs_terms(x: np.ndarray, *, tensor: int, delta: int, rotate_this: bool, band
     ax = np.abs(np.asarray(x, dtype=np.float64))
     s_ = np.array(ax, copy=True)
     if rotate_this:
-        c, s = phases(delta, d_rot, base)
+        if positions is not None:
+            c, s = token_phases(positions, d_rot, base, sections)
+        else:
+            c, s = phases(delta, d_rot, base)
         c, s = np.abs(c), np.abs(s)
         p, q = pair_columns(d_rot, pairing)
         for o in bands:

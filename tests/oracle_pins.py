@@ -226,6 +226,33 @@ def pin_bf16_rounding(o):
 
 
 # --------------------------------------------------------------------- builder
+def pin_reanchor(o):
+    """Per-token re-anchoring (QV-PIC Eq. 2; KAMERA §4 for the uniform case).
+    (a) a uniform offset (d, d, d) on every token is R(d) for any sections, bit for bit;
+    (b) 1-D offsets p_t = p0 + t on unrotated keys equal a complex multiply by
+        exp(i p_t theta) per token (independent formula, NeoX halves);
+    (c) with blocked sections (16, 24, 24) of a 128-wide head, pair i follows t, h or w
+        by its index, using the band's global frequency theta_i: each section checked
+        against a complex multiply with its own component."""
+    rng = np.random.default_rng(41)
+    T, d, base = 24, 128, 1e6
+    x = rng.standard_normal((T, d))
+    for sec in [(0, 0, 0), (16, 24, 24), (32, 16, 16)]:
+        dl = 12345
+        y = o.rotate_positions(x, np.full((T, 3), dl), sec, [0], d, base, o.NEOX)
+        assert np.array_equal(y, o.rotate(x, dl, [0], d, base, o.NEOX)), sec
+    th = base ** (-2.0 * np.arange(d // 2) / d)
+    pos1 = 1000 + np.arange(T)
+    y = o.rotate_positions(x, np.stack([pos1, 0 * pos1, 0 * pos1], 1), (0, 0, 0), [0], d, base, o.NEOX)
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * pos1[:, None] * th[None, :])
+    assert np.max(np.abs(y - np.concatenate([z.real, z.imag], 1))) <= 1e-12
+    pos = np.stack([rng.integers(0, 4096, T), rng.integers(0, 64, T), rng.integers(0, 64, T)], 1)
+    y = o.rotate_positions(x, pos, (16, 24, 24), [0], d, base, o.NEOX)
+    comp = np.concatenate([np.zeros(16, int), np.ones(24, int), 2 * np.ones(24, int)])
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * pos[:, comp] * th[None, :])
+    assert np.max(np.abs(y - np.concatenate([z.real, z.imag], 1))) <= 1e-12
+
+
 def pin_builder_planted(b):
     """Planted spectrum Delta = Q1 diag(sigma) Q2^T with sigma_i = 0.3*0.9^i: the top-m
     singular values are the planted ones, and the Eckart-Young residual
@@ -292,4 +319,4 @@ def pin_orbit_mean(b):
 ORACLE_PINS = [pin_theta_geometric, pin_pairs_from_pages, pin_complex_multiply, pin_composition,
                pin_norm_and_inverse, pin_identity, pin_large_delta_phase, pin_patch_is_matmul,
                pin_full_rank_reconstructs, pin_survivor_rotation_only, pin_paging_bruteforce,
-               pin_bf16_rounding]
+               pin_bf16_rounding, pin_reanchor]

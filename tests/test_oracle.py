@@ -118,9 +118,34 @@ def _mut_mla_latent_band(m):
     m.band_offsets = lambda fam, h=0, d=0, lat=0: [0] if fam == m.MLA else orig(fam, h, d, lat)
 
 
+def _mut_sections_off_by_one(m):
+    orig = m.pair_sections
+    m.pair_sections = lambda d, sec: np.roll(orig(d, sec), 1)
+
+
+def _mut_sections_all_t(m):
+    m.pair_sections = lambda d, sec: np.zeros(d // 2, dtype=np.int64)
+
+
+def _mut_theta_within_section(m):
+    def token_phases(positions, d_rot, base, sections):
+        pos = np.asarray(positions, dtype=np.int64).reshape(len(positions), -1)
+        sec = m.pair_sections(d_rot, sections)
+        idx = np.arange(d_rot // 2) - np.array([0, sections[0], sections[0] + sections[1]])[sec]
+        phi = pos[:, sec] * (np.float64(base) ** (-2.0 * idx / d_rot))[None, :]
+        return np.cos(phi), np.sin(phi)
+    m.token_phases = token_phases
+
+
+def _mut_first_token_positions(m):
+    orig = m.token_phases
+    m.token_phases = lambda pos, d, b, sec: orig(np.repeat(np.asarray(pos)[:1], len(pos), 0), d, b, sec)
+
+
 MUTANTS = [_mut_sign, _mut_cos_sin_swapped, _mut_pairing, _mut_theta_half, _mut_theta_shift,
            _mut_theta_f32, _mut_patch_before_rotate, _mut_patch_rank_reversed, _mut_round_truncate,
-           _mut_round_double, _mut_page_no_slot0, _mut_v_rotated, _mut_mla_latent_band]
+           _mut_round_double, _mut_page_no_slot0, _mut_v_rotated, _mut_mla_latent_band,
+           _mut_sections_off_by_one, _mut_sections_all_t, _mut_theta_within_section, _mut_first_token_positions]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__[5:])
