@@ -210,6 +210,9 @@ def main() -> int:
                     help="patch only the deeper half of the layers (every factor starts at layer L // 2)")
     ap.add_argument("--shared-basis", action="store_true",
                     help="every chunk uses the same per-layer V for a factor slot (only U differs per chunk)")
+    ap.add_argument("--positions", action="store_true",
+                    help="re-anchor every rehydrated chunk token by token with (t, h, w) M-RoPE ids "
+                         "(64-token frames on an 8 x 8 grid at the chunk's start) instead of one delta")
     ap.add_argument("--builder", action="store_true",
                     help="time the patch builder (kamera_build_patch) on one chunk-layer of --config instead")
     ap.add_argument("--builder-iterations", type=int, default=16)
@@ -227,13 +230,14 @@ def main() -> int:
 
     from workloads import make_workload
     wl = make_workload(args.config, rank=args.rank)
-    if args.deep_half or args.shared_basis:
-        wl = make_workload(args.config, rank=args.rank, shared_basis=args.shared_basis,
+    variant = args.deep_half or args.shared_basis or args.positions
+    if variant:
+        wl = make_workload(args.config, rank=args.rank, shared_basis=args.shared_basis, positions=args.positions,
                            patch_layer0=wl.layout.num_layers // 2 if args.deep_half else None)
     # The CPU oracle leg forks worker processes, so it runs before this process
     # touches the GPU (forking a process whose HIP runtime threads are live can deadlock).
     cpu = None
-    if not args.no_cpu and not args.deep_half and not args.shared_basis and wl.layout.family == 0 and not any(c.in_place for c in wl.chunks):
+    if not args.no_cpu and not variant and wl.layout.family == 0 and not any(c.in_place for c in wl.chunks):
         t_cpu = time.perf_counter()
         cpu = cpu_baseline(args.config, wl, args.cpu_units)
         print(f"# cpu oracle leg done in {time.perf_counter() - t_cpu:.1f} s", file=sys.stderr, flush=True)
@@ -330,7 +334,8 @@ def main() -> int:
     tokens = wl.total_tokens
     alg_bytes = dw.algorithmic_bytes()
     achieved = alg_bytes / (kernel_us * 1e-6) / 1e9
-    traffic = measured_traffic(args.config)
+    # counters are taken on the plain workloads only
+    traffic = None if variant or args.rank is not None else measured_traffic(args.config)
 
     out = {
         "metric": METRIC,
@@ -347,7 +352,9 @@ def main() -> int:
         "data": "synthetic: seeded N(0,1) canonical KV, orthonormal factors with geometric spectra",
         "config": {"workload": WORKLOADS[args.config] + ("" if args.rank is None else f" (rank overridden: m={args.rank})")
                    + (" (deep-half patches: layers L/2..L-1 only)" if args.deep_half else "")
-                   + (" (one V basis per layer shared by all chunks)" if args.shared_basis else ""),
+                   + (" (one V basis per layer shared by all chunks)" if args.shared_basis else "")
+                   + (" (per-token (t, h, w) re-anchoring, M-RoPE sections %s)" % (wl.layout.mrope_section,)
+                      if args.positions else ""),
                    "name": args.config, "chunks": len(wl.chunks),
                    "tokens": tokens, "layers": wl.layout.num_layers, "row_width": wl.layout.row_width},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

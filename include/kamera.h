@@ -86,7 +86,9 @@ enum { KAMERA_NEOX = 0, KAMERA_GPTJ = 1 };
 /* chunk flags */
 enum {
   KAMERA_PATCH = 1u,     /* add the chunk's factors (else rotation only; V, c_KV copied as stored) */
-  KAMERA_IN_PLACE = 2u   /* read the rows from the destination itself and write them back       */
+  KAMERA_IN_PLACE = 2u,  /* read the rows from the destination itself and write them back       */
+  KAMERA_POSITIONS = 4u  /* rotate token t by its own offsets positions[t] (per-token re-anchoring,
+                            QV-PIC Eq. 2) instead of the chunk-wide delta                        */
 };
 
 enum { KAMERA_MAX_FACTORS = 4, KAMERA_MAX_RANK = 256 };
@@ -103,6 +105,10 @@ typedef struct kamera_layout {
   int32_t page_size;     /* tokens per pool page (>= 1); used by paged destinations       */
   int32_t reserved;      /* must be 0                                                     */
   double rope_base;      /* RoPE base (> 0, finite), e.g. 1e4 or 1e6                      */
+  int32_t mrope_section[3];  /* KAMERA_POSITIONS chunks: rotary pairs driven by the t, h and w
+                                offsets, blocked in that order (sum = d_rot / 2, e.g. 16, 24, 24
+                                for a 128-wide head); all 0: every pair follows t (1-D RoPE)    */
+  int32_t reserved2;     /* must be 0                                                     */
 } kamera_layout;
 
 /* One stored factor pair of a chunk (preprint App. A: U[:, :m]*S[:m] and V_m; the
@@ -133,6 +139,10 @@ typedef struct kamera_chunk {
   const int32_t* block_table;  /* HOST page ids; token t lives at slot s = slot0 + t, page
                                   block_table[s / page_size], offset s % page_size of the pool;
                                   NULL selects the dense destination                          */
+  const int32_t* positions;    /* KAMERA_POSITIONS: DEVICE [T][3] int32 offsets (t, h, w) of each
+                                  token, |offset| < 2^31; read when the batch is uploaded; pair i
+                                  of token t turns by positions[t][section(i)] * theta_i.
+                                  Ignored without the flag                                    */
   int32_t slot0;               /* 0 <= slot0 < page_size                                       */
   int32_t num_factors;         /* 0 .. KAMERA_MAX_FACTORS                                      */
   kamera_factor factors[KAMERA_MAX_FACTORS];
@@ -158,8 +168,14 @@ typedef struct kamera_plan {
 } kamera_plan;
 
 /* Bytes of device workspace needed for a batch of `num_chunks` chunks whose block
- * tables hold `total_block_table_entries` page ids in total. */
+ * tables hold `total_block_table_entries` page ids in total and none of which has
+ * KAMERA_POSITIONS (those also need a cos/sin table; use kamera_batch_workspace_bytes). */
 size_t kamera_workspace_bytes(int32_t num_chunks, int64_t total_block_table_entries);
+
+/* Bytes of device workspace needed for exactly this batch (block tables and the per-token
+ * cos/sin tables of KAMERA_POSITIONS chunks included); 0 if the arguments are invalid. */
+size_t kamera_batch_workspace_bytes(const kamera_layout* layout, const kamera_chunk* chunks,
+                                    int32_t num_chunks);
 
 /* Rotation-only relocation in place (preprint §5: sliding-window survivors need only
  * R(delta)): rotates the K rotary bands (GQA) or the k_rope band (MLA) of tokens

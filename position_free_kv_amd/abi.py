@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkamera.so")
 GQA, MLA = 0, 1
 F32, BF16 = 0, 1
 NEOX, GPTJ = 0, 1
-PATCH, IN_PLACE = 1, 2
+PATCH, IN_PLACE, POSITIONS = 1, 2, 4
 MAX_FACTORS = 4
 MAX_RANK = 256
 BUILD_MAX_RANK = 64
@@ -27,7 +27,8 @@ BUILD_MAX_ORBIT = 32
 STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAMERA_E_RANK",
           "KAMERA_E_DELTA", "KAMERA_E_PAGE", "KAMERA_E_OVERLAP", "KAMERA_E_ALIGN",
           "KAMERA_E_WORKSPACE", "KAMERA_E_UNSUPPORTED", "KAMERA_E_HIP"]
-EXPORTED = ["kamera_workspace_bytes", "kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
+EXPORTED = ["kamera_workspace_bytes", "kamera_batch_workspace_bytes", "kamera_relocate", "kamera_rehydrate",
+            "kamera_rehydrate_batched",
             "kamera_plan_upload", "kamera_plan_launch", "kamera_status_string", "kamera_last_error",
             "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch", "kamera_build_orbit_patch"]
 
@@ -36,7 +37,8 @@ class Layout(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int32), ("dtype", ctypes.c_int32), ("num_layers", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("latent_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("pairing", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double)]
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("mrope_section", ctypes.c_int32 * 3), ("reserved2", ctypes.c_int32)]
 
 
 class Factor(ctypes.Structure):
@@ -49,7 +51,8 @@ class Chunk(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("flags", ctypes.c_uint32), ("delta", ctypes.c_int64),
                 ("k_src", ctypes.c_void_p), ("v_src", ctypes.c_void_p), ("src_layer_stride", ctypes.c_int64),
                 ("k_dst", ctypes.c_void_p), ("v_dst", ctypes.c_void_p), ("dst_layer_stride", ctypes.c_int64),
-                ("block_table", ctypes.POINTER(ctypes.c_int32)), ("slot0", ctypes.c_int32),
+                ("block_table", ctypes.POINTER(ctypes.c_int32)), ("positions", ctypes.c_void_p),
+                ("slot0", ctypes.c_int32),
                 ("num_factors", ctypes.c_int32), ("factors", Factor * MAX_FACTORS)]
 
 
@@ -83,6 +86,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.kamera_workspace_bytes.argtypes = [i32, i64]
         L.kamera_workspace_bytes.restype = sz
+        L.kamera_batch_workspace_bytes.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), i32]
+        L.kamera_batch_workspace_bytes.restype = sz
         L.kamera_relocate.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Pool), ctypes.POINTER(ctypes.c_int32),
                                       i32, i32, i64, vp, sz, vp]
         L.kamera_rehydrate.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), ctypes.POINTER(Pool), vp, sz, vp]
@@ -142,9 +147,9 @@ def _stream(stream) -> Optional[int]:
 
 def make_layout(family: int, dtype: int, num_layers: int, *, num_kv_heads: int = 0, head_dim: int = 0,
                 latent_dim: int = 0, rope_dim: int = 0, pairing: int = NEOX, rope_base: float = 10000.0,
-                page_size: int = 16) -> Layout:
+                page_size: int = 16, mrope_section: Sequence[int] = (0, 0, 0)) -> Layout:
     return Layout(family, dtype, num_layers, num_kv_heads, head_dim, latent_dim, rope_dim, pairing, page_size, 0,
-                  float(rope_base))
+                  float(rope_base), (ctypes.c_int32 * 3)(*[int(v) for v in mrope_section]), 0)
 
 
 class ChunkDesc:
@@ -152,7 +157,7 @@ class ChunkDesc:
 
     def __init__(self, *, num_tokens: int, delta: int, flags: int, k_src=None, v_src=None, src_layer_stride: int = 0,
                  k_dst=None, v_dst=None, dst_layer_stride: int = 0, block_table=None, slot0: int = 0,
-                 factors: Sequence[dict] = ()):
+                 factors: Sequence[dict] = (), positions=None):
         c = Chunk()
         c.num_tokens, c.flags, c.delta = int(num_tokens), int(flags), int(delta)
         c.k_src, c.v_src, c.src_layer_stride = _ptr(k_src), _ptr(v_src), int(src_layer_stride)
@@ -161,6 +166,7 @@ class ChunkDesc:
         if block_table is not None:
             self._table = np.ascontiguousarray(block_table, dtype=np.int32)
             c.block_table = self._table.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        c.positions = _ptr(positions)  # device [T][3] int32 offsets (with the POSITIONS flag)
         c.slot0 = int(slot0)
         if len(factors) > MAX_FACTORS:
             raise ValueError(f"at most {MAX_FACTORS} factors per chunk")
@@ -187,14 +193,10 @@ def workspace_bytes(num_chunks: int, total_block_table_entries: int = 0) -> int:
     return int(lib().kamera_workspace_bytes(int(num_chunks), int(total_block_table_entries)))
 
 
-def batch_workspace_bytes(chunks: Sequence, page_size: int) -> int:
-    """Workspace needed by this batch (its chunks' block-table entries included)."""
-    pages = 0
-    for c in chunks:
-        cc = c.c if isinstance(c, ChunkDesc) else c
-        if bool(cc.block_table) and cc.num_tokens > 0:
-            pages += (cc.slot0 + cc.num_tokens + page_size - 1) // page_size
-    return workspace_bytes(len(chunks), pages)
+def batch_workspace_bytes(layout: Layout, chunks: Sequence) -> int:
+    """Workspace needed by exactly this batch (block tables and per-token cos/sin tables included)."""
+    arr, n = _chunk_array(chunks)
+    return int(lib().kamera_batch_workspace_bytes(ctypes.byref(layout), arr, n))
 
 
 def _ws(workspace):

@@ -21,6 +21,7 @@ constexpr int kMaxFactors = 4;
 // kMaxKSteps 32-wide k-steps of V operands in registers. Kernel variant
 // v = (slabs - 1) * 4 + log2(k-step capacity), capacity in {1, 2, 4, 8}.
 constexpr int kMaxKSteps = 8;
+constexpr int kVariantPositions = 8;   // added to the variant: batches with per-token offsets
 constexpr int kMfmaRangeTokens = 128;  // tokens per wave task (8 tiles)
 
 struct alignas(16) DevFactor {
@@ -49,6 +50,9 @@ struct alignas(16) DevChunk {
   int64_t dst_ls;       // elements between layers (destination / pool)
   int64_t delta;
   const int32_t* pages; // device copy of the block table (NULL: dense destination)
+  const int32_t* positions;  // per-token offsets [T][3] (KAMERA_POSITIONS), caller's device memory
+  const float* phase;   // per-token cos/sin table [T][d_rot/2][2] in the workspace (positions chunks)
+  int64_t phase0;       // first entry of this chunk in the batch's table space
   int64_t task0;        // first task id of this chunk
   int32_t T;
   uint32_t flags;
@@ -85,7 +89,8 @@ struct alignas(16) DevHeader {
   int32_t page_shift;   // log2(page_size) when it is a power of two, else -1
   int32_t xcd_window_log2;  // MFMA path: log2 of the workgroups an XCD takes in a row (0: plain order)
   int64_t layer_tasks;  // > 0: layer-major task order, this many tasks per layer (task0 within a layer)
-  int64_t pad2;
+  int32_t mrope[3];     // rotary pairs following the t, h, w offsets (all 0: every pair follows t)
+  int32_t pad2;
 };
 
 }  // namespace kamera

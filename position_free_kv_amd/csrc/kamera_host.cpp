@@ -21,6 +21,7 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                           hipStream_t stream);
 hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int64_t entries, hipStream_t stream);
 }  // namespace kamera
 
 using namespace kamera;
@@ -42,10 +43,16 @@ kamera_status fail(kamera_status st, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Workspace: header | chunk records | block tables | per-token cos/sin tables. The
+// first three are packed on the host and copied in; the tables are computed on the
+// device from the chunks' position offsets when the batch is uploaded.
 size_t ws_bytes(int64_t nchunks, int64_t pages) {
   return round_up(sizeof(DevHeader), kAlign) + round_up((size_t)nchunks * sizeof(DevChunk), kAlign) +
          round_up((size_t)pages * sizeof(int32_t), kAlign);
 }
+
+// cos/sin table bytes of one chunk with per-token offsets
+size_t phase_bytes(int64_t T, int d_rot) { return round_up((size_t)T * (d_rot / 2) * 2 * sizeof(float), kAlign); }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -119,6 +126,7 @@ kamera_status check_layout(const kamera_layout* L) {
   if (L->reserved != 0) return fail(KAMERA_E_SHAPE, "layout.reserved must be 0");
   if (!(L->rope_base > 0.0) || !std::isfinite(L->rope_base))
     return fail(KAMERA_E_SHAPE, "rope_base must be positive and finite");
+  if (L->reserved2 != 0) return fail(KAMERA_E_SHAPE, "layout.reserved2 must be 0");
   if (L->family == KAMERA_GQA) {
     if (L->num_kv_heads < 1) return fail(KAMERA_E_SHAPE, "num_kv_heads must be >= 1");
     if (L->head_dim < 2 || L->head_dim % 2 || L->head_dim > 512)
@@ -130,6 +138,11 @@ kamera_status check_layout(const kamera_layout* L) {
       return fail(KAMERA_E_SHAPE, "rope_dim must be even in [2, 512] (got %d)", L->rope_dim);
     if ((int64_t)L->latent_dim + L->rope_dim > (1 << 20)) return fail(KAMERA_E_SHAPE, "row too wide");
   }
+  const int s0 = L->mrope_section[0], s1 = L->mrope_section[1], s2 = L->mrope_section[2];
+  if (s0 < 0 || s1 < 0 || s2 < 0) return fail(KAMERA_E_SHAPE, "mrope_section entries must be >= 0");
+  const int npairs = (L->family == KAMERA_GQA ? L->head_dim : L->rope_dim) / 2;
+  if ((s0 || s1 || s2) && (int64_t)s0 + s1 + s2 != npairs)
+    return fail(KAMERA_E_SHAPE, "mrope_section must add up to d_rot / 2 = %d (got %d + %d + %d)", npairs, s0, s1, s2);
   return KAMERA_OK;
 }
 
@@ -140,7 +153,11 @@ int row_width(const kamera_layout* L) {
 struct Packed {
   std::vector<unsigned char>& blob;  // header | chunks | pages (thread-local, reused across calls)
   std::vector<int64_t>& page_off;    // per chunk: offset (entries) of its page table, -1 if dense
-  size_t bytes = 0;
+  std::vector<int64_t>& phase_off;   // per chunk: byte offset of its cos/sin table, -1 if none
+  size_t upload_bytes = 0;           // header | chunks | pages
+  size_t bytes = 0;                  // the whole workspace (tables included)
+  int64_t phase_entries = 0;         // table entries (token, pair) of the batch
+  bool positions = false;
   int64_t tasks = 0;
   int kernel = 0;   // 0 none, 1 mfma, 2 generic
   int variant = 0;
@@ -208,8 +225,13 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   for (int i = 0; i < n; ++i) {
     const kamera_chunk& c = chunks[i];
     if (c.num_tokens < 0) return fail(KAMERA_E_SHAPE, "chunk %d: num_tokens < 0", i);
-    if (c.flags & ~(uint32_t)(KAMERA_PATCH | KAMERA_IN_PLACE))
+    if (c.flags & ~(uint32_t)(KAMERA_PATCH | KAMERA_IN_PLACE | KAMERA_POSITIONS))
       return fail(KAMERA_E_UNSUPPORTED, "chunk %d: unknown flag bits 0x%x", i, c.flags);
+    if ((c.flags & KAMERA_POSITIONS) && c.num_tokens > 0) {
+      if (!c.positions) return fail(KAMERA_E_NULL, "chunk %d: KAMERA_POSITIONS without positions", i);
+      if (!aligned(c.positions, sizeof(int32_t)))
+        return fail(KAMERA_E_ALIGN, "chunk %d: positions must be 4-byte aligned", i);
+    }
     if (c.delta <= -(int64_t(1) << 31) || c.delta >= (int64_t(1) << 31))
       return fail(KAMERA_E_DELTA, "chunk %d: |delta| must be < 2^31", i);
     if (c.num_factors < 0 || c.num_factors > KAMERA_MAX_FACTORS)
@@ -317,13 +339,28 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
       }
     }
   }
-  // 128-wide groups keep at most 4 k-steps of V operands in registers
-  if (mfma && need_ksteps > (L->family == KAMERA_GQA && L->head_dim == 128 ? kMaxKSteps / 2 : kMaxKSteps))
-    mfma = false;
+  // 128-wide groups keep at most 4 k-steps of V operands in registers; with per-token
+  // offsets (a cos/sin set per tile in registers as well) 2 k-steps, 64-wide groups 4
+  bool any_positions = false;
+  for (int i = 0; i < n; ++i)
+    if ((chunks[i].flags & KAMERA_POSITIONS) && chunks[i].num_tokens > 0) any_positions = true;
+  const bool wide = L->family == KAMERA_GQA && L->head_dim == 128;
+  if (mfma && need_ksteps > (wide ? kMaxKSteps / 2 : kMaxKSteps)) mfma = false;
+  if (mfma && any_positions && need_ksteps > (wide ? 2 : 4)) mfma = false;
 
   // -------------------------------------------------------------- pack
-  out.bytes = ws_bytes(n, total_pages);
-  out.blob.assign(out.bytes, 0);
+  out.upload_bytes = ws_bytes(n, total_pages);
+  out.bytes = out.upload_bytes;
+  out.phase_off.assign((size_t)n, -1);
+  out.phase_entries = 0;
+  out.positions = false;
+  for (int i = 0; i < n; ++i)
+    if ((chunks[i].flags & KAMERA_POSITIONS) && chunks[i].num_tokens > 0) {
+      out.phase_off[(size_t)i] = (int64_t)out.bytes;
+      out.bytes += phase_bytes(chunks[i].num_tokens, d_rot);
+      out.positions = true;
+    }
+  out.blob.assign(out.upload_bytes, 0);
   DevHeader* hd = reinterpret_cast<DevHeader*>(out.blob.data());
   DevChunk* dc = reinterpret_cast<DevChunk*>(out.blob.data() + round_up(sizeof(DevHeader), kAlign));
   int32_t* pg = reinterpret_cast<int32_t*>(out.blob.data() + round_up(sizeof(DevHeader), kAlign) +
@@ -342,6 +379,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   hd->page_size = P;
   hd->page_shift = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
   hd->rope_base = L->rope_base;
+  for (int k = 0; k < 3; ++k) hd->mrope[k] = L->mrope_section[k];
   hd->group_cols = mfma ? (L->family == KAMERA_GQA ? L->head_dim : kSlab) : F;
   hd->rope_group = (mfma && L->family == KAMERA_MLA) ? L->latent_dim / kSlab : -1;
   // XCD window (measured on MI355X): rows of more than 8 column groups (e.g. 32 heads x
@@ -368,6 +406,11 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
     d.flags = c.flags;
     d.delta = c.delta;
     d.slot0 = c.slot0;
+    d.phase0 = out.phase_entries;
+    if (out.phase_off[(size_t)i] >= 0) {
+      d.positions = c.positions;
+      out.phase_entries += (int64_t)c.num_tokens * (d_rot / 2);
+    }
     if (c.num_tokens == 0) continue;
     const bool in_place = c.flags & KAMERA_IN_PLACE;
     const bool patch = c.flags & KAMERA_PATCH;
@@ -450,7 +493,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   if (mfma) {
     int cap_log2 = 0;
     while ((1 << cap_log2) < need_ksteps) ++cap_log2;
-    out.variant = (hd->group_cols / kSlab - 1) * 4 + cap_log2;
+    out.variant = (hd->group_cols / kSlab - 1) * 4 + cap_log2 + (out.positions ? kVariantPositions : 0);
   }
   return KAMERA_OK;
 }
@@ -459,7 +502,8 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
                           void* ws, size_t ws_size, void* stream, kamera_plan* plan) {
   thread_local std::vector<unsigned char> blob;
   thread_local std::vector<int64_t> page_off;
-  Packed pk{blob, page_off};
+  thread_local std::vector<int64_t> phase_off;
+  Packed pk{blob, page_off, phase_off};
   kamera_status st = pack_batch(L, chunks, n, pool, pk);
   if (st != KAMERA_OK) return st;
   if (!ws) return fail(KAMERA_E_WORKSPACE, "workspace is NULL");
@@ -473,9 +517,18 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
                       ? nullptr
                       : reinterpret_cast<const int32_t*>((char*)ws + pages_off +
                                                          (size_t)pk.page_off[(size_t)i] * sizeof(int32_t));
+  for (int i = 0; i < n; ++i)
+    dc[i].phase = pk.phase_off[(size_t)i] < 0 ? nullptr
+                                              : reinterpret_cast<const float*>((char*)ws + pk.phase_off[(size_t)i]);
   if (pk.tasks > 0) {
-    st = upload(pk.blob.data(), pk.bytes, ws, (hipStream_t)stream);
+    st = upload(pk.blob.data(), pk.upload_bytes, ws, (hipStream_t)stream);
     if (st != KAMERA_OK) return st;
+    if (pk.phase_entries > 0) {  // per-token cos/sin tables, computed once per upload
+      const DevHeader* hd = reinterpret_cast<const DevHeader*>(ws);
+      const DevChunk* dcd = reinterpret_cast<const DevChunk*>((const char*)ws + round_up(sizeof(DevHeader), kAlign));
+      const hipError_t e = launch_phase_table(hd, dcd, pk.phase_entries, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
+    }
   }
   std::memset(plan, 0, sizeof(*plan));
   plan->workspace = ws;
@@ -494,6 +547,22 @@ extern "C" {
 size_t kamera_workspace_bytes(int32_t num_chunks, int64_t total_block_table_entries) {
   if (num_chunks < 0 || total_block_table_entries < 0) return 0;
   return ws_bytes(num_chunks, total_block_table_entries);
+}
+
+size_t kamera_batch_workspace_bytes(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks) {
+  if (!layout || num_chunks < 0 || (num_chunks > 0 && !chunks) || layout->page_size < 1) return 0;
+  const int d_rot = layout->family == KAMERA_GQA ? layout->head_dim : layout->rope_dim;
+  const int P = layout->page_size;
+  int64_t pages = 0;
+  size_t tables = 0;
+  for (int i = 0; i < num_chunks; ++i) {
+    const kamera_chunk& c = chunks[i];
+    if (c.num_tokens < 0 || c.slot0 < 0) return 0;
+    if (c.num_tokens == 0) continue;
+    if (c.block_table) pages += (c.slot0 + (int64_t)c.num_tokens + P - 1) / P;
+    if (c.flags & KAMERA_POSITIONS) tables += phase_bytes(c.num_tokens, d_rot);
+  }
+  return ws_bytes(num_chunks, pages) + tables;
 }
 
 kamera_status kamera_plan_upload(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks,

@@ -151,7 +151,16 @@ struct Geo {
   static constexpr int LDS = 16 * RS;          // bytes per wave
 };
 
-template <int NSLAB, int NK>
+// Rotary pair (index into the band's d_rot/2 pairs) of coefficient slot j of a lane
+// in the MFMA layout; slots 2k and 2k+1 are always neighbouring pairs.
+__device__ __forceinline__ int lane_pair(int rot, int j, int lg) {
+  if (rot == ROT_NEOX_SLABS) return 32 * (j >> 3) + 8 * lg + (j & 7);   // slab-0 element j
+  if (rot == ROT_NEOX_RUNS) return 8 * lg + (j & 7);                    // run-0 element j
+  const int e2 = 2 * j, s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;     // GPT-J pair (2j, 2j+1)
+  return (64 * s + 32 * r + 8 * lg + e) >> 1;
+}
+
+template <int NSLAB, int NK, bool POS>
 __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& ch, int layer, int tensor,
                                           int colbase, int tok0, int ntiles, int rot, const int* kfac,
                                           const int* kstep, int lane, unsigned char* lds) {
@@ -166,20 +175,37 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   const uint16_t* src = (const uint16_t*)ch.src[tensor] + (int64_t)layer * ch.src_ls + colbase + 8 * lchunk;
   uint16_t* dst = (uint16_t*)ch.dst[tensor] + (int64_t)layer * ch.dst_ls + colbase + 8 * lchunk;
 
-  // ---- rotation coefficients for the pairs this lane holds (MFMA layout)
-  float cs[NSLAB * 8], sn[NSLAB * 8];
-  if (rot != ROT_NONE) {
+  // ---- rotation coefficients for the pairs this lane holds (MFMA layout): one
+  // set per chunk (delta), or, for chunks with per-token offsets, the set of this
+  // lane's token read from the batch's cos/sin table for every tile (the next
+  // tile's set is loaded with the next tile's rows).
+  // Where registers allow (one slab, or one k-step) the next tile's set is loaded
+  // with the next tile's rows; otherwise at the top of its own tile.
+  const bool tok_phase = POS && rot != ROT_NONE && (ch.flags & 4u) != 0;
+  constexpr bool kPrefetchPhase = NSLAB == 1 || NK <= 1;
+  float cs[NSLAB * 8], sn[NSLAB * 8], pcs[NSLAB * 8], psn[NSLAB * 8];
+  auto load_phase = [&](int tile, float (&c_)[NSLAB * 8], float (&s_)[NSLAB * 8]) {
+    if constexpr (POS) {
+      const int t = min(tok0 + tile * kTileTokens + c, T - 1);
+      const float* row = ch.phase + (int64_t)t * hd.d_rot;  // [d_rot/2] x (cos, sin)
+#pragma unroll
+      for (int k = 0; k < NSLAB * 4; ++k) {
+        const f32x4 v = *(const f32x4*)(row + 2 * lane_pair(rot, 2 * k, lg));
+        c_[2 * k] = v[0];
+        s_[2 * k] = v[1];
+        c_[2 * k + 1] = v[2];
+        s_[2 * k + 1] = v[3];
+      }
+    }
+  };
+  if (tok_phase) {
+    load_phase(0, cs, sn);
+  } else if (rot != ROT_NONE) {
     float cl = 1.f, sl = 0.f;
     if (lane < (hd.d_rot >> 1)) phase_fp64(hd.rope_base, hd.d_rot, ch.delta, lane, cl, sl);
 #pragma unroll
     for (int j = 0; j < NSLAB * 8; ++j) {
-      int p;
-      if (rot == ROT_NEOX_SLABS) p = 32 * (j >> 3) + 8 * lg + (j & 7);   // slab-0 element j
-      else if (rot == ROT_NEOX_RUNS) p = 8 * lg + (j & 7);               // run-0 element j
-      else {                                                              // GPT-J pair (2j, 2j+1)
-        const int e2 = 2 * j, s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;
-        p = (64 * s + 32 * r + 8 * lg + e) >> 1;
-      }
+      const int p = lane_pair(rot, j, lg);
       cs[j] = __shfl(cl, p, 64);
       sn[j] = __shfl(sl, p, 64);
     }
@@ -313,7 +339,11 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
 
   load_tile(0, cur, ucur);
   for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 1 < ntiles) load_tile(tile + 1, nxt, unxt);
+    if (tile + 1 < ntiles) {
+      load_tile(tile + 1, nxt, unxt);
+      if (kPrefetchPhase && tok_phase) load_phase(tile + 1, pcs, psn);
+    }
+    if (!kPrefetchPhase && tok_phase && tile > 0) load_phase(tile, cs, sn);
     const int tt = tok0 + tile * kTileTokens;
     u32x4 out[G::NI];
     if (!compute) {
@@ -409,18 +439,25 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
       for (int i = 0; i < G::NI; ++i) cur[i] = nxt[i];
 #pragma unroll
       for (int j = 0; j < NK; ++j) ucur[j] = unxt[j];
+      if (kPrefetchPhase && tok_phase) {
+#pragma unroll
+        for (int j = 0; j < NSLAB * 8; ++j) {
+          cs[j] = pcs[j];
+          sn[j] = psn[j];
+        }
+      }
     }
   }
 }
 
-template <int NSLAB, int NKMAX>
+template <int NSLAB, int NKMAX, bool POS>
 __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const DevChunk& ch, int layer,
                                               int tensor, int colbase, int tok0, int ntiles, int rot,
                                               const int* kfac, const int* kstep, int lane, unsigned char* lds) {
 #define KAMERA_NK_CASE(N)                                                                                   \
   case N:                                                                                                  \
     if constexpr (N <= NKMAX)                                                                              \
-      mfma_task<NSLAB, N>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds);       \
+      mfma_task<NSLAB, N, POS>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds);  \
     break;
   switch (nk) {
     KAMERA_NK_CASE(0)
@@ -437,7 +474,7 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 #undef KAMERA_NK_CASE
 }
 
-template <int NSLAB, int NKMAX>
+template <int NSLAB, int NKMAX, bool POS>
 __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHeader* __restrict__ hdr,
                                                                 const DevChunk* __restrict__ chunks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerBlock * Geo<NSLAB>::LDS];
@@ -472,7 +509,8 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
 
   int rot = ROT_NONE;
   const bool band = hd.family == 0 ? (tensor == 0) : (g == hd.rope_group);
-  if (band && ch.delta != 0) rot = hd.pairing == 1 ? ROT_GPTJ : (hd.d_rot == 128 ? ROT_NEOX_SLABS : ROT_NEOX_RUNS);
+  const bool turns = ch.delta != 0 || (POS && (ch.flags & 4u) != 0);
+  if (band && turns) rot = hd.pairing == 1 ? ROT_GPTJ : (hd.d_rot == 128 ? ROT_NEOX_SLABS : ROT_NEOX_RUNS);
 
   // 32-wide k-steps of the factors covering this group's columns
   int kfac[kMaxKSteps], kstep[kMaxKSteps];
@@ -490,7 +528,7 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
     }
   }
   if ((ch.flags & 2u) && rot == ROT_NONE && nk == 0) return;  // in place and nothing changes
-  mfma_dispatch<NSLAB, NKMAX>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
+  mfma_dispatch<NSLAB, NKMAX, POS>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
                               lds_all + wave * Geo<NSLAB>::LDS);
 }
 
@@ -536,9 +574,10 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
   const int tensor = ch.stream_tensor[tcd.stream];
   const bool in_place = (ch.flags & 2u) != 0;
   const bool patch = (ch.flags & 1u) != 0;
-  const bool rotate = tensor == 0 && ch.delta != 0;
+  const bool tok_phase = tensor == 0 && (ch.flags & 4u) != 0;  // per-token offsets: cos/sin table
+  const bool rotate = tensor == 0 && (ch.delta != 0 || tok_phase);
   const int npairs = hd.d_rot >> 1;
-  if (rotate)
+  if (rotate && !tok_phase)
     for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
       float c, s;
       phase_fp64(hd.rope_base, hd.d_rot, ch.delta, p, c, s);
@@ -598,7 +637,7 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
       }
       float a = ld<T>(src, so + cp), bb = ld<T>(src, so + cq);
       if (rotate) {
-        const float2 cs = tab[i];
+        const float2 cs = tok_phase ? ((const float2*)ch.phase)[(int64_t)t * npairs + i] : tab[i];
         const float na = fmaf(a, cs.x, -(bb * cs.y));
         const float nb = fmaf(a, cs.y, bb * cs.x);
         a = na;
@@ -612,6 +651,38 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
       st<T>(dst, dof + cq, bb);
     }
   }
+}
+
+// ============================================================================
+// Per-token cos/sin table of chunks with position offsets (QV-PIC Eq. 2: M-RoPE
+// applied with each token's own (t, h, w) position). Entry (t, i) of a chunk's
+// table holds cos/sin of positions[t][section(i)] * theta_i, the angle formed and
+// evaluated in fp64 like the per-chunk phase, rounded once to fp32. Pairs are
+// assigned to the t, h, w components in blocks of mrope[0], mrope[1], mrope[2]
+// pairs; all zero means every pair follows component t (1-D RoPE).
+// ============================================================================
+__global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __restrict__ hdr,
+                                                             const DevChunk* __restrict__ chunks, int64_t entries) {
+  const int64_t e = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  if (e >= entries) return;
+  const DevHeader& hd = *hdr;
+  // the last chunk whose table starts at or before entry e owns it (chunks without
+  // a table take no entries, so a later chunk with the same start is the owner)
+  int lo = 0, hi = hd.nchunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunks[mid].phase0 <= e) lo = mid; else hi = mid - 1;
+  }
+  const DevChunk& ch = chunks[lo];
+  const int np = hd.d_rot >> 1;
+  const int64_t r = e - ch.phase0;
+  const int64_t t = r / np;
+  const int i = (int)(r - t * np);
+  int comp = 0;
+  if (hd.mrope[0] | hd.mrope[1] | hd.mrope[2]) comp = i < hd.mrope[0] ? 0 : (i < hd.mrope[0] + hd.mrope[1] ? 1 : 2);
+  float c, s;
+  phase_fp64(hd.rope_base, hd.d_rot, (int64_t)ch.positions[t * 3 + comp], i, c, s);
+  ((float2*)ch.phase)[t * np + i] = make_float2(c, s);
 }
 
 // ============================================================================
@@ -635,9 +706,17 @@ hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t 
   return hipGetLastError();
 }
 
-template <int NSLAB, int NKMAX>
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int64_t entries, hipStream_t stream) {
+  if (entries <= 0) return hipSuccess;
+  const int64_t blocks = (entries + kBlockThreads - 1) / kBlockThreads;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(phase_table, dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream, hdr, chunks, entries);
+  return hipGetLastError();
+}
+
+template <int NSLAB, int NKMAX, bool POS = false>
 static void launch_one(dim3 grid, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
-  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX>), grid, dim3(kMfmaBlockThreads), 0, stream, hdr, chunks);
+  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), grid, dim3(kMfmaBlockThreads), 0, stream, hdr, chunks);
 }
 
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
@@ -654,6 +733,12 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
     case 4: launch_one<2, 1>(grid, stream, hdr, chunks); break;
     case 5: launch_one<2, 2>(grid, stream, hdr, chunks); break;
     case 6: launch_one<2, 4>(grid, stream, hdr, chunks); break;
+    // batches with per-token offsets (kVariantPositions + the variant above)
+    case 8: launch_one<1, 1, true>(grid, stream, hdr, chunks); break;
+    case 9: launch_one<1, 2, true>(grid, stream, hdr, chunks); break;
+    case 10: launch_one<1, 4, true>(grid, stream, hdr, chunks); break;
+    case 12: launch_one<2, 1, true>(grid, stream, hdr, chunks); break;
+    case 13: launch_one<2, 2, true>(grid, stream, hdr, chunks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -57,8 +57,12 @@ def expect_block(wl: Workload, ch: ChunkSpec, layer: int, tensor: int,
     bands = O.band_offsets(lay.family, lay.num_kv_heads, lay.head_dim, lay.latent_dim)
     d_rot = O.rotary_width(lay.family, lay.head_dim, lay.rope_dim)
     rotate_this = tensor == 0          # K for GQA/MHA, the whole row for MLA
+    pos = None
+    if ch.positions is not None:
+        pos = ch.positions if rows is None else ch.positions[np.asarray(rows)]
     kw = dict(tensor=tensor, delta=ch.delta, rotate_this=rotate_this, bands=bands, d_rot=d_rot,
-              base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched)
+              base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched, positions=pos,
+              sections=lay.mrope_section)
     y = O.rehydrate_tensor(x, family=lay.family, **kw)
     S = O.abs_terms(x, **kw)
     m_total = sum(f.u.shape[1] for f in facs if f.tensor == tensor) if ch.patched else 0

@@ -46,9 +46,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     # natural C layout on x86_64 (checked against the header's field order)
-    assert ctypes.sizeof(abi.Layout) == 48
+    assert ctypes.sizeof(abi.Layout) == 64
     assert ctypes.sizeof(abi.Factor) == 40
-    assert ctypes.sizeof(abi.Chunk) == 80 + 4 * 40
+    assert ctypes.sizeof(abi.Chunk) == 88 + 4 * 40
     assert ctypes.sizeof(abi.Pool) == 32
     assert ctypes.sizeof(abi.Plan) == 64
 
@@ -116,6 +116,12 @@ def status_of(fn):
     ("workspace_small", "KAMERA_E_WORKSPACE"),
     ("workspace_null", "KAMERA_E_WORKSPACE"),
     ("too_many_factors", "KAMERA_E_SHAPE"),
+    ("positions_null", "KAMERA_E_NULL"),
+    ("positions_misaligned", "KAMERA_E_ALIGN"),
+    ("mrope_sum", "KAMERA_E_SHAPE"),
+    ("mrope_negative", "KAMERA_E_SHAPE"),
+    ("reserved2", "KAMERA_E_SHAPE"),
+    ("positions_table_not_in_workspace", "KAMERA_E_WORKSPACE"),
 ])
 def test_validation_errors(case, expect):
     lay = gqa_layout()
@@ -172,8 +178,35 @@ def test_validation_errors(case, expect):
         c = chunk()
         c.c.num_factors = 5
         f = lambda: run(cs=[c])
+    elif case == "positions_null":
+        f = lambda: run(cs=[chunk(flags=abi.PATCH | abi.POSITIONS)])
+    elif case == "positions_misaligned":
+        f = lambda: run(cs=[chunk(flags=abi.POSITIONS, positions=FAKE + 2)])
+    elif case == "mrope_sum":
+        f = lambda: run(L=gqa_layout(mrope_section=(16, 24, 23)))
+    elif case == "mrope_negative":
+        f = lambda: run(L=gqa_layout(mrope_section=(-8, 36, 36)))
+    elif case == "reserved2":
+        L2 = gqa_layout()
+        L2.reserved2 = 1
+        f = lambda: run(L=L2)
+    elif case == "positions_table_not_in_workspace":
+        # sized for the packed descriptors alone: the per-token cos/sin table does not fit
+        c = chunk(flags=abi.POSITIONS, positions=FAKE + 0x900000)
+        f = lambda: run(cs=[c], ws=(WS[0], abi.workspace_bytes(1, 0)))
     name, msg = status_of(f)
     assert name == expect, (case, name, msg)
+
+
+def test_batch_workspace_bytes_counts_tables():
+    """Per-token cos/sin tables: [T][d_rot/2] (cos, sin) fp32 per re-anchored chunk, 256-byte rounded."""
+    lay = gqa_layout(mrope_section=(16, 24, 24))
+    plain = abi.batch_workspace_bytes(lay, [chunk(), chunk(num_tokens=100)])
+    assert plain == abi.workspace_bytes(2, 0)
+    withpos = abi.batch_workspace_bytes(lay, [chunk(), chunk(num_tokens=100, flags=abi.POSITIONS, positions=FAKE)])
+    assert withpos - plain == -(-100 * 64 * 8 // 256) * 256
+    paged = abi.batch_workspace_bytes(lay, [chunk(num_tokens=40, slot0=3, block_table=np.array([1, 2, 3]))])
+    assert paged == abi.workspace_bytes(1, 3)
 
 
 def test_partial_page_sharing_is_not_an_overlap():

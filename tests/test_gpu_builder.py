@@ -336,7 +336,7 @@ def test_removal_patch_in_place():
     ch = abi.ChunkDesc(num_tokens=T, delta=-E, flags=abi.PATCH | abi.IN_PLACE, block_table=pages, slot0=0,
                        factors=[dict(u=du, v=dv, tensor=0, col0=0, width=F, rank=rank)])
     lay_abi = _abi_layout(lay)
-    ws = torch.empty(abi.batch_workspace_bytes([ch], P), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(abi.batch_workspace_bytes(lay_abi, [ch]), dtype=torch.uint8, device="cuda")
     abi.rehydrate(lay_abi, ch, abi.make_pool(pool, None, num_pages=24), ws)
     torch.cuda.synchronize()
     got = pool.view(-1, F)[flat].cpu().numpy().view(np.uint16)

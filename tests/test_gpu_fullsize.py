@@ -64,6 +64,19 @@ def test_fullsize_dense(name, blocks, rows):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_fullsize_positions(name):
+    """Per-token (t, h, w) re-anchoring of every chunk at full size (three-section M-RoPE ids
+    of 64-token frames at the chunk's start)."""
+    dw = _stage(name, positions=True)
+    dw.run()
+    torch.cuda.synchronize()
+    _sampled_parity(dw, 16, 32, seed=100 + int(name[1:]))
+    assert _run_twice_identical(dw, lambda: [t for buf in dw.dense for t in buf])
+    del dw
+    torch.cuda.empty_cache()
+
+
 def test_fullsize_mla_patch_off_bytes():
     """C3 with the patch off: c_KV columns of every output row equal the stored ones."""
     dw = _stage("C3", patch=False)

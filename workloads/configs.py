@@ -36,7 +36,7 @@ import numpy as np
 GQA, MLA = 0, 1
 F32, BF16 = 0, 1
 NEOX, GPTJ = 0, 1
-PATCH, IN_PLACE = 1, 2
+PATCH, IN_PLACE, POSITIONS = 1, 2, 4
 
 CONFIG_NAMES = ("C1", "C2", "C3", "C4", "C5")
 _ROOT = {"C1": 1001, "C2": 1002, "C3": 1003, "C4": 1004, "C5": 1005}
@@ -60,6 +60,11 @@ class LayoutSpec:
     pairing: int = NEOX
     rope_base: float = 10000.0
     page_size: int = 16
+    mrope_section: tuple = (0, 0, 0)   # rotary pairs following the t, h, w offsets (all 0: 1-D)
+
+    @property
+    def d_rot(self) -> int:
+        return self.head_dim if self.family == GQA else self.rope_dim
 
     @property
     def row_width(self) -> int:
@@ -108,6 +113,7 @@ class ChunkSpec:
     block_table: Optional[np.ndarray] = None
     slot0: int = 0
     role: str = "rehydrate"          # "rehydrate" | "survivor"
+    positions: Optional[np.ndarray] = None   # [T][3] int32 (t, h, w) offsets, with the POSITIONS flag
 
     @property
     def patched(self) -> bool:
@@ -202,17 +208,53 @@ def _gqa_factors(key, F, m, sigma, layer0=0):
             FactorSpec(tensor=1, col0=0, width=F, rank=m, sigma=sigma, key=key, slot=1, layer0=layer0)]
 
 
+FRAME_TOKENS, FRAME_GRID = 64, 8   # a video frame / screenshot tile: 8 x 8 merged patches
+
+
+def grid_positions(num_tokens: int, start: int, frame_tokens: int = FRAME_TOKENS,
+                   grid_w: int = FRAME_GRID) -> np.ndarray:
+    """(t, h, w) position ids of a run of visual tokens placed at `start`: token k is
+    patch (k % frame_tokens) of frame k // frame_tokens, in row-major order on a grid
+    grid_w wide; each component is offset by `start` (three-section M-RoPE ids of
+    Qwen2-VL-style backbones). [T][3] int32."""
+    k = np.arange(num_tokens, dtype=np.int64)
+    patch_ = k % frame_tokens
+    pos = np.stack([k // frame_tokens, patch_ // grid_w, patch_ % grid_w], axis=1) + int(start)
+    return pos.astype(np.int32)
+
+
+def mrope_sections(d_rot: int) -> tuple:
+    """Blocked t/h/w split of the d_rot/2 rotary pairs in the 1 : 1.5 : 1.5 proportion of
+    Qwen2-VL's (16, 24, 24) for 128-wide heads."""
+    n = d_rot // 2
+    t = n // 4
+    h = (n - t) // 2
+    return (t, h, n - t - h)
+
+
 def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Optional[int] = None,
                   tokens: Optional[int] = None, rank: Optional[int] = None,
                   patch: bool = True, max_tokens: Optional[int] = None,
-                  patch_layer0: Optional[int] = None, shared_basis: bool = False) -> Workload:
+                  patch_layer0: Optional[int] = None, shared_basis: bool = False,
+                  positions: bool = False) -> Workload:
     """Build config `name` (C1..C5). Keyword overrides shrink it for fast tests;
     patch_layer0 makes every factor start at that layer (e.g. L // 2: the deep-half
     patches of the preprint's Table 2, layers below it carry no patch); shared_basis
     gives every chunk the same per-layer V for a factor slot (the preprint's §4: the
-    deficit's directions are shared across items, only the coefficients U differ)."""
+    deficit's directions are shared across items, only the coefficients U differ);
+    positions re-anchors every rehydrated chunk token by token with three-section
+    (t, h, w) ids of 64-token frames placed at the chunk's start (QV-PIC Eq. 2: keys
+    stored unrotated, M-RoPE applied with the request positions); survivors keep delta."""
     wl = _make_workload(name, num_layers=num_layers, num_chunks=num_chunks, tokens=tokens, rank=rank,
                         patch=patch, max_tokens=max_tokens)
+    if positions:
+        import dataclasses
+        wl.layout = dataclasses.replace(wl.layout, mrope_section=mrope_sections(wl.layout.d_rot))
+        for c in wl.chunks:
+            if not c.in_place:
+                c.positions = grid_positions(c.num_tokens, c.delta)
+                c.flags |= POSITIONS
+        wl.description += "; per-token (t, h, w) re-anchoring"
     if patch_layer0 is not None:
         if not 0 <= patch_layer0 < wl.layout.num_layers:
             raise ValueError("patch_layer0 outside [0, L)")

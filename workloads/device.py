@@ -90,14 +90,18 @@ class DeviceWorkload:
         self._stage(jobs, fac_keys)
         torch.cuda.synchronize(self.device)
 
+        # per-token (t, h, w) offsets of re-anchored chunks, [T][3] int32 on the device
+        self.positions = {c.index: torch.from_numpy(np.ascontiguousarray(c.positions, dtype=np.int32)).to(self.device)
+                          for c in wl.chunks if c.positions is not None}
         self.descs = [self._desc(c) for c in wl.chunks]
         self.pool_desc = None
         if self.pool is not None:
             self.pool_desc = abi.make_pool(self.pool[0], self.pool[1] if nt == 2 else None, wl.num_pages)
         self.layout = abi.make_layout(lay.family, lay.dtype, self.L, num_kv_heads=lay.num_kv_heads,
                                       head_dim=lay.head_dim, latent_dim=lay.latent_dim, rope_dim=lay.rope_dim,
-                                      pairing=lay.pairing, rope_base=lay.rope_base, page_size=self.P)
-        self.ws_bytes = abi.batch_workspace_bytes(self.descs, self.P)
+                                      pairing=lay.pairing, rope_base=lay.rope_base, page_size=self.P,
+                                      mrope_section=lay.mrope_section)
+        self.ws_bytes = abi.batch_workspace_bytes(self.layout, self.descs)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
     # ------------------------------------------------------------------ staging
@@ -146,7 +150,8 @@ class DeviceWorkload:
 
     def _desc(self, c: ChunkSpec) -> abi.ChunkDesc:
         nt = self.lay.num_tensors
-        kw = dict(num_tokens=c.num_tokens, delta=c.delta, flags=c.flags, slot0=c.slot0)
+        kw = dict(num_tokens=c.num_tokens, delta=c.delta, flags=c.flags, slot0=c.slot0,
+                  positions=self.positions.get(c.index))
         if c.block_table is not None:
             kw["block_table"] = c.block_table
         elif c.dst_buffer >= 0:
@@ -174,7 +179,7 @@ class DeviceWorkload:
         for c in self.wl.chunks:
             d = self._desc(c)
             d.c.delta = 0
-            d.c.flags = d.c.flags & ~abi.PATCH
+            d.c.flags = d.c.flags & ~(abi.PATCH | abi.POSITIONS)
             d.c.num_factors = 0
             out.append(d)
         return out
@@ -222,6 +227,8 @@ class DeviceWorkload:
                 total += L * 2 * T * cols * es
                 continue
             total += L * self.lay.num_tensors * 2 * T * F * es
+            if c.positions is not None:   # the (t, h, w) offsets, read once per chunk
+                total += T * 3 * 4
             if c.patched:
                 for f in c.factors:
                     total += (L - f.layer0) * T * f.rank * es
