@@ -51,8 +51,12 @@ size_t ws_bytes(int64_t nchunks, int64_t pages) {
          round_up((size_t)pages * sizeof(int32_t), kAlign);
 }
 
-// cos/sin table bytes of one chunk with per-token offsets
-size_t phase_bytes(int64_t T, int d_rot) { return round_up((size_t)T * (d_rot / 2) * 2 * sizeof(float), kAlign); }
+// cos/sin table of one chunk with per-token offsets: (cos, sin) fp32 of every rotary
+// pair of every token, the token count padded to whole 16-token tiles
+int64_t phase_tokens(int64_t T) { return (T + kTileTokens - 1) / kTileTokens * kTileTokens; }
+size_t phase_bytes(int64_t T, int d_rot) {
+  return round_up((size_t)phase_tokens(T) * (d_rot / 2) * 2 * sizeof(float), kAlign);
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -156,7 +160,7 @@ struct Packed {
   std::vector<int64_t>& phase_off;   // per chunk: byte offset of its cos/sin table, -1 if none
   size_t upload_bytes = 0;           // header | chunks | pages
   size_t bytes = 0;                  // the whole workspace (tables included)
-  int64_t phase_entries = 0;         // table entries (token, pair) of the batch
+  int64_t phase_entries = 0;         // table entries (padded token, pair) of the batch
   bool positions = false;
   int64_t tasks = 0;
   int kernel = 0;   // 0 none, 1 mfma, 2 generic
@@ -409,7 +413,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
     d.phase0 = out.phase_entries;
     if (out.phase_off[(size_t)i] >= 0) {
       d.positions = c.positions;
-      out.phase_entries += (int64_t)c.num_tokens * (d_rot / 2);
+      out.phase_entries += phase_tokens(c.num_tokens) * (d_rot / 2);
     }
     if (c.num_tokens == 0) continue;
     const bool in_place = c.flags & KAMERA_IN_PLACE;

@@ -69,6 +69,44 @@ __device__ __forceinline__ void phase_fp64(double base, int d_rot, int64_t delta
   s = (float)sd;
 }
 
+// Rotary pair (index into the band's d_rot/2 pairs) of coefficient slot j of a lane
+// (lg = lane >> 4) in the MFMA layout; slots 2k and 2k+1 are always neighbouring pairs.
+__device__ __forceinline__ int lane_pair(int rot, int j, int lg) {
+  if (rot == ROT_NEOX_SLABS) return 32 * (j >> 3) + 8 * lg + (j & 7);   // slab-0 element j
+  if (rot == ROT_NEOX_RUNS) return 8 * lg + (j & 7);                    // run-0 element j
+  const int e2 = 2 * j, s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;     // GPT-J pair (2j, 2j+1)
+  return (64 * s + 32 * r + 8 * lg + e) >> 1;
+}
+
+// Rotation mode of a layout's rotary band in the MFMA path.
+__device__ __forceinline__ int band_rot(const DevHeader& hd) {
+  return hd.pairing == 1 ? ROT_GPTJ : (hd.d_rot == 128 ? ROT_NEOX_SLABS : ROT_NEOX_RUNS);
+}
+
+// Float offset of (cos, sin) of pair i of token t in a chunk's per-token table.
+// Bands of 64 or 128 columns (every MFMA layout) store the table tile-major in the
+// MFMA lane order: tile t/16 is a block of 16 * d_rot floats holding, for each
+// coefficient step k (two neighbouring pairs, lane_pair(2k)) and lane group lg, the
+// 16 tokens' (cos, sin, cos, sin) as 16 bytes each, so the wave instruction that
+// loads step k of a tile reads 1 KB of consecutive bytes. Other widths (generic
+// kernel only) store [token][pair].
+__device__ __forceinline__ int64_t phase_offset(const DevHeader& hd, int64_t t, int i) {
+  if (hd.d_rot != 64 && hd.d_rot != 128) return (t * (hd.d_rot >> 1) + i) * 2;
+  int k, lg;
+  const int rot = band_rot(hd);
+  if (rot == ROT_NEOX_SLABS) {        // i = 32 (k >> 2) + 8 lg + 2 (k & 3) + half
+    lg = (i >> 3) & 3;
+    k = 4 * (i >> 5) + ((i & 7) >> 1);
+  } else if (rot == ROT_NEOX_RUNS) {  // i = 8 lg + 2 k + half
+    lg = i >> 3;
+    k = (i & 7) >> 1;
+  } else {                            // i = 32 (k >> 2) + 16 ((k >> 1) & 1) + 4 lg + 2 (k & 1) + half
+    lg = (i >> 2) & 3;
+    k = 4 * (i >> 5) + 2 * ((i >> 4) & 1) + ((i >> 1) & 1);
+  }
+  return (t >> 4) * 16 * hd.d_rot + ((k * 4 + lg) * 16 + (t & 15)) * 4 + 2 * (i & 1);
+}
+
 __device__ __forceinline__ int find_chunk(const DevChunk* __restrict__ chunks, int n, int64_t task) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
@@ -151,15 +189,6 @@ struct Geo {
   static constexpr int LDS = 16 * RS;          // bytes per wave
 };
 
-// Rotary pair (index into the band's d_rot/2 pairs) of coefficient slot j of a lane
-// in the MFMA layout; slots 2k and 2k+1 are always neighbouring pairs.
-__device__ __forceinline__ int lane_pair(int rot, int j, int lg) {
-  if (rot == ROT_NEOX_SLABS) return 32 * (j >> 3) + 8 * lg + (j & 7);   // slab-0 element j
-  if (rot == ROT_NEOX_RUNS) return 8 * lg + (j & 7);                    // run-0 element j
-  const int e2 = 2 * j, s = e2 >> 4, r = (e2 >> 3) & 1, e = e2 & 7;     // GPT-J pair (2j, 2j+1)
-  return (64 * s + 32 * r + 8 * lg + e) >> 1;
-}
-
 template <int NSLAB, int NK, bool POS>
 __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& ch, int layer, int tensor,
                                           int colbase, int tok0, int ntiles, int rot, const int* kfac,
@@ -185,12 +214,11 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   constexpr bool kPrefetchPhase = NSLAB == 1 || NK <= 1;
   float cs[NSLAB * 8], sn[NSLAB * 8], pcs[NSLAB * 8], psn[NSLAB * 8];
   auto load_phase = [&](int tile, float (&c_)[NSLAB * 8], float (&s_)[NSLAB * 8]) {
-    if constexpr (POS) {
-      const int t = min(tok0 + tile * kTileTokens + c, T - 1);
-      const float* row = ch.phase + (int64_t)t * hd.d_rot;  // [d_rot/2] x (cos, sin)
+    if constexpr (POS) {  // tile-major table (phase_offset): step k of the tile is 1 KB
+      const float* blk = ch.phase + (int64_t)((tok0 >> 4) + tile) * 16 * hd.d_rot + 4 * lane;
 #pragma unroll
       for (int k = 0; k < NSLAB * 4; ++k) {
-        const f32x4 v = *(const f32x4*)(row + 2 * lane_pair(rot, 2 * k, lg));
+        const f32x4 v = *(const f32x4*)(blk + 256 * k);
         c_[2 * k] = v[0];
         s_[2 * k] = v[1];
         c_[2 * k + 1] = v[2];
@@ -510,7 +538,7 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
   int rot = ROT_NONE;
   const bool band = hd.family == 0 ? (tensor == 0) : (g == hd.rope_group);
   const bool turns = ch.delta != 0 || (POS && (ch.flags & 4u) != 0);
-  if (band && turns) rot = hd.pairing == 1 ? ROT_GPTJ : (hd.d_rot == 128 ? ROT_NEOX_SLABS : ROT_NEOX_RUNS);
+  if (band && turns) rot = band_rot(hd);
 
   // 32-wide k-steps of the factors covering this group's columns
   int kfac[kMaxKSteps], kstep[kMaxKSteps];
@@ -637,7 +665,7 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
       }
       float a = ld<T>(src, so + cp), bb = ld<T>(src, so + cq);
       if (rotate) {
-        const float2 cs = tok_phase ? ((const float2*)ch.phase)[(int64_t)t * npairs + i] : tab[i];
+        const float2 cs = tok_phase ? *(const float2*)(ch.phase + phase_offset(hd, t, i)) : tab[i];
         const float na = fmaf(a, cs.x, -(bb * cs.y));
         const float nb = fmaf(a, cs.y, bb * cs.x);
         a = na;
@@ -676,13 +704,13 @@ __global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __
   const DevChunk& ch = chunks[lo];
   const int np = hd.d_rot >> 1;
   const int64_t r = e - ch.phase0;
-  const int64_t t = r / np;
+  const int64_t t = r / np;             // token of the padded tile range; past T: a copy of T-1
   const int i = (int)(r - t * np);
   int comp = 0;
   if (hd.mrope[0] | hd.mrope[1] | hd.mrope[2]) comp = i < hd.mrope[0] ? 0 : (i < hd.mrope[0] + hd.mrope[1] ? 1 : 2);
   float c, s;
-  phase_fp64(hd.rope_base, hd.d_rot, (int64_t)ch.positions[t * 3 + comp], i, c, s);
-  ((float2*)ch.phase)[t * np + i] = make_float2(c, s);
+  phase_fp64(hd.rope_base, hd.d_rot, (int64_t)ch.positions[min(t, (int64_t)ch.T - 1) * 3 + comp], i, c, s);
+  *(float2*)(ch.phase + phase_offset(hd, t, i)) = make_float2(c, s);
 }
 
 // ============================================================================

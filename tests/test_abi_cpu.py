@@ -199,12 +199,13 @@ def test_validation_errors(case, expect):
 
 
 def test_batch_workspace_bytes_counts_tables():
-    """Per-token cos/sin tables: [T][d_rot/2] (cos, sin) fp32 per re-anchored chunk, 256-byte rounded."""
+    """Per-token cos/sin tables: (cos, sin) fp32 per pair of every token of a re-anchored chunk, tokens padded
+    to whole 16-token tiles, 256-byte rounded."""
     lay = gqa_layout(mrope_section=(16, 24, 24))
     plain = abi.batch_workspace_bytes(lay, [chunk(), chunk(num_tokens=100)])
     assert plain == abi.workspace_bytes(2, 0)
     withpos = abi.batch_workspace_bytes(lay, [chunk(), chunk(num_tokens=100, flags=abi.POSITIONS, positions=FAKE)])
-    assert withpos - plain == -(-100 * 64 * 8 // 256) * 256
+    assert withpos - plain == -(-112 * 64 * 8 // 256) * 256
     paged = abi.batch_workspace_bytes(lay, [chunk(num_tokens=40, slot0=3, block_table=np.array([1, 2, 3]))])
     assert paged == abi.workspace_bytes(1, 3)
 
