@@ -12,7 +12,13 @@ constexpr int kBlockThreads = 256;           // generic and copy-in kernels
 // token block and the next block, so a workgroup's waves share U rows (4 heads)
 // and V rows (2 blocks) through the CU's caches; measured faster than 4 or 16.
 constexpr int kWavesPerBlock = 8;
-constexpr int kMfmaBlockThreads = kWaveSize * kWavesPerBlock;
+// One-slab variants with at most 2 k-steps (MLA rows, 64-wide heads) fit 3 waves per
+// SIMD; 4-wave workgroups let 3 of them share a CU (12 waves, against 8 with 8-wave
+// workgroups): measured 9% faster on the 27-layer MLA batch.
+constexpr int kWavesPerBlockNarrow = 4;
+constexpr int mfma_waves_per_block(int nslab, int nkmax) {
+  return (nslab == 1 && nkmax <= 2) ? kWavesPerBlockNarrow : kWavesPerBlock;
+}
 constexpr int kSlab = 64;          // columns per slab of the MFMA path
 constexpr int kTileTokens = 16;    // tokens per MFMA tile (the N dimension)
 constexpr int kMaxFactors = 4;

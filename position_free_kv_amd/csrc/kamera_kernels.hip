@@ -503,9 +503,10 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 }
 
 template <int NSLAB, int NKMAX, bool POS>
-__global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHeader* __restrict__ hdr,
-                                                                const DevChunk* __restrict__ chunks) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWavesPerBlock * Geo<NSLAB>::LDS];
+__global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
+    const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
+  constexpr int kWaves = mfma_waves_per_block(NSLAB, NKMAX);
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWaves * Geo<NSLAB>::LDS];
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const DevHeader& hd = *hdr;
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(kMfmaBlockThreads) void rehydrate_mfma(const DevHea
       blk = (j >> wl) * win + (x << wl) + (j & ((1 << wl) - 1));
     }
   }
-  const int64_t task = blk * kWavesPerBlock + wave;
+  const int64_t task = blk * kWaves + wave;
   if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
   const TaskCoord tcd = decode_task(hd, chunks, task);
   const DevChunk& ch = chunks[tcd.chunk];
@@ -743,33 +744,34 @@ hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int6
 }
 
 template <int NSLAB, int NKMAX, bool POS = false>
-static void launch_one(dim3 grid, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
-  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), grid, dim3(kMfmaBlockThreads), 0, stream, hdr, chunks);
+static hipError_t launch_one(int64_t tasks, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
+  constexpr int w = mfma_waves_per_block(NSLAB, NKMAX);
+  const int64_t blocks = (tasks + w - 1) / w;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0, stream,
+                     hdr, chunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                        hipStream_t stream) {
-  const int64_t blocks = (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks);
+  if (tasks <= 0) return hipSuccess;
   switch (variant) {  // variant = (nslab - 1) * 4 + log2(nk_max)
-    case 0: launch_one<1, 1>(grid, stream, hdr, chunks); break;
-    case 1: launch_one<1, 2>(grid, stream, hdr, chunks); break;
-    case 2: launch_one<1, 4>(grid, stream, hdr, chunks); break;
-    case 3: launch_one<1, 8>(grid, stream, hdr, chunks); break;
-    case 4: launch_one<2, 1>(grid, stream, hdr, chunks); break;
-    case 5: launch_one<2, 2>(grid, stream, hdr, chunks); break;
-    case 6: launch_one<2, 4>(grid, stream, hdr, chunks); break;
+    case 0: return launch_one<1, 1>(tasks, stream, hdr, chunks);
+    case 1: return launch_one<1, 2>(tasks, stream, hdr, chunks);
+    case 2: return launch_one<1, 4>(tasks, stream, hdr, chunks);
+    case 3: return launch_one<1, 8>(tasks, stream, hdr, chunks);
+    case 4: return launch_one<2, 1>(tasks, stream, hdr, chunks);
+    case 5: return launch_one<2, 2>(tasks, stream, hdr, chunks);
+    case 6: return launch_one<2, 4>(tasks, stream, hdr, chunks);
     // batches with per-token offsets (kVariantPositions + the variant above)
-    case 8: launch_one<1, 1, true>(grid, stream, hdr, chunks); break;
-    case 9: launch_one<1, 2, true>(grid, stream, hdr, chunks); break;
-    case 10: launch_one<1, 4, true>(grid, stream, hdr, chunks); break;
-    case 12: launch_one<2, 1, true>(grid, stream, hdr, chunks); break;
-    case 13: launch_one<2, 2, true>(grid, stream, hdr, chunks); break;
+    case 8: return launch_one<1, 1, true>(tasks, stream, hdr, chunks);
+    case 9: return launch_one<1, 2, true>(tasks, stream, hdr, chunks);
+    case 10: return launch_one<1, 4, true>(tasks, stream, hdr, chunks);
+    case 12: return launch_one<2, 1, true>(tasks, stream, hdr, chunks);
+    case 13: return launch_one<2, 2, true>(tasks, stream, hdr, chunks);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,

@@ -5,12 +5,15 @@ kernel trace, one per counter, as rocprofv3 collects counters in runs of their
 own), then summarise:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c2 -- \\
-        python3 bench.py --steps 200 --warmup 20 --no-cpu
+        python3 bench.py --config C2 --steps 200 --warmup 20 --no-cpu > OUT/trace.log
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o c2 -- \\
-        python3 bench.py --steps 5 --warmup 1 --no-cpu
+        python3 bench.py --config C2 --steps 5 --warmup 1 --no-cpu
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/prof_write -o c2 -- \\
-        python3 bench.py --steps 5 --warmup 1 --no-cpu
+        python3 bench.py --config C2 --steps 5 --warmup 1 --no-cpu
     python3 profile_summary.py OUT C2
+
+(the -o prefix is the workload name in lower case; OUT/trace.log holds the traced
+run's bench.py JSON line)
 
 HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what
 the same counter reads for bench.py's plain 1 GiB device copy (reads 1 GiB,
@@ -53,11 +56,17 @@ def _kernel_kib(agg):
     return sum(vals) / len(vals), len(vals)
 
 
+def _bench_line(out: str) -> dict:
+    with open(os.path.join(out, "trace.log")) as fh:
+        return json.loads(next(ln for ln in fh if ln.startswith("{")))
+
+
 def main(out: str, cfg: str) -> None:
-    stats = _rows(os.path.join(out, "prof_trace", "c2_kernel_stats.csv"))
-    bench = json.loads(open(os.path.join(out, "prof_trace_bench.json")).read())
-    fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", "c2_counter_collection.csv")))
-    write = _per_kernel(_rows(os.path.join(out, "prof_write", "c2_counter_collection.csv")))
+    pre = cfg.lower()
+    stats = _rows(os.path.join(out, "prof_trace", f"{pre}_kernel_stats.csv"))
+    bench = _bench_line(out)
+    fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", f"{pre}_counter_collection.csv")))
+    write = _per_kernel(_rows(os.path.join(out, "prof_write", f"{pre}_counter_collection.csv")))
     f_copy, w_copy = _copy_kib(fetch), _copy_kib(write)
     f_scale, w_scale = (COPY_BYTES / 1024) / f_copy, (COPY_BYTES / 1024) / w_copy
     f_k, nf = _kernel_kib(fetch)
@@ -76,8 +85,8 @@ def main(out: str, cfg: str) -> None:
         "",
         "## kernel trace (rocprofv3 --kernel-trace --stats)",
         "",
-        "command: rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c2 -- "
-        "python3 bench.py --steps 200 --warmup 20 --no-cpu",
+        f"command: rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o {pre} -- "
+        f"python3 bench.py --config {cfg} --steps 200 --warmup 20 --no-cpu",
         "",
         "| kernel | calls | average us | min us | max us | share of GPU time |",
         "|---|---|---|---|---|---|",
@@ -93,8 +102,8 @@ def main(out: str, cfg: str) -> None:
         "",
         "## HBM bytes (rocprofv3 --pmc, one counter per run)",
         "",
-        "commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write -o c2 -- "
-        "python3 bench.py --steps 5 --warmup 1 --no-cpu",
+        f"commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write -o {pre} -- "
+        f"python3 bench.py --config {cfg} --steps 5 --warmup 1 --no-cpu",
         "",
         "| counter | plain 1 GiB copy (KiB/dispatch) | scale to bytes | kernel (KiB/dispatch, mean of n) | kernel bytes |",
         "|---|---|---|---|---|",
