@@ -204,6 +204,76 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   const uint16_t* src = (const uint16_t*)ch.src[tensor] + (int64_t)layer * ch.src_ls + colbase + 8 * lchunk;
   uint16_t* dst = (uint16_t*)ch.dst[tensor] + (int64_t)layer * ch.dst_ls + colbase + 8 * lchunk;
 
+  // Pool pages. The task's page ids (at most 64) are read once, lane i holding the
+  // i-th; with pages of >= 16 slots a 16-token tile spans at most two of them, which
+  // v_readlane extracts at a uniform index, so no memory read sits on the row
+  // address path. Other page sizes read the table once per row.
+  const int pshift = hd.page_shift;
+  int pg_base = 0, pg_last = 0, pg_reg = 0;
+  bool two_pages = false;
+  if (pages != nullptr) {
+    const int s_first = ch.slot0 + tok0, s_end = ch.slot0 + min(tok0 + ch.tb_tokens, T) - 1;
+    pg_base = pshift >= 0 ? s_first >> pshift : s_first / P;
+    pg_last = pshift >= 0 ? s_end >> pshift : s_end / P;
+    two_pages = P >= kTileTokens && pg_last - pg_base < 64;
+    if (two_pages && lane <= pg_last - pg_base) pg_reg = pages[pg_base + lane];
+  }
+  auto page_row = [&](int tt, int t) -> int64_t {  // element offset of token t's row (tile starting at tt)
+    const int s = ch.slot0 + t;
+    const int pi = pshift >= 0 ? s >> pshift : s / P;
+    const int off = pshift >= 0 ? s & (P - 1) : s - pi * P;
+    int pg;
+    if (two_pages) {
+      const int s0 = ch.slot0 + tt;
+      const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
+      const int pg0 = __builtin_amdgcn_readlane(pg_reg, pi0 - pg_base);
+      const int pg1 = __builtin_amdgcn_readlane(pg_reg, min(pi0 + 1, pg_last) - pg_base);
+      pg = pi == pi0 ? pg0 : pg1;
+    } else {
+      pg = pages[pi];
+    }
+    return ((int64_t)pg * P + off) * F;
+  };
+  // A tile whose 16 rows sit in one page (or in dense rows) is addressed from one
+  // uniform base, like dense rows; only tiles that straddle pages take page_row.
+  auto tile_base = [&](bool paged, int tt, int64_t& base) -> bool {
+    if (!paged) {
+      base = (int64_t)tt * F;
+      return true;
+    }
+    if (!two_pages) return false;
+    const int s0 = ch.slot0 + tt;
+    const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
+    const int off0 = s0 - pi0 * P;
+    if (off0 + kTileTokens > P) return false;
+    base = ((int64_t)__builtin_amdgcn_readlane(pg_reg, pi0 - pg_base) * P + off0) * F;
+    return true;
+  };
+
+  // The first tile's rows are requested before the per-task set-up (phase, V operands),
+  // so the set-up runs while they are in flight.
+  u32x4 cur[G::NI], nxt[G::NI];
+  auto load_rows = [&](int tile, u32x4 (&raw)[G::NI]) {
+    // Rows past the chunk end load the last row instead (computed, never stored), so
+    // no loaded value is merged with a default and the loads stay in flight.
+    const int tt = tok0 + tile * kTileTokens;
+    int64_t base;
+    if (tile_base(in_place && pages, tt, base)) {
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = min(tt + i * G::RPI + lrow, T - 1);
+        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + base + (int64_t)(t - tt) * F));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::NI; ++i) {
+        const int t = min(tt + i * G::RPI + lrow, T - 1);
+        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + page_row(tt, t)));
+      }
+    }
+  };
+  load_rows(0, cur);
+
   // ---- rotation coefficients for the pairs this lane holds (MFMA layout): one
   // set per chunk (delta), or, for chunks with per-token offsets, the set of this
   // lane's token read from the batch's cos/sin table for every tile (the next
@@ -281,73 +351,9 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
 
   const bool compute = (rot != ROT_NONE) || (NK > 0);
 
-  // Pool pages. The task's page ids (at most 64) are read once, lane i holding the
-  // i-th; with pages of >= 16 slots a 16-token tile spans at most two of them, which
-  // v_readlane extracts at a uniform index, so no memory read sits on the row
-  // address path. Other page sizes read the table once per row.
-  const int pshift = hd.page_shift;
-  int pg_base = 0, pg_last = 0, pg_reg = 0;
-  bool two_pages = false;
-  if (pages != nullptr) {
-    const int s_first = ch.slot0 + tok0, s_end = ch.slot0 + min(tok0 + ch.tb_tokens, T) - 1;
-    pg_base = pshift >= 0 ? s_first >> pshift : s_first / P;
-    pg_last = pshift >= 0 ? s_end >> pshift : s_end / P;
-    two_pages = P >= kTileTokens && pg_last - pg_base < 64;
-    if (two_pages && lane <= pg_last - pg_base) pg_reg = pages[pg_base + lane];
-  }
-  auto page_row = [&](int tt, int t) -> int64_t {  // element offset of token t's row (tile starting at tt)
-    const int s = ch.slot0 + t;
-    const int pi = pshift >= 0 ? s >> pshift : s / P;
-    const int off = pshift >= 0 ? s & (P - 1) : s - pi * P;
-    int pg;
-    if (two_pages) {
-      const int s0 = ch.slot0 + tt;
-      const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
-      const int pg0 = __builtin_amdgcn_readlane(pg_reg, pi0 - pg_base);
-      const int pg1 = __builtin_amdgcn_readlane(pg_reg, min(pi0 + 1, pg_last) - pg_base);
-      pg = pi == pi0 ? pg0 : pg1;
-    } else {
-      pg = pages[pi];
-    }
-    return ((int64_t)pg * P + off) * F;
-  };
-  // A tile whose 16 rows sit in one page (or in dense rows) is addressed from one
-  // uniform base, like dense rows; only tiles that straddle pages take page_row.
-  auto tile_base = [&](bool paged, int tt, int64_t& base) -> bool {
-    if (!paged) {
-      base = (int64_t)tt * F;
-      return true;
-    }
-    if (!two_pages) return false;
-    const int s0 = ch.slot0 + tt;
-    const int pi0 = pshift >= 0 ? s0 >> pshift : s0 / P;
-    const int off0 = s0 - pi0 * P;
-    if (off0 + kTileTokens > P) return false;
-    base = ((int64_t)__builtin_amdgcn_readlane(pg_reg, pi0 - pg_base) * P + off0) * F;
-    return true;
-  };
-
-  u32x4 cur[G::NI], nxt[G::NI];
   bf16x8 ucur[NK > 0 ? NK : 1], unxt[NK > 0 ? NK : 1];
-
-  auto load_tile = [&](int tile, u32x4 (&raw)[G::NI], bf16x8 (&ub)[NK > 0 ? NK : 1]) {
-    // Rows past the chunk end load the last row instead (computed, never stored), so
-    // no loaded value is merged with a default and the loads stay in flight.
+  auto load_u = [&](int tile, bf16x8 (&ub)[NK > 0 ? NK : 1]) {  // U rows of the tile's tokens
     const int tt = tok0 + tile * kTileTokens;
-    int64_t base;
-    if (tile_base(in_place && pages, tt, base)) {
-#pragma unroll
-      for (int i = 0; i < G::NI; ++i) {
-        const int t = min(tt + i * G::RPI + lrow, T - 1);
-        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + base + (int64_t)(t - tt) * F));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < G::NI; ++i) {
-        const int t = min(tt + i * G::RPI + lrow, T - 1);
-        raw[i] = __builtin_nontemporal_load((const u32x4*)(src + page_row(tt, t)));
-      }
-    }
     const int t = min(tt + c, T - 1);
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -365,10 +371,12 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
     }
   };
 
-  load_tile(0, cur, ucur);
+
+  load_u(0, ucur);
   for (int tile = 0; tile < ntiles; ++tile) {
     if (tile + 1 < ntiles) {
-      load_tile(tile + 1, nxt, unxt);
+      load_rows(tile + 1, nxt);
+      load_u(tile + 1, unxt);
       if (kPrefetchPhase && tok_phase) load_phase(tile + 1, pcs, psn);
     }
     if (!kPrefetchPhase && tok_phase && tile > 0) load_phase(tile, cs, sn);
