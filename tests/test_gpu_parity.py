@@ -12,7 +12,8 @@ import torch
 from tests.gpu_util import (check_all, custom_workload, factor, gqa_chunks, pool_untouched_ok, say,
                             touched_tensors)
 from workloads import make_workload
-from workloads.configs import BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, ChunkSpec, LayoutSpec
+from workloads.configs import (BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, POSITIONS, ChunkSpec, LayoutSpec,
+                               grid_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -292,3 +293,64 @@ def test_relocation_composes_on_gpu():
     vx = bf16_value(x.cpu().numpy().view(np.uint16)).reshape(-1, 2, 2, 64)
     norm = np.sqrt(vx[:, :, 0] ** 2 + vx[:, :, 1] ** 2)[:, :, None, :]
     assert np.all(np.abs(va - vb) <= 2 * ulp_bf16(norm))
+
+
+# ---------------------------------------------------------------- limits
+@pytest.mark.parametrize("case", ["rank256_gqa128", "head512", "head512_gptj", "mla_rope512", "mla_rank256",
+                                  "four_factors_rank256"])
+def test_maximum_sizes(case):
+    """The ABI's upper limits: rank KAMERA_MAX_RANK (256), 512-wide heads and rope bands,
+    four factors of the largest rank on one tensor (all past the MFMA variants' register
+    budget, so the generic kernel runs them)."""
+    say(f"[limits] {case}")
+    if case.startswith("mla"):
+        rope = 512 if case == "mla_rope512" else 64
+        lat = 64 if case == "mla_rope512" else 512
+        rank = 256 if case == "mla_rank256" else 16
+        lay = LayoutSpec(MLA, BF16, 1, latent_dim=lat, rope_dim=rope, rope_base=1e4)
+        F = lat + rope
+        chunks = [ChunkSpec(index=0, num_tokens=40, delta=77777, flags=PATCH, canon_id=0,
+                            factors=[factor(0, 0, 0, 0, F, rank), factor(0, 1, 0, lat, rope, rank)], dst_buffer=0)]
+    elif case == "four_factors_rank256":
+        lay = LayoutSpec(GQA, BF16, 1, num_kv_heads=2, head_dim=128, rope_base=1e6)
+        facs = [factor(0, s, 0, 64 * s, 128, 256, sigma0=0.1) for s in range(3)] + [factor(0, 3, 1, 0, 256, 256)]
+        chunks = [ChunkSpec(index=0, num_tokens=300, delta=-5000, flags=PATCH, canon_id=0, factors=facs,
+                            dst_buffer=0)]
+    else:
+        hd = 512 if case.startswith("head512") else 128
+        rank = 256 if case == "rank256_gqa128" else 24
+        lay = LayoutSpec(GQA, BF16, 1, num_kv_heads=2, head_dim=hd, rope_base=1e6,
+                         pairing=GPTJ if "gptj" in case else NEOX)
+        chunks = gqa_chunks(2, [300, 33], [123456, -99], 2, hd, rank)
+    assert_parity(run_dw(custom_workload(lay, chunks)))
+
+
+def test_many_chunks_in_one_batch():
+    """300 chunks of 0 to 40 tokens in one launch (the task decode searches a long chunk
+    list; empty chunks own no tasks), half of them paged, every third one re-anchored token
+    by token (the cos/sin table kernel searches the same list)."""
+    say("[many chunks]")
+    P = 16
+    lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=P,
+                     mrope_section=(16, 24, 24))
+    rng = np.random.default_rng(77)
+    pages = rng.permutation(2000).astype(np.int32)
+    chunks, cur = [], 0
+    for i in range(300):
+        T = int(rng.integers(0, 41))
+        kw = dict(index=i, num_tokens=T, delta=int(rng.integers(-50000, 50000)), flags=PATCH, canon_id=i,
+                  factors=[factor(i, 0, 0, 0, 256, 8), factor(i, 1, 1, 0, 256, 8)])
+        if i % 2:
+            n = -(-(3 + T) // P)
+            kw.update(block_table=pages[cur:cur + n].copy(), slot0=3)
+            cur += n
+        else:
+            kw.update(dst_buffer=i // 2)
+        if i % 3 == 0:
+            kw.update(positions=grid_positions(T, int(rng.integers(0, 9000)), frame_tokens=16, grid_w=4),
+                      flags=PATCH | POSITIONS)
+        chunks.append(ChunkSpec(**kw))
+    wl = custom_workload(lay, chunks, num_pages=2000)
+    dw = run_dw(wl)
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
