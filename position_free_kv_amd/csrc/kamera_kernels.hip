@@ -57,16 +57,24 @@ __device__ __forceinline__ uint16_t f_to_bf(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// cos/sin of delta * theta_i, theta_i = base^(-2i/d_rot), angle formed and
-// evaluated in fp64, then rounded once to fp32.
-__device__ __forceinline__ void phase_fp64(double base, int d_rot, int64_t delta, int i, float& c,
-                                           float& s) {
-  const double th = pow(base, (-2.0 * (double)i) / (double)d_rot);
-  const double phi = (double)delta * th;
+// theta_i = base^(-2i/d_rot) in fp64.
+__device__ __forceinline__ double theta_fp64(double base, int d_rot, int i) {
+  return pow(base, (-2.0 * (double)i) / (double)d_rot);
+}
+
+// cos/sin of p * theta, the angle formed and evaluated in fp64, then rounded once to fp32.
+__device__ __forceinline__ void phase_at(double th, int64_t p, float& c, float& s) {
+  const double phi = (double)p * th;
   double sd, cd;
   sincos(phi, &sd, &cd);
   c = (float)cd;
   s = (float)sd;
+}
+
+// cos/sin of delta * theta_i (the per-chunk phase).
+__device__ __forceinline__ void phase_fp64(double base, int d_rot, int64_t delta, int i, float& c,
+                                           float& s) {
+  phase_at(theta_fp64(base, d_rot, i), delta, c, s);
 }
 
 // Rotary pair (index into the band's d_rot/2 pairs) of coefficient slot j of a lane
@@ -712,9 +720,12 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
 // ============================================================================
 __global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __restrict__ hdr,
                                                              const DevChunk* __restrict__ chunks, int64_t entries) {
+  __shared__ double theta[256];   // theta_i of the band's d_rot/2 <= 256 pairs, once per workgroup
+  const DevHeader& hd = *hdr;
+  for (int i = threadIdx.x; i < (hd.d_rot >> 1); i += kBlockThreads) theta[i] = theta_fp64(hd.rope_base, hd.d_rot, i);
+  __syncthreads();
   const int64_t e = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (e >= entries) return;
-  const DevHeader& hd = *hdr;
   // the last chunk whose table starts at or before entry e owns it (chunks without
   // a table take no entries, so a later chunk with the same start is the owner)
   int lo = 0, hi = hd.nchunks - 1;
@@ -730,7 +741,7 @@ __global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __
   int comp = 0;
   if (hd.mrope[0] | hd.mrope[1] | hd.mrope[2]) comp = i < hd.mrope[0] ? 0 : (i < hd.mrope[0] + hd.mrope[1] ? 1 : 2);
   float c, s;
-  phase_fp64(hd.rope_base, hd.d_rot, (int64_t)ch.positions[min(t, (int64_t)ch.T - 1) * 3 + comp], i, c, s);
+  phase_at(theta[i], (int64_t)ch.positions[min(t, (int64_t)ch.T - 1) * 3 + comp], c, s);
   *(float2*)(ch.phase + phase_offset(hd, t, i)) = make_float2(c, s);
 }
 
