@@ -287,12 +287,11 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   load_rows(0, cur);
   if (kDeep && ntiles > 1) load_rows(1, nxt);
 
-  // ---- rotation coefficients for the pairs this lane holds (MFMA layout): one
-  // set per chunk (delta), or, for chunks with per-token offsets, the set of this
-  // lane's token read from the batch's cos/sin table for every tile (the next
-  // tile's set is loaded with the next tile's rows).
-  // Where registers allow (one slab, or one k-step) the next tile's set is loaded
-  // with the next tile's rows; otherwise at the top of its own tile.
+  // ---- rotation coefficients for the pairs this lane holds (MFMA layout): one set per
+  // chunk (delta), or, for chunks with per-token offsets, the set of this lane's token,
+  // read from the batch's cos/sin table for every tile. Where registers allow (one slab,
+  // or one k-step) the next tile's set is loaded with the next tile's rows; otherwise at
+  // the top of its own tile.
   const bool tok_phase = POS && rot != ROT_NONE && (ch.flags & 4u) != 0;
   constexpr bool kPrefetchPhase = NSLAB == 1 || NK <= 1;
   float cs[NSLAB * 8], sn[NSLAB * 8], pcs[NSLAB * 8], psn[NSLAB * 8];
