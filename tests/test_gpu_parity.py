@@ -354,3 +354,37 @@ def test_many_chunks_in_one_batch():
     dw = run_dw(wl)
     assert_parity(dw)
     assert pool_untouched_ok(dw)
+
+
+@pytest.mark.parametrize("positions", [False, True])
+def test_plan_launch_in_a_captured_graph(positions):
+    """kamera_plan_launch recorded in a HIP graph (the plan was uploaded eagerly; a launch
+    enqueues only the main kernel): every replay, with the outputs cleared eagerly in between,
+    reproduces the eager result bit for bit."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    say(f"[graph] positions={positions}")
+    wl = make_workload("C2", num_layers=2, num_chunks=3, tokens=150, positions=positions)
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for buf in dw.dense for t in buf]
+    assert_parity(dw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan = dw.plan()          # uploads (and builds the cos/sin tables) on the side stream, eagerly
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        abi.plan_launch(plan)     # captured on torch's capture stream
+    for rep in range(3):
+        for buf in dw.dense:
+            for t in buf:
+                t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t for buf in dw.dense for t in buf]
+        assert all(torch.equal(a, b) for a, b in zip(eager, got)), f"replay {rep}"
