@@ -219,8 +219,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
-                                   "several GPUs would each run their own share (see DESIGN.md); only --gpus 1 "
-                                   "is measured"}), flush=True)
+                                   "several GPUs would each rehydrate their own chunks (or layers) with no "
+                                   "exchange between them; only --gpus 1 is measured"}), flush=True)
         return 2
     if args.builder:
         if args.config not in BUILDER_SHAPES:

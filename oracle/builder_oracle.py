@@ -10,8 +10,9 @@ conditioned KV minus the *relocated* canonical R(delta).KV(B|empty); its SVD
 is truncated to the top m components and stored as (U*Sigma, V^T) (Fig. 2(d):
 "store U Sigma, V^T").
 
-The SVD is LAPACK's (scipy.linalg.svd, gesdd driver), the library routine the
-north star names as the reference for the truncated factorisation.
+The SVD is LAPACK's (scipy.linalg.svd, gesdd driver): the truncated factorisation
+that a builder's factors are checked against through their Eckart-Young residual
+energy (the optimum rank-m residual is the sum of the discarded sigma_i^2).
 """
 from __future__ import annotations
 

@@ -22,7 +22,7 @@ What it computes, and where the pages say so (page titles as cited):
   KAMERA §5: sliding-window survivors need the rotation only.
   KAMERA §6: the rebuilt KV lands in a paged KV pool.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * frequencies: textbook RoPE, theta_i = base^(-2i/d_rot), i < d_rot/2;
   * pairing: NeoX half split (i, i + d_rot/2) unless GPT-J (2i, 2i+1) is asked;
   * sign: a' = a cos(phi) - b sin(phi), b' = a sin(phi) + b cos(phi), phi = delta*theta_i,
