@@ -181,7 +181,9 @@ size_t kamera_batch_workspace_bytes(const kamera_layout* layout, const kamera_ch
  * R(delta)): rotates the K rotary bands (GQA) or the k_rope band (MLA) of tokens
  * [0, num_tokens) stored in `pool`; V and c_KV are neither read nor written.
  * block_table (HOST) maps slots as in kamera_chunk; NULL maps slot s to pool row s
- * (page s / page_size, offset s % page_size), i.e. the pool as dense rows. */
+ * (page s / page_size, offset s % page_size), i.e. the pool as dense rows. Either way the
+ * workspace needs kamera_workspace_bytes(1, pages spanned by slots [slot0, slot0 +
+ * num_tokens)) bytes. */
 kamera_status kamera_relocate(const kamera_layout* layout, const kamera_pool* pool,
                               const int32_t* block_table, int32_t slot0, int32_t num_tokens,
                               int64_t delta, void* workspace, size_t workspace_bytes, void* stream);
