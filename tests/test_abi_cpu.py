@@ -44,6 +44,16 @@ def test_library_exports_every_declared_symbol():
     assert abi.version().startswith("kamera-gfx950")
 
 
+@pytest.mark.parametrize("lang,std", [("c", "c11"), ("c++", "c++11")])
+def test_header_compiles_on_its_own(lang, std):
+    """include/kamera.h is a self-contained C ABI: strict C11 and C++11 accept it alone."""
+    import subprocess
+    cc = "gcc" if lang == "c" else "g++"
+    r = subprocess.run([cc, f"-std={std}", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only", "-x", lang,
+                        HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_struct_sizes_match_header():
     # natural C layout on x86_64 (checked against the header's field order)
     assert ctypes.sizeof(abi.Layout) == 64
