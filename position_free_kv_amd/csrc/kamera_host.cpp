@@ -395,7 +395,13 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
     hd->xcd_window_log2 = ngroups > kWavesPerBlock ? 4 : (ngroups == kWavesPerBlock ? 2 : 0);
   }
 
-  const int tb_tokens = mfma ? kMfmaRangeTokens : 16;
+  // Generic kernel: one workgroup per 16 tokens, or per 4 tokens when the batch is too
+  // small to fill the chip that way (fewer than 1024 workgroups of 16 tokens): each
+  // thread then has about one element to compute instead of waiting out several memory
+  // round trips in turn (a single-layer 256-token fp32 chunk: 14.8 -> 6.3 us).
+  int64_t generic_rows = 0;
+  for (int i = 0; i < n; ++i) generic_rows += (int64_t)chunks[i].num_tokens * L->num_layers * ntensors;
+  const int tb_tokens = mfma ? kMfmaRangeTokens : (generic_rows >= 16 * 1024 ? 16 : 4);
   const bool layer_major = kLayerMajorPaged && mfma && any_paged;
   int64_t task = 0;
   int64_t page_cursor = 0;

@@ -62,6 +62,15 @@ def test_config_parity_small(name, kw):
                     assert np.array_equal(dw.out_rows(ch, layer, 1), wl.pool_rows(ch, layer, 1))
 
 
+def test_generic_kernel_large_fp32_batch():
+    """fp32 batches run the generic kernel; one large enough to fill the chip takes 16-token
+    workgroups (small ones take 4-token workgroups, as in the single-layer config above)."""
+    say("[generic fp32, 16-token blocks]")
+    wl = make_workload("C1", num_layers=8, num_chunks=8)
+    assert sum(c.num_tokens for c in wl.chunks) * 8 * 2 >= 16 * 1024
+    assert_parity(run_dw(wl))
+
+
 # ---------------------------------------------------------------- bit-exact identity
 @pytest.mark.parametrize("family", ["gqa128", "gqa64", "mla", "gqa_f32"])
 def test_identity_delta0_nopatch(family):
