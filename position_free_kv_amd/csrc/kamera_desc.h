@@ -58,7 +58,6 @@ struct alignas(16) DevChunk {
   const int32_t* pages; // device copy of the block table (NULL: dense destination)
   const int32_t* positions;  // per-token offsets [T][3] (KAMERA_POSITIONS), caller's device memory
   const float* phase;   // per-token cos/sin table in the workspace (positions chunks; see phase_offset)
-  int64_t phase0;       // first entry (padded token, pair) of this chunk in the batch's table space
   int64_t task0;        // first task id of this chunk
   int32_t T;
   uint32_t flags;

@@ -21,7 +21,8 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                           hipStream_t stream);
 hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
-hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int64_t entries, hipStream_t stream);
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t max_entries,
+                              hipStream_t stream);
 }  // namespace kamera
 
 using namespace kamera;
@@ -161,6 +162,7 @@ struct Packed {
   size_t upload_bytes = 0;           // header | chunks | pages
   size_t bytes = 0;                  // the whole workspace (tables included)
   int64_t phase_entries = 0;         // table entries (padded token, pair) of the batch
+  int64_t phase_max = 0;             // the most entries of one chunk's table
   bool positions = false;
   int64_t tasks = 0;
   int kernel = 0;   // 0 none, 1 mfma, 2 generic
@@ -357,6 +359,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   out.bytes = out.upload_bytes;
   out.phase_off.assign((size_t)n, -1);
   out.phase_entries = 0;
+  out.phase_max = 0;
   out.positions = false;
   for (int i = 0; i < n; ++i)
     if ((chunks[i].flags & KAMERA_POSITIONS) && chunks[i].num_tokens > 0) {
@@ -416,10 +419,11 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
     d.flags = c.flags;
     d.delta = c.delta;
     d.slot0 = c.slot0;
-    d.phase0 = out.phase_entries;
     if (out.phase_off[(size_t)i] >= 0) {
       d.positions = c.positions;
-      out.phase_entries += phase_tokens(c.num_tokens) * (d_rot / 2);
+      const int64_t ne = phase_tokens(c.num_tokens) * (d_rot / 2);
+      out.phase_entries += ne;
+      out.phase_max = std::max(out.phase_max, ne);
     }
     if (c.num_tokens == 0) continue;
     const bool in_place = c.flags & KAMERA_IN_PLACE;
@@ -536,7 +540,7 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
     if (pk.phase_entries > 0) {  // per-token cos/sin tables, computed once per upload
       const DevHeader* hd = reinterpret_cast<const DevHeader*>(ws);
       const DevChunk* dcd = reinterpret_cast<const DevChunk*>((const char*)ws + round_up(sizeof(DevHeader), kAlign));
-      const hipError_t e = launch_phase_table(hd, dcd, pk.phase_entries, (hipStream_t)stream);
+      const hipError_t e = launch_phase_table(hd, dcd, n, pk.phase_max, (hipStream_t)stream);
       if (e != hipSuccess) return fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
     }
   }

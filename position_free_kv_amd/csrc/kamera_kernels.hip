@@ -718,25 +718,20 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
 // pairs; all zero means every pair follows component t (1-D RoPE).
 // ============================================================================
 __global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __restrict__ hdr,
-                                                             const DevChunk* __restrict__ chunks, int64_t entries) {
+                                                             const DevChunk* __restrict__ chunks, int blocks_per_chunk) {
   __shared__ double theta[256];   // theta_i of the band's d_rot/2 <= 256 pairs, once per workgroup
   const DevHeader& hd = *hdr;
-  for (int i = threadIdx.x; i < (hd.d_rot >> 1); i += kBlockThreads) theta[i] = theta_fp64(hd.rope_base, hd.d_rot, i);
-  __syncthreads();
-  const int64_t e = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
-  if (e >= entries) return;
-  // the last chunk whose table starts at or before entry e owns it (chunks without
-  // a table take no entries, so a later chunk with the same start is the owner)
-  int lo = 0, hi = hd.nchunks - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunks[mid].phase0 <= e) lo = mid; else hi = mid - 1;
-  }
-  const DevChunk& ch = chunks[lo];
+  // workgroup b covers entries [256 (b % blocks_per_chunk), ...) of chunk b / blocks_per_chunk
+  const DevChunk& ch = chunks[blockIdx.x / blocks_per_chunk];
   const int np = hd.d_rot >> 1;
-  const int64_t r = e - ch.phase0;
-  const int64_t t = r / np;             // token of the padded tile range; past T: a copy of T-1
-  const int i = (int)(r - t * np);
+  const int64_t n_entries = ch.phase ? (int64_t)((ch.T + kTileTokens - 1) / kTileTokens) * kTileTokens * np : 0;
+  const int64_t e = (int64_t)(blockIdx.x % blocks_per_chunk) * kBlockThreads + threadIdx.x;
+  if (e - threadIdx.x >= n_entries) return;  // uniform over the workgroup, before its barrier
+  for (int i = threadIdx.x; i < np; i += kBlockThreads) theta[i] = theta_fp64(hd.rope_base, hd.d_rot, i);
+  __syncthreads();
+  if (e >= n_entries) return;
+  const int64_t t = e / np;             // token of the padded tile range; past T: a copy of T-1
+  const int i = (int)(e - t * np);
   int comp = 0;
   if (hd.mrope[0] | hd.mrope[1] | hd.mrope[2]) comp = i < hd.mrope[0] ? 0 : (i < hd.mrope[0] + hd.mrope[1] ? 1 : 2);
   float c, s;
@@ -765,11 +760,13 @@ hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int64_t entries, hipStream_t stream) {
-  if (entries <= 0) return hipSuccess;
-  const int64_t blocks = (entries + kBlockThreads - 1) / kBlockThreads;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(phase_table, dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream, hdr, chunks, entries);
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t max_entries,
+                              hipStream_t stream) {
+  if (max_entries <= 0 || nchunks <= 0) return hipSuccess;
+  const int64_t per_chunk = (max_entries + kBlockThreads - 1) / kBlockThreads;
+  if (per_chunk > 0x7fffffffLL || per_chunk * nchunks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(phase_table, dim3((unsigned)(per_chunk * nchunks)), dim3(kBlockThreads), 0, stream, hdr, chunks,
+                     (int)per_chunk);
   return hipGetLastError();
 }
 
