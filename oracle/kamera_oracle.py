@@ -132,7 +132,7 @@ def rotate(x: np.ndarray, delta: int, band_offsets: Sequence[int], d_rot: int, b
 
 
 # ----------------------------------------------------------------------------
-# Per-token re-anchoring (QV-PIC Eq. 2: model-native M-RoPE applied with request
+# Per-token re-anchoring (QV-PIC Eq. 2: the backbone's own M-RoPE applied at the request
 # positions; KAMERA §4: a uniform shift of (t, h, w) is the 1-D rotation R(delta))
 # ----------------------------------------------------------------------------
 def pair_sections(d_rot: int, sections: Sequence[int]) -> np.ndarray:

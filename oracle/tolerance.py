@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/kamera_oracle.py).
 
-The fidelity bar comes from the Kamera preprint §6: the rebuilt KV lands
-within one bf16 ULP of recompute. With y the exact fp64 result, r = bf16(y)
-rounded once, and g the device output (fp32 accumulation, then one rounding):
+The fidelity bar comes from the Kamera preprint §6: the rebuilt KV agrees with a
+recompute to within one bf16 unit in the last place. With y the exact fp64 result,
+r = bf16(y) rounded once, and g the device output (fp32 accumulation, then one rounding):
 
   P1  |ord(g) - ord(r)| <= 1          ord = monotone integer order of bf16 codes, +0 == -0
   P2  |g - y| <= ulp_bf16(g)/2 + gamma_n * S

@@ -1,6 +1,6 @@
 """GPU parity: the HIP library against the fp64 oracle, element by element (small sizes).
 
-Bar (Kamera preprint §6, "within one bf16 ULP of recompute"): every bf16 output
+Bar (Kamera preprint §6: the rebuilt KV agrees with a recompute to one bf16 ulp): every bf16 output
 is within one bf16 step of the once-rounded fp64 result (P1) or within the fp32
 accumulation bound (P2); fp32 outputs meet P3. Indexing, untouched bytes and the
 identity case are bit-exact.
