@@ -12,7 +12,9 @@ from typing import Iterable, List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkamera.so")
+# KAMERA_LIBRARY names another build of the same library to load instead (the host-code
+# sanitizer test loads an AddressSanitizer build of the host part this way)
+LIB_PATH = os.environ.get("KAMERA_LIBRARY") or os.path.join(_HERE, "libkamera.so")
 
 GQA, MLA = 0, 1
 F32, BF16 = 0, 1

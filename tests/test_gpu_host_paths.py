@@ -116,3 +116,34 @@ def test_concurrent_callers_match_a_single_thread():
     assert not errors, errors
     for dw, r in zip(dws, ref):
         assert all(torch.equal(a, b) for a, b in zip(outs(dw), r))
+
+
+def test_evicted_chunk_recalled_into_new_pages_is_byte_identical():
+    """Eviction is reversible because the canonical rows are kept (Kamera preprint §5): a chunk
+    rehydrated into pool pages, evicted (its pages overwritten), then recalled from its
+    canonical rows into different pages gives the same bytes row for row."""
+    from position_free_kv_amd import abi
+    from tests.gpu_util import custom_workload, factor
+    from workloads.configs import BF16, GQA, PATCH, ChunkSpec, LayoutSpec
+    from workloads.device import DeviceWorkload
+    say("[evict+recall]")
+    P, T = 16, 150
+    lay = LayoutSpec(GQA, BF16, 3, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=P)
+    perm = np.random.default_rng(8).permutation(40).astype(np.int32)
+    n = -(-(3 + T) // P)
+    ch = ChunkSpec(index=0, num_tokens=T, delta=7777, flags=PATCH, canon_id=0,
+                   factors=[factor(0, 0, 0, 0, 256, 32), factor(0, 1, 1, 0, 256, 32)],
+                   block_table=perm[:n].copy(), slot0=3)
+    dw = DeviceWorkload(custom_workload(lay, [ch], dense_rows=[], num_pages=40))
+    dw.run()
+    torch.cuda.synchronize()
+    first = [[dw.out_rows(ch, layer, t) for t in (0, 1)] for layer in range(3)]
+    for t in dw.pool:                       # evict: every page overwritten
+        t.fill_(0x1234)
+    ch2 = ChunkSpec(**{**ch.__dict__, "block_table": perm[n:2 * n].copy(), "slot0": 9})
+    dw.wl.chunks = [ch2]
+    abi.rehydrate_batched(dw.layout, [dw._desc(ch2)], dw.pool_desc, dw.workspace)
+    torch.cuda.synchronize()
+    for layer in range(3):
+        for t in (0, 1):
+            assert np.array_equal(dw.out_rows(ch2, layer, t), first[layer][t]), (layer, t)
