@@ -159,6 +159,18 @@ def test_planted_bf16_c2_shape(tensor, col0, width, rank):
     check_case(case, rank=rank, iterations=16, sub_tol=1e-6, sig_tol=1e-4)
 
 
+def test_planted_bf16_c4_shape():
+    """C4 row shape (32 heads x 128, base 1e4): the whole 4096-wide K row of a 2048-token chunk,
+    rank 32 (the widest rows the builder is measured on; p = 80 of 2048 directions). The bf16
+    rounding of 2048 x 4096 stored rows leaves a noise floor of about 2^-9 (sqrt(T) + sqrt(W))
+    ~ 0.2 in the deficit's spectrum, so the planted values decay slowly enough (0.95) that all
+    32 kept ones stay well above it."""
+    case = BuilderCase(gqa(BF16, 32, 128, base=1e4), tensor=0, num_tokens=2048, delta=4096, col0=0, width=4096,
+                       sigma0=8.0, ratio=0.95, planted_rank=96, seed=14)
+    say("[builder] planted bf16 C4-shape 2048x4096 m=32")
+    check_case(case, rank=32, iterations=16, sub_tol=1e-6, sig_tol=1e-4)
+
+
 @pytest.mark.parametrize("col0,width,rank,delta", [(0, 576, 32, -3000), (512, 64, 16, 4096)])
 def test_planted_bf16_mla(col0, width, rank, delta):
     """MLA 512 + 64 row: the factor over the whole row, and the k_rope-only factor (exact: p = width)."""
