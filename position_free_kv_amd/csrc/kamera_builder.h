@@ -31,6 +31,8 @@ struct BuildArgs {
   double* vm;           // [W][m]
   double* bz;           // [p][p]  Gram of the block being orthonormalised
   double* lf;           // [p][p]  its Cholesky factor (lower)
+  double* zpart;        // [ksplit][p][W] partial products of Z = Q G (ksplit > 1)
+  int ksplit;           // slices of the sum over j in Z = Q G
   int* flag;            // 1: Cholesky QR rejected the block, the CGS2 fallback runs
   double base;          // RoPE base
   int T, F, W, col0, m, p, iters;

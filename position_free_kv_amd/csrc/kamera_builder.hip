@@ -191,32 +191,69 @@ __global__ __launch_bounds__(kThreads) void start_k(BuildArgs a) {
   if (e < (int64_t)a.p * a.W) a.z[e] = hash_uniform((uint64_t)e);
 }
 
-// Z[k][i] = sum_j Q[k][j] G[j][i]. A workgroup covers 64 columns i and kZRows rows
-// k; its 4 waves split the sum over j and add their partial sums in LDS (fixed
-// order, so the result is deterministic).
-constexpr int kZRows = 8;
+// Z[k][i] = sum_j Q[k][j] G[j][i] (Q: p x W, p <= 80; G: W x W). A workgroup computes all p rows
+// of 64 columns over one slice of the sum (workgroup (cb, s): columns 64 cb + [0, 64), j in
+// slice s of zt_split(W)), staging 32-wide chunks of Q and G in LDS; thread (tr, tc) of a 16 x 16
+// grid accumulates rows tr + 16 r (r < 5) and columns tc + 16 c (c < 4), so its LDS reads and the
+// final writes have unit stride across the wave. Each G element is read once per slice and used
+// for 80 rows. With more than one slice the partial products go to zpart and zred_k adds them
+// in slice order (deterministic).
+constexpr int kZCols = 64, kZChunk = 32;
 __global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
-  __shared__ double part[kThreads / 64][kZRows][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = blockIdx.x * 64 + lane;
-  const int k0 = blockIdx.y * kZRows;
-  const int nr = min(kZRows, a.p - k0);
-  double acc[kZRows];
+  __shared__ double qs[kBuildMaxSubspace][kZChunk + 1];
+  __shared__ double gs[kZChunk][kZCols + 1];
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int c0 = blockIdx.x * kZCols;
+  const int kl = (a.W + a.ksplit - 1) / a.ksplit;
+  const int j0 = blockIdx.y * kl, j1 = min(a.W, j0 + kl);
+  double acc[5][4];
 #pragma unroll
-  for (int r = 0; r < kZRows; ++r) acc[r] = 0.0;
-  if (i < a.W)
-    for (int j = wave; j < a.W; j += kThreads / 64) {
-      const double g = a.gram[(int64_t)j * a.W + i];
+  for (int r = 0; r < 5; ++r)
 #pragma unroll
-      for (int r = 0; r < kZRows; ++r)
-        if (r < nr) acc[r] = fma(a.q[(int64_t)(k0 + r) * a.W + j], g, acc[r]);
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+  for (int jc = j0; jc < j1; jc += kZChunk) {
+    const int kn = min(kZChunk, j1 - jc);
+    for (int e = tid; e < kBuildMaxSubspace * kZChunk; e += kThreads) {
+      const int r = e / kZChunk, k = e % kZChunk;
+      qs[r][k] = (r < a.p && k < kn) ? a.q[(int64_t)r * a.W + jc + k] : 0.0;
     }
+    for (int e = tid; e < kZChunk * kZCols; e += kThreads) {
+      const int k = e / kZCols, c = e % kZCols;
+      gs[k][c] = (k < kn && c0 + c < a.W) ? a.gram[(int64_t)(jc + k) * a.W + c0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < kZChunk; ++k) {  // entries past kn are zero and add nothing
+      double qv[5], gv[4];
 #pragma unroll
-  for (int r = 0; r < kZRows; ++r) part[wave][r][lane] = acc[r];
-  __syncthreads();
-  if (wave == 0 && i < a.W)
-    for (int r = 0; r < nr; ++r)
-      a.z[(int64_t)(k0 + r) * a.W + i] = part[0][r][lane] + part[1][r][lane] + part[2][r][lane] + part[3][r][lane];
+      for (int r = 0; r < 5; ++r) qv[r] = qs[tr + 16 * r][k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gv[c] = gs[k][tc + 16 * c];
+#pragma unroll
+      for (int r = 0; r < 5; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fma(qv[r], gv[c], acc[r][c]);
+    }
+    __syncthreads();
+  }
+  double* out = a.ksplit > 1 ? a.zpart + (int64_t)blockIdx.y * a.p * a.W : a.z;
+#pragma unroll
+  for (int r = 0; r < 5; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = tr + 16 * r, col = c0 + tc + 16 * c;
+      if (row < a.p && col < a.W) out[(int64_t)row * a.W + col] = acc[r][c];
+    }
+}
+
+// Z = the sum of the slices' partial products, added in slice order.
+__global__ __launch_bounds__(kThreads) void zred_k(BuildArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t n = (int64_t)a.p * a.W;
+  if (e >= n) return;
+  double v = 0.0;
+  for (int s = 0; s < a.ksplit; ++s) v += a.zpart[(int64_t)s * n + e];
+  a.z[e] = v;
 }
 
 // Q = rows of Z orthonormalised by classical Gram-Schmidt with one
@@ -522,11 +559,21 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
+// Slices of the sum in Z = Q G: enough workgroups to fill the chip (about 512 with 64-column
+// blocks), each slice at least 16 terms long.
+int zt_split(int64_t W) {
+  const int64_t blocks = (W + kZCols - 1) / kZCols;
+  int64_t ks = (512 + blocks - 1) / blocks;
+  ks = std::min<int64_t>(ks, std::max<int64_t>(W / 16, 1));
+  return (int)std::max<int64_t>(ks, 1);
+}
+
 size_t build_workspace_bytes(int64_t T, int64_t W, int64_t m) {
   const int64_t p = std::min<int64_t>(kBuildMaxSubspace, std::min(W, T));
+  const int64_t ks = zt_split(W);
   const size_t d = sizeof(double);
   return align256(T * W * d) + align256(W * W * d) + 2 * align256(p * W * d) + 4 * align256(p * p * d) +
-         align256(p * d) + align256(W * m * d) + 256;
+         align256(p * d) + align256(W * m * d) + (ks > 1 ? align256(ks * p * W * d) : 0) + 256;
 }
 
 void build_workspace_carve(BuildArgs& a, void* ws) {
@@ -547,6 +594,8 @@ void build_workspace_carve(BuildArgs& a, void* ws) {
   a.vm = take((int64_t)a.W * a.m);
   a.bz = take((int64_t)a.p * a.p);
   a.lf = take((int64_t)a.p * a.p);
+  a.ksplit = zt_split(a.W);
+  a.zpart = a.ksplit > 1 ? take((int64_t)a.ksplit * a.p * a.W) : nullptr;
   a.flag = (int*)c;
 }
 
@@ -571,12 +620,17 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
   };
   orthonormalise();
-  const dim3 zgrid(blocks_for(a.W, 64), blocks_for(a.p, kZRows));
-  for (int it = 0; it <= a.iters; ++it) {  // the range finder's product, then `iters` power steps
+  const dim3 zgrid(blocks_for(a.W, kZCols), a.ksplit);
+  const dim3 rgrid(blocks_for((int64_t)a.p * a.W, kThreads));
+  auto product = [&]() {  // a.z = a.q G
     hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
+    if (a.ksplit > 1) hipLaunchKernelGGL(zred_k, rgrid, blk, 0, st, a);
+  };
+  for (int it = 0; it <= a.iters; ++it) {  // the range finder's product, then `iters` power steps
+    product();
     orthonormalise();
   }
-  hipLaunchKernelGGL(zt_k, zgrid, blk, 0, st, a);
+  product();
   hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.z, a.h);
   hipLaunchKernelGGL(jacobi_k, dim3(1), dim3(kJacobiThreads), 0, st, a);
   hipLaunchKernelGGL(finish_k, dim3(blocks_for((int64_t)a.W * a.m, kThreads)), blk, 0, st, a);
