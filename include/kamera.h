@@ -128,8 +128,10 @@ typedef struct kamera_factor {
 /* One chunk to relocate/rehydrate across all L layers. */
 typedef struct kamera_chunk {
   int32_t num_tokens;          /* T >= 0 (0: nothing to do)                                   */
-  uint32_t flags;              /* KAMERA_PATCH | KAMERA_IN_PLACE                              */
-  int64_t delta;               /* signed position shift p1 - p0, |delta| < 2^31              */
+  uint32_t flags;              /* KAMERA_PATCH | KAMERA_IN_PLACE | KAMERA_POSITIONS            */
+  int64_t delta;               /* signed position shift p1 - p0, |delta| < 2^31 (not used by
+                                  KAMERA_POSITIONS chunks, which turn each token by its own
+                                  offsets)                                                    */
   const void* k_src;           /* device [L][T][F] canonical K (MLA: the row); unused in place */
   const void* v_src;           /* device [L][T][F] canonical V (GQA); unused for MLA/in place */
   int64_t src_layer_stride;    /* elements between layers of k_src/v_src; 0 means T*F          */
@@ -173,7 +175,9 @@ typedef struct kamera_plan {
 size_t kamera_workspace_bytes(int32_t num_chunks, int64_t total_block_table_entries);
 
 /* Bytes of device workspace needed for exactly this batch (block tables and the per-token
- * cos/sin tables of KAMERA_POSITIONS chunks included); 0 if the arguments are invalid. */
+ * cos/sin tables of KAMERA_POSITIONS chunks included; a table holds (cos, sin) in fp32 for
+ * every rotary pair of every token, tokens rounded up to a multiple of 16); 0 if the
+ * arguments are invalid. */
 size_t kamera_batch_workspace_bytes(const kamera_layout* layout, const kamera_chunk* chunks,
                                     int32_t num_chunks);
 
