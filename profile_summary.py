@@ -13,7 +13,11 @@ own), then summarise:
     python3 profile_summary.py OUT C2
 
 (the -o prefix is the workload name in lower case; OUT/trace.log holds the traced
-run's bench.py JSON line)
+run's bench.py JSON line). For per-token re-anchoring, trace
+`bench.py --config C2 --positions ...` the same way and summarise with
+`python3 profile_summary.py OUT C2 --positions`: the summary then covers the
+variant that reads the per-token cos/sin table, and counter runs are optional
+(without OUT/prof_fetch and OUT/prof_write the HBM-bytes section is left out).
 
 HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what
 the same counter reads for bench.py's plain 1 GiB device copy (reads 1 GiB,
@@ -61,24 +65,23 @@ def _bench_line(out: str) -> dict:
         return json.loads(next(ln for ln in fh if ln.startswith("{")))
 
 
-def main(out: str, cfg: str) -> None:
+def main(out: str, cfg: str, positions: bool = False) -> None:
     pre = cfg.lower()
     stats = _rows(os.path.join(out, "prof_trace", f"{pre}_kernel_stats.csv"))
     bench = _bench_line(out)
-    fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", f"{pre}_counter_collection.csv")))
-    write = _per_kernel(_rows(os.path.join(out, "prof_write", f"{pre}_counter_collection.csv")))
-    f_copy, w_copy = _copy_kib(fetch), _copy_kib(write)
-    f_scale, w_scale = (COPY_BYTES / 1024) / f_copy, (COPY_BYTES / 1024) / w_copy
-    f_k, nf = _kernel_kib(fetch)
-    w_k, nw = _kernel_kib(write)
-    fetch_b = f_k * 1024 * f_scale
-    write_b = w_k * 1024 * w_scale
-    main_row = next(r for r in stats if KERNEL in r["Name"])
+    # the kernel the bench line measures: with --positions, the instantiation that
+    # reads per-token tables (template flag true); the same-pattern copy in that
+    # run is the plain variant and is listed but not summarised
+    main_row = next(r for r in stats if KERNEL in r["Name"] and (not positions or ", true>" in r["Name"]))
     avg_us = float(main_row["AverageNs"]) / 1e3
     alg = bench["algorithmic_bytes"]
+    suffix = "_positions" if positions else ""
+    flag = " --positions" if positions else ""
+    have_pmc = all(os.path.exists(os.path.join(out, d, f"{pre}_counter_collection.csv"))
+                   for d in ("prof_fetch", "prof_write"))
 
     lines = [
-        f"# rocprofv3 summary: {KERNEL} on the {cfg} workload",
+        f"# rocprofv3 summary: {KERNEL} on the {cfg} workload{' (per-token re-anchoring)' if positions else ''}",
         "",
         f"workload: {bench['config']['workload']}",
         f"kernel source hash: {bench['kernel_source_hash']}",
@@ -86,7 +89,7 @@ def main(out: str, cfg: str) -> None:
         "## kernel trace (rocprofv3 --kernel-trace --stats)",
         "",
         f"command: rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o {pre} -- "
-        f"python3 bench.py --config {cfg} --steps 200 --warmup 20 --no-cpu",
+        f"python3 bench.py --config {cfg}{flag} --steps 200 --warmup 20 --no-cpu",
         "",
         "| kernel | calls | average us | min us | max us | share of GPU time |",
         "|---|---|---|---|---|---|",
@@ -97,33 +100,50 @@ def main(out: str, cfg: str) -> None:
                      f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines += [
         "",
+        f"summarised kernel: {main_row['Name'].split('(')[0]}",
         f"bench.py's own HIP-event figure for the same kernel in the same run: {bench['kernel_us']:.1f} us "
         f"(rocprofv3 average {avg_us:.1f} us).",
-        "",
-        "## HBM bytes (rocprofv3 --pmc, one counter per run)",
-        "",
-        f"commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write -o {pre} -- "
-        f"python3 bench.py --config {cfg} --steps 5 --warmup 1 --no-cpu",
-        "",
-        "| counter | plain 1 GiB copy (KiB/dispatch) | scale to bytes | kernel (KiB/dispatch, mean of n) | kernel bytes |",
-        "|---|---|---|---|---|",
-        f"| FETCH_SIZE | {f_copy:.0f} | x{f_scale:.3f} | {f_k:.0f} (n={nf}) | {fetch_b / 1e6:.1f} MB |",
-        f"| WRITE_SIZE | {w_copy:.0f} | x{w_scale:.3f} | {w_k:.0f} (n={nw}) | {write_b / 1e6:.1f} MB |",
-        "",
-        f"measured HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB; algorithmic: {alg / 1e6:.1f} MB "
-        f"(ratio {(fetch_b + write_b) / alg:.3f})",
-        f"measured bandwidth: {(fetch_b + write_b) / (avg_us * 1e-6) / 1e9:.0f} GB/s; algorithmic: "
-        f"{alg / (avg_us * 1e-6) / 1e9:.0f} GB/s of 8000 ({alg / (avg_us * 1e-6) / 8e12:.1%})",
+        f"algorithmic bytes per launch: {alg / 1e6:.1f} MB, {alg / (avg_us * 1e-6) / 1e9:.0f} GB/s at the rocprofv3 "
+        f"average ({alg / (avg_us * 1e-6) / 8e12:.1%} of 8000 GB/s)",
     ]
+    if have_pmc:
+        fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", f"{pre}_counter_collection.csv")))
+        write = _per_kernel(_rows(os.path.join(out, "prof_write", f"{pre}_counter_collection.csv")))
+        f_copy, w_copy = _copy_kib(fetch), _copy_kib(write)
+        f_scale, w_scale = (COPY_BYTES / 1024) / f_copy, (COPY_BYTES / 1024) / w_copy
+        f_k, nf = _kernel_kib(fetch)
+        w_k, nw = _kernel_kib(write)
+        fetch_b = f_k * 1024 * f_scale
+        write_b = w_k * 1024 * w_scale
+        lines += [
+            "",
+            "## HBM bytes (rocprofv3 --pmc, one counter per run)",
+            "",
+            f"commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write "
+            f"-o {pre} -- python3 bench.py --config {cfg}{flag} --steps 5 --warmup 1 --no-cpu",
+            "",
+            "| counter | plain 1 GiB copy (KiB/dispatch) | scale to bytes | kernel (KiB/dispatch, mean of n) "
+            "| kernel bytes |",
+            "|---|---|---|---|---|",
+            f"| FETCH_SIZE | {f_copy:.0f} | x{f_scale:.3f} | {f_k:.0f} (n={nf}) | {fetch_b / 1e6:.1f} MB |",
+            f"| WRITE_SIZE | {w_copy:.0f} | x{w_scale:.3f} | {w_k:.0f} (n={nw}) | {write_b / 1e6:.1f} MB |",
+            "",
+            f"measured HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB; algorithmic: {alg / 1e6:.1f} MB "
+            f"(ratio {(fetch_b + write_b) / alg:.3f})",
+            f"measured bandwidth: {(fetch_b + write_b) / (avg_us * 1e-6) / 1e9:.0f} GB/s; algorithmic: "
+            f"{alg / (avg_us * 1e-6) / 1e9:.0f} GB/s of 8000 ({alg / (avg_us * 1e-6) / 8e12:.1%})",
+        ]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"rehydrate_mfma_{cfg}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"rehydrate_mfma_{cfg}{suffix}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    with open(os.path.join(ROOT, "profiles", f"traffic_{cfg}.json"), "w") as fh:
-        json.dump({"kernel_source_hash": bench["kernel_source_hash"], "hbm_bytes_per_launch": fetch_b + write_b,
-                   "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
-                   "rocprof_avg_us": avg_us}, fh, indent=1)
+    if have_pmc and not positions:
+        with open(os.path.join(ROOT, "profiles", f"traffic_{cfg}.json"), "w") as fh:
+            json.dump({"kernel_source_hash": bench["kernel_source_hash"], "hbm_bytes_per_launch": fetch_b + write_b,
+                       "fetch_bytes": fetch_b, "write_bytes": write_b, "fetch_scale": f_scale, "write_scale": w_scale,
+                       "rocprof_avg_us": avg_us}, fh, indent=1)
     print("\n".join(lines))
 
 
 if __name__ == "__main__":
-    main(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else "C2")
+    args = [a for a in sys.argv[1:] if not a.startswith("--")]
+    main(args[0], args[1] if len(args) > 1 else "C2", positions="--positions" in sys.argv[1:])
