@@ -142,9 +142,11 @@ typedef struct kamera_chunk {
                                   block_table[s / page_size], offset s % page_size of the pool;
                                   NULL selects the dense destination                          */
   const int32_t* positions;    /* KAMERA_POSITIONS: DEVICE [T][3] int32 offsets (t, h, w) of each
-                                  token, |offset| < 2^31; read when the batch is uploaded; pair i
-                                  of token t turns by positions[t][section(i)] * theta_i.
-                                  Ignored without the flag                                    */
+                                  token, |offset| < 2^31; read on `stream` (stream-ordered, like
+                                  every device input) by the upload of the batch, which turns
+                                  them into a cos/sin table in the workspace; a plan relaunched
+                                  later does not read them again. Pair i of token t turns by
+                                  positions[t][section(i)] * theta_i. Ignored without the flag */
   int32_t slot0;               /* 0 <= slot0 < page_size                                       */
   int32_t num_factors;         /* 0 .. KAMERA_MAX_FACTORS                                      */
   kamera_factor factors[KAMERA_MAX_FACTORS];
@@ -200,7 +202,10 @@ kamera_status kamera_rehydrate(const kamera_layout* layout, const kamera_chunk* 
 /* Eq. 1 for a batch of chunks in one launch: each chunk has its own delta, patch flag,
  * factors and destination (dense rows, or pages of `pool`). Pool slots written by two
  * chunks of one batch are rejected (KAMERA_E_OVERLAP); dense destinations are the
- * caller's to keep disjoint. `pool` may be NULL when no chunk uses a block table. */
+ * caller's to keep disjoint, and so is every source row of an out-of-place chunk from
+ * every row the batch writes (only KAMERA_IN_PLACE reads and writes the same rows: each
+ * element is read, then written, by one lane). `pool` may be NULL when no chunk uses a
+ * block table. */
 kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera_chunk* chunks,
                                        int32_t num_chunks, const kamera_pool* pool,
                                        void* workspace, size_t workspace_bytes, void* stream);

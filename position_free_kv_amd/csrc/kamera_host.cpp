@@ -633,6 +633,10 @@ kamera_status kamera_relocate(const kamera_layout* layout, const kamera_pool* po
     if (slot0 < 0) return fail(KAMERA_E_PAGE, "slot0 < 0");
     const int64_t np = ((int64_t)slot0 % P + num_tokens + P - 1) / P;
     const int64_t first = slot0 / P;
+    // range first, so that an oversized request fails before the identity table is built
+    if (first + np > (int64_t)pool->num_pages)
+      return fail(KAMERA_E_PAGE, "rows [%d, %lld) outside the pool's %lld rows", slot0, (long long)slot0 + num_tokens,
+                  (long long)pool->num_pages * P);
     ident.resize((size_t)np);
     for (int64_t k = 0; k < np; ++k) ident[(size_t)k] = (int32_t)(first + k);
     block_table = ident.data();

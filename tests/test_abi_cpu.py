@@ -8,6 +8,8 @@ import ctypes
 import os
 import re
 
+import time
+
 import numpy as np
 import pytest
 
@@ -247,6 +249,13 @@ def test_relocate_validates_pages():
     name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, None, 0, 40, 5, WS, 0))   # needs 3 pages
     assert name == "KAMERA_E_PAGE"
     name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, np.array([0, 5]), 0, 20, 5, WS, 0))
+    assert name == "KAMERA_E_PAGE"
+    # dense rows (no table): the range is checked against the pool before any table is built,
+    # so the largest token count fails at once instead of allocating a table of 2^27 pages
+    t0 = time.perf_counter()
+    name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, None, 3, 2 ** 31 - 1, 5, WS, 0))
+    assert name == "KAMERA_E_PAGE" and time.perf_counter() - t0 < 1.0
+    name, _ = status_of(lambda: abi.relocate(gqa_layout(), pool, None, 32, 1, 5, WS, 0))   # row 32 of 32
     assert name == "KAMERA_E_PAGE"
 
 
