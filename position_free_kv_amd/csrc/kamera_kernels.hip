@@ -259,12 +259,18 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   };
 
   // The first tile's rows are requested before the per-task set-up (phase, V operands),
-  // so the set-up runs while they are in flight.
+  // so the set-up runs while they are in flight (tasks without prefetch, below, excepted).
   u32x4 cur[G::NI], nxt[G::NI], nxt2[G::NI];
   // Tasks without k-steps (rotation or copy only, e.g. sliding-window survivors) hold no V
   // operands or U rows, so they keep a second tile in flight ahead of the current one
   // without raising the kernel's register peak (survivors +1.4% measured).
   constexpr bool kDeep = NK == 0;
+  // One-slab tasks with two k-steps (the MLA rope band under the row factor and the band
+  // factor) request each tile's rows and U rows at the top of that tile, not one tile ahead:
+  // the 16 registers saved put the whole instantiation at <= 128 VGPRs, 4 waves per SIMD
+  // for every task of the batch instead of 3 (27-layer MLA batch 195.5 -> 194.8 us; with
+  // per-token offsets 201.1 -> 199.9 us).
+  constexpr bool kNoPf = NSLAB == 1 && NK == 2;
   auto load_rows = [&](int tile, u32x4 (&raw)[G::NI]) {
     // Rows past the chunk end load the last row instead (computed, never stored), so
     // no loaded value is merged with a default and the loads stay in flight.
@@ -284,16 +290,16 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
       }
     }
   };
-  load_rows(0, cur);
+  if (!kNoPf) load_rows(0, cur);
   if (kDeep && ntiles > 1) load_rows(1, nxt);
 
   // ---- rotation coefficients for the pairs this lane holds (MFMA layout): one set per
   // chunk (delta), or, for chunks with per-token offsets, the set of this lane's token,
-  // read from the batch's cos/sin table for every tile. Where registers allow (one slab,
-  // or one k-step) the next tile's set is loaded with the next tile's rows; otherwise at
-  // the top of its own tile.
+  // read from the batch's cos/sin table for every tile. Where the next tile's rows are
+  // prefetched and registers allow (one slab, or one k-step) the next tile's set is loaded
+  // with them; otherwise at the top of its own tile.
   const bool tok_phase = POS && rot != ROT_NONE && (ch.flags & 4u) != 0;
-  constexpr bool kPrefetchPhase = NSLAB == 1 || NK <= 1;
+  constexpr bool kPrefetchPhase = !kNoPf && (NSLAB == 1 || NK <= 1);
   float cs[NSLAB * 8], sn[NSLAB * 8], pcs[NSLAB * 8], psn[NSLAB * 8];
   auto load_phase = [&](int tile, float (&c_)[NSLAB * 8], float (&s_)[NSLAB * 8]) {
     if constexpr (POS) {  // tile-major table (phase_offset): step k of the tile is 1 KB
@@ -384,9 +390,12 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   };
 
 
-  load_u(0, ucur);
+  if (!kNoPf) load_u(0, ucur);
   for (int tile = 0; tile < ntiles; ++tile) {
-    if (kDeep) {
+    if (kNoPf) {
+      load_rows(tile, cur);
+      load_u(tile, ucur);
+    } else if (kDeep) {
       if (tile + 2 < ntiles) load_rows(tile + 2, nxt2);
       if (kPrefetchPhase && tok_phase && tile + 1 < ntiles) load_phase(tile + 1, pcs, psn);
     } else if (tile + 1 < ntiles) {
@@ -485,7 +494,7 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
         if (t < T) __builtin_nontemporal_store(out[i], (u32x4*)(dst + page_row(tt, t)));
       }
     }
-    if (tile + 1 < ntiles) {
+    if (!kNoPf && tile + 1 < ntiles) {
 #pragma unroll
       for (int i = 0; i < G::NI; ++i) cur[i] = nxt[i];
       if (kDeep) {
