@@ -12,9 +12,9 @@ constexpr int kBlockThreads = 256;           // generic and copy-in kernels
 // token block and the next block, so a workgroup's waves share U rows (4 heads)
 // and V rows (2 blocks) through the CU's caches; measured faster than 4 or 16.
 constexpr int kWavesPerBlock = 8;
-// One-slab variants with at most 2 k-steps (MLA rows, 64-wide heads) fit 3 waves per
-// SIMD; 4-wave workgroups let 3 of them share a CU (12 waves, against 8 with 8-wave
-// workgroups): measured 9% faster on the 27-layer MLA batch.
+// One-slab variants with at most 2 k-steps (MLA rows, 64-wide heads) stay within 128
+// VGPRs, 4 waves per SIMD; 4-wave workgroups let 4 of them share a CU (16 waves, against
+// 8 with 8-wave workgroups): measured 9% faster on the 27-layer MLA batch.
 constexpr int kWavesPerBlockNarrow = 4;
 constexpr int mfma_waves_per_block(int nslab, int nkmax) {
   return (nslab == 1 && nkmax <= 2) ? kWavesPerBlockNarrow : kWavesPerBlock;
