@@ -328,13 +328,36 @@ __global__ __launch_bounds__(kThreads) void dots_k(BuildArgs a, const double* x,
 // below 1e-14 (pass 1) or 1e-6 (pass 2) of its column's squared norm, which
 // CholeskyQR2 could not bring back to orthogonality. A rejection sets the flag
 // (pass 0 sets it, later passes can only add to it) and the CGS2 fallback runs.
-// 16 waves on a 32 x 32 grid: the trailing updates, not the step barriers, dominate.
+//
+// Blocked by 16 columns: wave 0 factors the diagonal block in registers (lane i holds
+// row i of the block; the pivot and the entries of column k are read with v_readlane,
+// so a pivot step costs no LDS round trip and no workgroup barrier), one thread per
+// row solves the panel below the block, and the workgroup updates the trailing
+// triangle: three barriers per block instead of two per pivot. Every pivot is still
+// the fully updated diagonal entry, so the breakdown test sees the values the
+// unblocked order would (up to rounding order). A pivot step is a chain of dependent
+// fp64 operations, so it is kept short: 1/sqrt(d) from v_rsq_f64 and two Newton steps
+// (relative error ~1 ulp; L[k][k] = d / sqrt(d), the column scaled by the product; a
+// pivot below 2^-1000, far under any useful scale, counts as a breakdown, which keeps the
+// estimate away from subnormal inputs), and no lane predication in the update (a lane's
+// entries above the diagonal take garbage and are never stored).
 constexpr int kCholThreads = 1024;
+constexpr int kCholB = 16;
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
   __shared__ double Ls[kBuildMaxSubspace][kBuildMaxSubspace + 1];
   __shared__ double dg[kBuildMaxSubspace];
+  __shared__ double dinv[kCholB];
   __shared__ double red[kCholThreads / 64];
+  __shared__ int bad_s;
   const int p = a.p;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double tr = 0.0;
   for (int i = threadIdx.x; i < p; i += blockDim.x) tr += a.bz[i * p + i];
   tr = block_sum(tr, red);
@@ -353,31 +376,83 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
       }
     }
   }
+  if (threadIdx.x == 0) bad_s = !(tr > 0.0) || !(tr < 1e300);
   __syncthreads();
-  int bad = !(tr > 0.0) || !(tr < 1e300);
-  for (int k = 0; k < p && !bad; ++k) {
-    const double d = Ls[k][k];
-    if (!(d > ratio * dg[k]) || !(d > 0.0) || !(d < 1e300)) {  // uniform: every thread reads the same pivot
-      bad = 1;
-      break;
-    }
-    const double rk = sqrt(d);
-    __syncthreads();  // the pivot is read before column k changes
-    for (int i = k + 1 + threadIdx.x; i < p; i += blockDim.x) Ls[i][k] /= rk;
-    if (threadIdx.x == 0) Ls[k][k] = rk;
-    __syncthreads();
-    // trailing lower triangle (i >= j > k); a 32 x 32 thread grid, no index division
-    for (int i = k + 1 + (threadIdx.x >> 5); i < p; i += kCholThreads / 32) {
-      const double lik = Ls[i][k];
+  for (int k0 = 0; k0 < p; k0 += kCholB) {
+    const int kb = min(kCholB, p - k0), k1 = k0 + kb;
+    if (wave == 0) {  // ---- diagonal block [k0, k1)^2 in registers
+      double r[kCholB];
 #pragma unroll
-      for (int jj = 0; jj < kBuildMaxSubspace; jj += 32) {  // independent entries: let them overlap
-        const int j = k + 1 + jj + (threadIdx.x & 31);
-        if (j <= i) Ls[i][j] = fma(-lik, Ls[j][k], Ls[i][j]);
+      for (int j = 0; j < kCholB; ++j) r[j] = (lane < kb && j <= lane) ? Ls[k0 + lane][k0 + j] : 0.0;
+      // Fully unrolled (register indices must be constants): steps past the block or
+      // after a rejected pivot are skipped by uniform conditions, never by a break.
+      int bad = bad_s;
+      const double dgl = lane < kb ? dg[k0 + lane] : 0.0;      // the block's original diagonal
+#pragma unroll
+      for (int k = 0; k < kCholB; ++k) {
+        if (!bad && k < kb) {                                   // uniform
+          const double d = readlane_f64(r[k], k);               // the pivot
+          if (!(d > ratio * readlane_f64(dgl, k)) || !(d > 0x1p-1000) || !(d < 1e300)) {
+            bad = 1;
+          } else {
+            double y = __builtin_amdgcn_rsq(d);                 // 1/sqrt(d), refined twice
+            y = y * fma(-0.5 * d * y, y, 1.5);
+            y = y * fma(-0.5 * d * y, y, 1.5);
+            const double lik = r[k] * y;                        // L[i][k] for the lanes below the pivot
+            r[k] = lane == k ? d * y : lik;
+#pragma unroll
+            for (int j = k + 1; j < kCholB; ++j)
+              if (j < kb) r[j] = fma(-lik, readlane_f64(r[k], j), r[j]);  // uniform condition
+          }
+        }
+      }
+      if (!bad) {
+#pragma unroll
+        for (int j = 0; j < kCholB; ++j)
+          if (lane < kb && j <= lane) Ls[k0 + lane][k0 + j] = r[j];
+        if (lane < kb) {
+          double djj = 0.0;
+#pragma unroll
+          for (int j = 0; j < kCholB; ++j) djj = j == lane ? r[j] : djj;
+          dinv[lane] = 1.0 / djj;
+        }
+      }
+      if (lane == 0) bad_s = bad;
+    }
+    __syncthreads();
+    if (bad_s) break;  // uniform
+    // ---- panel: rows i >= k1 of columns [k0, k1), L[i][K] = B[i][K] L_KK^-T, row by row
+    for (int i = k1 + threadIdx.x; i < p; i += blockDim.x) {
+      double x[kCholB];
+#pragma unroll
+      for (int j = 0; j < kCholB; ++j) {
+        if (j < kb) {  // uniform
+          double v = Ls[i][k0 + j];
+#pragma unroll
+          for (int l = 0; l < j; ++l) v = fma(-x[l], Ls[k0 + j][k0 + l], v);
+          x[j] = v * dinv[j];
+          Ls[i][k0 + j] = x[j];
+        }
+      }
+    }
+    __syncthreads();
+    // ---- trailing triangle k1 <= j <= i < p: B[i][j] -= L[i][K] . L[j][K]
+    for (int i = k1 + (threadIdx.x >> 5); i < p; i += kCholThreads / 32) {
+#pragma unroll
+      for (int jj = 0; jj < kBuildMaxSubspace; jj += 32) {
+        const int j = k1 + jj + (threadIdx.x & 31);
+        if (j <= i) {  // the block's 16 products unrolled: their loads are independent
+          double v = Ls[i][j];
+#pragma unroll
+          for (int l = 0; l < kCholB; ++l)
+            if (l < kb) v = fma(-Ls[i][k0 + l], Ls[j][k0 + l], v);
+          Ls[i][j] = v;
+        }
       }
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) *a.flag = pass == 0 ? bad : (*a.flag | bad);
+  if (threadIdx.x == 0) *a.flag = pass == 0 ? bad_s : (*a.flag | bad_s);
   for (int r0 = 0; r0 < p; r0 += kCholThreads / 32) {  // lower triangle; the upper part is never read
     const int r = r0 + (threadIdx.x >> 5);
 #pragma unroll
@@ -394,12 +469,6 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
 // L is kept transposed in LDS so the lanes read a contiguous row of it. All of a
 // column is read before any of it is written, so src == dst is allowed.
 constexpr int kTrsmWaves = 8;
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
 
 __global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const double* src, double* dst) {
   __shared__ double Lt[kBuildMaxSubspace][kBuildMaxSubspace + 1];  // Lt[k][r] = L[r][k]
