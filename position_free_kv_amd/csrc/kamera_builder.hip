@@ -388,22 +388,23 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
       // after a rejected pivot are skipped by uniform conditions, never by a break.
       int bad = bad_s;
       const double dgl = lane < kb ? dg[k0 + lane] : 0.0;      // the block's original diagonal
+      // A rejected pivot only raises the flag (the block is discarded); the arithmetic goes
+      // on with a harmless value, so no step branches on it. Lanes at and past kb hold
+      // zeros and the entries they produce are never stored, so the updates need no guard.
 #pragma unroll
       for (int k = 0; k < kCholB; ++k) {
-        if (!bad && k < kb) {                                   // uniform
-          const double d = readlane_f64(r[k], k);               // the pivot
-          if (!(d > ratio * readlane_f64(dgl, k)) || !(d > 0x1p-1000) || !(d < 1e300)) {
-            bad = 1;
-          } else {
-            double y = __builtin_amdgcn_rsq(d);                 // 1/sqrt(d), refined twice
-            y = y * fma(-0.5 * d * y, y, 1.5);
-            y = y * fma(-0.5 * d * y, y, 1.5);
-            const double lik = r[k] * y;                        // L[i][k] for the lanes below the pivot
-            r[k] = lane == k ? d * y : lik;
+        if (k < kb) {                                           // uniform
+          const double d0 = readlane_f64(r[k], k);              // the pivot
+          const bool ok = d0 > ratio * readlane_f64(dgl, k) && d0 > 0x1p-1000 && d0 < 1e300;
+          bad |= !ok;
+          const double d = ok ? d0 : 1.0;
+          double y = __builtin_amdgcn_rsq(d);                   // 1/sqrt(d), refined twice
+          y = y * fma(-0.5 * d * y, y, 1.5);
+          y = y * fma(-0.5 * d * y, y, 1.5);
+          const double lik = r[k] * y;                          // L[i][k] for the lanes below the pivot
+          r[k] = lane == k ? d * y : lik;
 #pragma unroll
-            for (int j = k + 1; j < kCholB; ++j)
-              if (j < kb) r[j] = fma(-lik, readlane_f64(r[k], j), r[j]);  // uniform condition
-          }
+          for (int j = k + 1; j < kCholB; ++j) r[j] = fma(-lik, readlane_f64(r[k], j), r[j]);
         }
       }
       if (!bad) {
