@@ -523,12 +523,20 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   // entries below 1e-17 ||H||_F are left alone: rounding noise of that size
   // reappears with every rotation, so chasing it would never end
   const double floor_abs = fmax(1e-17 * sqrt(block_sum(ss, red)), 1e-300);
+  // A round: wave 0 derives the rotations of the round's n/2 disjoint pairs; then one flat
+  // pass applies A <- J^T A J and E <- E J. The pairs split the rows and the columns alike,
+  // so the 2 x 2 blocks (row pair k, column pair l) partition A and a block's new values
+  // depend only on its own four entries and the two rotations: a thread reads and writes
+  // whole blocks, in place, and no entry is touched by two threads. E is updated by
+  // (row, pair) items. Two barriers per round; every lane of every wave has work.
+  const int np2 = n / 2, nblk = np2 * np2, nitems = nblk + p * np2;
+  const uint32_t inv_np2 = ((1u << 20) + np2 - 1) / np2;  // b / np2 = (b * inv_np2) >> 20, exact for b < 2^14
   for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
     __syncthreads();
     if (threadIdx.x == 0) rotated = 0;
     __syncthreads();
     for (int round = 0; round < n - 1; ++round) {
-      for (int k = threadIdx.x; k < n / 2; k += blockDim.x) {
+      for (int k = threadIdx.x; k < np2; k += blockDim.x) {
         int x, y;
         if (k == 0) {
           x = n - 1;
@@ -555,27 +563,28 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
         sn[k] = s;
       }
       __syncthreads();
-      // the waves take the pairs in turn; the 64 lanes of a wave walk the rows/columns
-      const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
-      for (int k = wv; k < n / 2; k += kJacobiThreads / 64) {  // A <- J^T A
-        if (qq[k] >= p || sn[k] == 0.0) continue;
-        const int lo = pp[k], hi = qq[k];
-        const double c = cs[k], s = sn[k];
-        for (int col = ln; col < p; col += 64) {
-          const double x = A[lo][col], y = A[hi][col];
-          A[lo][col] = c * x - s * y;
-          A[hi][col] = s * x + c * y;
-        }
-      }
-      __syncthreads();
-      for (int k = wv; k < n / 2; k += kJacobiThreads / 64) {  // A <- A J, E <- E J
-        if (qq[k] >= p || sn[k] == 0.0) continue;
-        const int lo = pp[k], hi = qq[k];
-        const double c = cs[k], s = sn[k];
-        for (int row = ln; row < p; row += 64) {
-          const double x = A[row][lo], y = A[row][hi];
-          A[row][lo] = c * x - s * y;
-          A[row][hi] = s * x + c * y;
+      for (int w = threadIdx.x; w < nitems; w += blockDim.x) {
+        if (w < nblk) {
+          const int k = (int)(((uint32_t)w * inv_np2) >> 20), l = w - k * np2;
+          const double sk = sn[k], sl = sn[l];
+          if (sk == 0.0 && sl == 0.0) continue;
+          const int pk = pp[k], qk = qq[k], pl = pp[l], ql = qq[l];
+          const bool hk = qk < p, hl = ql < p;  // a pair with the bye has one row / column
+          const double ck = cs[k], cl = cs[l];
+          const double x00 = A[pk][pl], x01 = hl ? A[pk][ql] : 0.0;
+          const double x10 = hk ? A[qk][pl] : 0.0, x11 = (hk && hl) ? A[qk][ql] : 0.0;
+          const double r00 = ck * x00 - sk * x10, r10 = sk * x00 + ck * x10;   // rows (pk, qk)
+          const double r01 = ck * x01 - sk * x11, r11 = sk * x01 + ck * x11;
+          A[pk][pl] = cl * r00 - sl * r01;                                     // columns (pl, ql)
+          if (hl) A[pk][ql] = sl * r00 + cl * r01;
+          if (hk) A[qk][pl] = cl * r10 - sl * r11;
+          if (hk && hl) A[qk][ql] = sl * r10 + cl * r11;
+        } else {
+          const int e = w - nblk, row = (int)(((uint32_t)e * inv_np2) >> 20), l = e - row * np2;
+          const double s = sn[l];
+          if (s == 0.0) continue;  // also every pair with the bye
+          const int lo = pp[l], hi = qq[l];
+          const double c = cs[l];
           const double u = E[row][lo], v = E[row][hi];
           E[row][lo] = c * u - s * v;
           E[row][hi] = s * u + c * v;
