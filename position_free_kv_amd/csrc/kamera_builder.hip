@@ -364,7 +364,8 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
   const double shift = pass == 0 ? 11.0 * ((double)a.W * p + (double)p * (p + 1)) * 0x1p-53 * tr : 0.0;
   const double ratio = pass == 0 ? 0.0 : (pass == 1 ? 1e-14 : 1e-6);
   // lower triangle only; 32 x 32 thread grid, loads unrolled so they overlap
-  for (int r0 = 0; r0 < p; r0 += kCholThreads / 32) {
+#pragma unroll
+  for (int r0 = 0; r0 < kBuildMaxSubspace; r0 += kCholThreads / 32) {
     const int r = r0 + (threadIdx.x >> 5);
 #pragma unroll
     for (int cc = 0; cc < kBuildMaxSubspace; cc += 32) {
@@ -467,29 +468,45 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
 // Q = L^-1 Z by forward substitution, one wave per column i of the block: lane l
 // holds rows l and l + 64. Step k takes the finished entry q_k from its lane
 // (v_readlane at a uniform index) and removes its contribution from the rows below;
-// L is kept transposed in LDS so the lanes read a contiguous row of it. All of a
-// column is read before any of it is written, so src == dst is allowed.
+// L is kept transposed in LDS so the lanes read a contiguous row of it. The LDS copy
+// holds only the strictly lower part (the diagonal enters through its reciprocals) and
+// zeros elsewhere, also past p, so the steps need no lane conditions and the loop is
+// unrolled over the largest p: the Lt reads are issued ahead of the dependency chain.
+// All of a column is read before any of it is written, so src == dst is allowed.
 constexpr int kTrsmWaves = 8;
 
 __global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const double* src, double* dst) {
-  __shared__ double Lt[kBuildMaxSubspace][kBuildMaxSubspace + 1];  // Lt[k][r] = L[r][k]
+  __shared__ double Lt[kBuildMaxSubspace][kBuildMaxSubspace + 1];  // Lt[k][r] = L[r][k], r > k
   __shared__ double inv[kBuildMaxSubspace];
   if (*a.flag) return;  // uniform: the fallback orthonormalises this block
   const int p = a.p, W = a.W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = wave; r < p; r += kTrsmWaves)
-    for (int k = lane; k < p; k += 64) Lt[k][r] = k <= r ? a.lf[r * p + k] : 0.0;
-  for (int r = threadIdx.x; r < p; r += blockDim.x) inv[r] = 1.0 / a.lf[r * p + r];
+  // compile-time trip counts: all of a thread's loads are in flight together (a runtime
+  // loop would wait for each load before the next)
+#pragma unroll
+  for (int rr = 0; rr < kBuildMaxSubspace; rr += kTrsmWaves) {
+    const int r = rr + wave;
+#pragma unroll
+    for (int kk = 0; kk < kBuildMaxSubspace + 64 - 1; kk += 64) {
+      const int k = kk + lane;
+      if (k < kBuildMaxSubspace) Lt[k][r] = (r < p && k < r) ? a.lf[r * p + k] : 0.0;
+    }
+  }
+  for (int r = threadIdx.x; r < kBuildMaxSubspace; r += blockDim.x) {
+    inv[r] = r < p ? 1.0 / a.lf[r * p + r] : 0.0;
+    Lt[r][kBuildMaxSubspace] = 0.0;  // the padding column: what lanes past the last row read
+  }
   __syncthreads();
   const int i = blockIdx.x * kTrsmWaves + wave;
   if (i >= W) return;  // uniform over the wave
-  const int r0 = lane, r1 = lane + 64;
+  const int r0 = lane, r1 = lane + 64, r1c = min(r1, kBuildMaxSubspace);
   double acc0 = r0 < p ? src[(int64_t)r0 * W + i] : 0.0;
   double acc1 = r1 < p ? src[(int64_t)r1 * W + i] : 0.0;
-  for (int k = 0; k < p; ++k) {
+#pragma unroll
+  for (int k = 0; k < kBuildMaxSubspace; ++k) {  // past p: q_k = 0 and the rows stay as they are
     const double qk = readlane_f64(k < 64 ? acc0 : acc1, k & 63) * inv[k];
-    if (r0 > k) acc0 = fma(-Lt[k][r0], qk, acc0);
-    if (r1 > k && r1 < p) acc1 = fma(-Lt[k][r1], qk, acc1);
+    acc0 = fma(-Lt[k][r0], qk, acc0);
+    acc1 = fma(-Lt[k][r1c], qk, acc1);
   }
   if (r0 < p) dst[(int64_t)r0 * W + i] = acc0 * inv[r0];
   if (r1 < p) dst[(int64_t)r1 * W + i] = acc1 * inv[r1];
