@@ -313,12 +313,20 @@ __global__ __launch_bounds__(kThreads) void dots_k(BuildArgs a, const double* x,
   const int lane = threadIdx.x & 63;
   if (e >= a.p * a.p) return;
   const int r = e / a.p, c = e % a.p;
+  // X X^T: entries (r, c) and (c, r) take the same products in the same order, so the
+  // wave of the upper one writes both and the other returns
+  const bool gram = x == y;
+  if (gram && c < r) return;  // uniform over the wave
   const double* xr = x + (int64_t)r * a.W;
   const double* yc = y + (int64_t)c * a.W;
   double s = 0.0;
-  for (int i = lane; i < a.W; i += 64) s = fma(xr[i], yc[i], s);
+#pragma unroll 8
+  for (int i = lane; i < a.W; i += 64) s = fma(xr[i], yc[i], s);  // unrolled: the loads overlap
   s = wave_sum(s);
-  if (lane == 0) out[e] = s;
+  if (lane == 0) {
+    out[e] = s;
+    if (gram) out[c * a.p + r] = s;
+  }
 }
 
 // Cholesky factor B = L L^T of the p x p Gram of a block (right-looking, in LDS).
@@ -331,9 +339,10 @@ __global__ __launch_bounds__(kThreads) void dots_k(BuildArgs a, const double* x,
 //
 // Blocked by 16 columns: wave 0 factors the diagonal block in registers (lane i holds
 // row i of the block; the pivot and the entries of column k are read with v_readlane,
-// so a pivot step costs no LDS round trip and no workgroup barrier), one thread per
-// row solves the panel below the block, and the workgroup updates the trailing
-// triangle: three barriers per block instead of two per pivot. Every pivot is still
+// so a pivot step costs no LDS round trip and no workgroup barrier) and carries up to 48
+// rows below it through the same eliminations (the panel; rows past the wave's 64 are
+// solved one per thread), then the workgroup updates the trailing triangle: two
+// barriers per block instead of two per pivot. Every pivot is still
 // the fully updated diagonal entry, so the breakdown test sees the values the
 // unblocked order would (up to rounding order). A pivot step is a chain of dependent
 // fp64 operations, so it is kept short: 1/sqrt(d) from v_rsq_f64 and two Newton steps
@@ -381,17 +390,21 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
   __syncthreads();
   for (int k0 = 0; k0 < p; k0 += kCholB) {
     const int kb = min(kCholB, p - k0), k1 = k0 + kb;
-    if (wave == 0) {  // ---- diagonal block [k0, k1)^2 in registers
+    if (wave == 0) {  // ---- columns [k0, k1) of rows k0 .. k0 + 63 in registers
+      // lane i holds row k0 + i: the diagonal block's rows (i < kb, lower part) and below
+      // them up to 48 panel rows, which the same eliminations turn into L[row][k0 .. k1)
       double r[kCholB];
+      const int row = k0 + lane;
 #pragma unroll
-      for (int j = 0; j < kCholB; ++j) r[j] = (lane < kb && j <= lane) ? Ls[k0 + lane][k0 + j] : 0.0;
+      for (int j = 0; j < kCholB; ++j) r[j] = (row < p && j < kb && (lane >= kb || j <= lane)) ? Ls[row][k0 + j] : 0.0;
       // Fully unrolled (register indices must be constants): steps past the block or
       // after a rejected pivot are skipped by uniform conditions, never by a break.
       int bad = bad_s;
       const double dgl = lane < kb ? dg[k0 + lane] : 0.0;      // the block's original diagonal
       // A rejected pivot only raises the flag (the block is discarded); the arithmetic goes
-      // on with a harmless value, so no step branches on it. Lanes at and past kb hold
-      // zeros and the entries they produce are never stored, so the updates need no guard.
+      // on with a harmless value, so no step branches on it. What a lane computes above its
+      // own diagonal or in columns at and past kb is never stored (rows past p hold zeros),
+      // so the updates need no guard.
 #pragma unroll
       for (int k = 0; k < kCholB; ++k) {
         if (k < kb) {                                           // uniform
@@ -411,7 +424,7 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
       if (!bad) {
 #pragma unroll
         for (int j = 0; j < kCholB; ++j)
-          if (lane < kb && j <= lane) Ls[k0 + lane][k0 + j] = r[j];
+          if (row < p && j < kb && (lane >= kb || j <= lane)) Ls[row][k0 + j] = r[j];
         if (lane < kb) {
           double djj = 0.0;
 #pragma unroll
@@ -423,8 +436,9 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
     }
     __syncthreads();
     if (bad_s) break;  // uniform
-    // ---- panel: rows i >= k1 of columns [k0, k1), L[i][K] = B[i][K] L_KK^-T, row by row
-    for (int i = k1 + threadIdx.x; i < p; i += blockDim.x) {
+    // ---- panel rows past wave 0's 64 (only with p > k0 + 64): L[i][K] = B[i][K] L_KK^-T, row by row
+    if (k0 + 64 < p) {  // uniform
+    for (int i = k0 + 64 + threadIdx.x; i < p; i += blockDim.x) {
       double x[kCholB];
 #pragma unroll
       for (int j = 0; j < kCholB; ++j) {
@@ -438,6 +452,7 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
       }
     }
     __syncthreads();
+    }
     // ---- trailing triangle k1 <= j <= i < p: B[i][j] -= L[i][K] . L[j][K]
     for (int i = k1 + (threadIdx.x >> 5); i < p; i += kCholThreads / 32) {
 #pragma unroll
