@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   __shared__ double cs[kBuildMaxSubspace / 2], sn[kBuildMaxSubspace / 2];
   __shared__ int pp[kBuildMaxSubspace / 2], qq[kBuildMaxSubspace / 2];
   __shared__ int order[kBuildMaxSubspace];
-  __shared__ int rotated;
+  __shared__ int rotated, rot_stamp;
   __shared__ double red[kJacobiThreads / 64];
   const int p = a.p;
   const int n = p + (p & 1);  // an even number of players; index p is a bye when p is odd
@@ -563,11 +563,17 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   // (row, pair) items. Two barriers per round; every lane of every wave has work.
   const int np2 = n / 2, nblk = np2 * np2, nitems = nblk + p * np2;
   const uint32_t inv_np2 = ((1u << 20) + np2 - 1) / np2;  // b / np2 = (b * inv_np2) >> 20, exact for b < 2^14
+  if (threadIdx.x == 0) rot_stamp = 0;  // published by the first sweep's barriers
   for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
     __syncthreads();
     if (threadIdx.x == 0) rotated = 0;
     __syncthreads();
     for (int round = 0; round < n - 1; ++round) {
+      // A round that turns no pair skips its pass. The rotating pairs write the round's own
+      // stamp: a later round can overwrite it only after every thread has read it (a round
+      // that turns something has a second barrier), and in a round that turns nothing any
+      // value seen differs from the round's stamp, so no reset (and no race on one) is needed.
+      const int stamp = sweep * n + round + 1;
       for (int k = threadIdx.x; k < np2; k += blockDim.x) {
         int x, y;
         if (k == 0) {
@@ -582,11 +588,20 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
         if (hi < p) {
           const double apq = A[lo][hi], app = A[lo][lo], aqq = A[hi][hi];
           if (fabs(apq) > floor_abs && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
-            const double th = (aqq - app) / (2.0 * apq);
-            const double t = fabs(th) > 1e150 ? 0.5 / th : (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(1.0 + th * th));
-            c = 1.0 / sqrt(1.0 + t * t);
-            s = t * c;
+            // t = tan of the rotation angle, the smaller root of t^2 + 2 th t - 1 = 0 with
+            // th = (aqq - app) / (2 apq), written without th: one square root, one division
+            // (the entries are Gram sums of bounded data, far below 1e154, so a^2 + b^2
+            // cannot overflow); c = 1/sqrt(1 + t^2) by v_rsq_f64 and two Newton steps
+            const double da = aqq - app, db = 2.0 * apq;
+            const double t = copysign(1.0, da) * db / (fabs(da) + sqrt(fma(da, da, db * db)));
+            const double u = fma(t, t, 1.0);
+            double y = __builtin_amdgcn_rsq(u);
+            y = y * fma(-0.5 * u * y, y, 1.5);
+            y = y * fma(-0.5 * u * y, y, 1.5);
+            c = y;
+            s = t * y;
             rotated = 1;
+            rot_stamp = stamp;
           }
         }
         pp[k] = lo;
@@ -595,6 +610,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
         sn[k] = s;
       }
       __syncthreads();
+      if (rot_stamp != stamp) continue;  // uniform: nothing turns this round
       for (int w = threadIdx.x; w < nitems; w += blockDim.x) {
         if (w < nblk) {
           const int k = (int)(((uint32_t)w * inv_np2) >> 20), l = w - k * np2;
