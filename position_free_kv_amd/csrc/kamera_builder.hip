@@ -11,10 +11,13 @@
 //   gram_k    G [W][W] (upper 32 x 32 tiles, mirrored)
 //   start_k   a deterministic pseudo-random start block Z0 [p][W]
 //   orthonormalisation of the block Z (p x W) into Q, once for the range
-//   finder and once per power step: shifted CholeskyQR3 (Fukaya, Kannan,
-//   Nakatsukasa, Yamamoto & Yanagisawa, SIAM J. Sci. Comput. 2020): a Cholesky
-//   QR pass on Z Z^T + sI, then two plain passes; each pass is B = X X^T
-//   (dots_k), B = L L^T (chol_k, one workgroup, LDS) and X <- L^-1 X (trsm_k).
+//   finder and once per power step: shifted CholeskyQR (Fukaya, Kannan,
+//   Nakatsukasa, Yamamoto & Yanagisawa, SIAM J. Sci. Comput. 2020), a Cholesky
+//   QR pass on Z Z^T + sI; the last one, whose Q enters the Rayleigh-Ritz step,
+//   adds two plain passes (shifted CholeskyQR3) for orthonormality to working
+//   precision, while the earlier ones only carry the span to the next product;
+//   each pass is B = X X^T (dots_k), B = L L^T (chol_k, one workgroup, LDS) and
+//   X <- L^-1 X (trsm_k).
 //   A block whose pivots collapse anyway (rank-deficient Z, e.g. Delta = 0)
 //   sets a flag and is orthonormalised by CGS2 instead (orth_k, one workgroup)
 //   zt_k      Z = Q G (rows of Q times the symmetric G)
@@ -735,18 +738,22 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(start_k, dim3(blocks_for((int64_t)a.p * a.W, kThreads)), blk, 0, st, a);
   const dim3 dgrid(blocks_for((int64_t)a.p * a.p, kThreads / 64));
   const dim3 tgrid(blocks_for(a.W, kTrsmWaves));
-  auto orthonormalise = [&]() {  // a.z -> a.q
+  // a.z -> a.q. Only the last orthonormalisation feeds the Rayleigh-Ritz step, which needs Q
+  // orthonormal to working precision: it takes all three passes. The earlier ones only carry
+  // the iterates' span (the same for any basis of it) to the next product and must keep that
+  // basis well conditioned, which the shifted pass alone does; they stop after it.
+  auto orthonormalise = [&](bool last) {
     hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.z, (const double*)a.z, a.bz);
     hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, 0);
     hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.z, a.q);
-    for (int pass = 1; pass <= 2; ++pass) {
+    for (int pass = 1; last && pass <= 2; ++pass) {
       hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.q, a.bz);
       hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, pass);
       hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.q, a.q);
     }
     hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
   };
-  orthonormalise();
+  orthonormalise(false);
   const dim3 zgrid(blocks_for(a.W, kZCols), a.ksplit);
   const dim3 rgrid(blocks_for((int64_t)a.p * a.W, kThreads));
   auto product = [&]() {  // a.z = a.q G
@@ -755,7 +762,7 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
   };
   for (int it = 0; it <= a.iters; ++it) {  // the range finder's product, then `iters` power steps
     product();
-    orthonormalise();
+    orthonormalise(it == a.iters);
   }
   product();
   hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.z, a.h);
