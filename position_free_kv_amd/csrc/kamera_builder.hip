@@ -537,6 +537,9 @@ __global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const dou
 // diagonal entries or against 1e-17 ||H||_F, and the sweeps stop once a whole
 // sweep skips every pair.
 constexpr int kJacobiThreads = 1024;
+// work items of a round at the largest p: the 2 x 2 blocks of A and the (row, pair) items of E
+constexpr int kJacobiItems = ((kBuildMaxSubspace / 2) * (kBuildMaxSubspace / 2) +
+                              kBuildMaxSubspace * (kBuildMaxSubspace / 2) + kJacobiThreads - 1) / kJacobiThreads;
 __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   __shared__ double A[kBuildMaxSubspace][kBuildMaxSubspace + 1];
   __shared__ double E[kBuildMaxSubspace][kBuildMaxSubspace + 1];
@@ -614,31 +617,36 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
       }
       __syncthreads();
       if (rot_stamp != stamp) continue;  // uniform: nothing turns this round
-      for (int w = threadIdx.x; w < nitems; w += blockDim.x) {
+      // a compile-time trip count (the largest p's items) so the items' LDS reads overlap
+#pragma unroll
+      for (int it = 0; it < kJacobiItems; ++it) {
+        const int w = threadIdx.x + it * kJacobiThreads;
         if (w < nblk) {
           const int k = (int)(((uint32_t)w * inv_np2) >> 20), l = w - k * np2;
           const double sk = sn[k], sl = sn[l];
-          if (sk == 0.0 && sl == 0.0) continue;
-          const int pk = pp[k], qk = qq[k], pl = pp[l], ql = qq[l];
-          const bool hk = qk < p, hl = ql < p;  // a pair with the bye has one row / column
-          const double ck = cs[k], cl = cs[l];
-          const double x00 = A[pk][pl], x01 = hl ? A[pk][ql] : 0.0;
-          const double x10 = hk ? A[qk][pl] : 0.0, x11 = (hk && hl) ? A[qk][ql] : 0.0;
-          const double r00 = ck * x00 - sk * x10, r10 = sk * x00 + ck * x10;   // rows (pk, qk)
-          const double r01 = ck * x01 - sk * x11, r11 = sk * x01 + ck * x11;
-          A[pk][pl] = cl * r00 - sl * r01;                                     // columns (pl, ql)
-          if (hl) A[pk][ql] = sl * r00 + cl * r01;
-          if (hk) A[qk][pl] = cl * r10 - sl * r11;
-          if (hk && hl) A[qk][ql] = sl * r10 + cl * r11;
-        } else {
+          if (sk != 0.0 || sl != 0.0) {
+            const int pk = pp[k], qk = qq[k], pl = pp[l], ql = qq[l];
+            const bool hk = qk < p, hl = ql < p;  // a pair with the bye has one row / column
+            const double ck = cs[k], cl = cs[l];
+            const double x00 = A[pk][pl], x01 = hl ? A[pk][ql] : 0.0;
+            const double x10 = hk ? A[qk][pl] : 0.0, x11 = (hk && hl) ? A[qk][ql] : 0.0;
+            const double r00 = ck * x00 - sk * x10, r10 = sk * x00 + ck * x10;   // rows (pk, qk)
+            const double r01 = ck * x01 - sk * x11, r11 = sk * x01 + ck * x11;
+            A[pk][pl] = cl * r00 - sl * r01;                                     // columns (pl, ql)
+            if (hl) A[pk][ql] = sl * r00 + cl * r01;
+            if (hk) A[qk][pl] = cl * r10 - sl * r11;
+            if (hk && hl) A[qk][ql] = sl * r10 + cl * r11;
+          }
+        } else if (w < nitems) {
           const int e = w - nblk, row = (int)(((uint32_t)e * inv_np2) >> 20), l = e - row * np2;
           const double s = sn[l];
-          if (s == 0.0) continue;  // also every pair with the bye
-          const int lo = pp[l], hi = qq[l];
-          const double c = cs[l];
-          const double u = E[row][lo], v = E[row][hi];
-          E[row][lo] = c * u - s * v;
-          E[row][hi] = s * u + c * v;
+          if (s != 0.0) {  // s == 0 also for every pair with the bye
+            const int lo = pp[l], hi = qq[l];
+            const double c = cs[l];
+            const double u = E[row][lo], v = E[row][hi];
+            E[row][lo] = c * u - s * v;
+            E[row][hi] = s * u + c * v;
+          }
         }
       }
       __syncthreads();
