@@ -45,7 +45,11 @@
  *     asynchronously; nothing is synchronised.
  *   - The library never allocates device memory. It keeps a small ring of
  *     pinned, device-mapped host staging buffers per device; a small copy-in
- *     kernel on `stream` moves each packed batch into the workspace.
+ *     kernel on `stream` moves each packed batch into the workspace. A one-shot
+ *     kamera_rehydrate_batched / kamera_rehydrate call on a small dense batch (at
+ *     most 11 chunks, none with a block table or KAMERA_POSITIONS) instead passes
+ *     the packed batch as the kernel's argument and leaves the workspace untouched
+ *     (it is still validated, so both routes accept the same arguments).
  *
  * Errors
  *   Every entry point returns a kamera_status. Arguments are validated on the

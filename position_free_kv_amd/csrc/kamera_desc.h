@@ -98,4 +98,14 @@ struct alignas(16) DevHeader {
   int32_t pad2;
 };
 
+// A small dense batch travels as a kernel argument instead: the dispatch carries the header
+// and up to kInlineChunks chunk records, so the call needs neither the staging copy nor the
+// copy-in kernel (batches with block tables or per-token tables still use the workspace).
+constexpr int kInlineChunks = 11;
+struct InlineBatch {
+  DevHeader hd;
+  DevChunk ch[kInlineChunks];
+};
+static_assert(sizeof(InlineBatch) <= 4096, "kernel arguments are limited to 4 KB");
+
 }  // namespace kamera

@@ -17,9 +17,9 @@
 
 namespace kamera {
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
-                       hipStream_t stream);
+                       hipStream_t stream, const InlineBatch* inl);
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
-                          hipStream_t stream);
+                          hipStream_t stream, const InlineBatch* inl);
 hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t max_entries,
                               hipStream_t stream);
@@ -164,6 +164,7 @@ struct Packed {
   int64_t phase_entries = 0;         // table entries (padded token, pair) of the batch
   int64_t phase_max = 0;             // the most entries of one chunk's table
   bool positions = false;
+  bool paged = false;                // a chunk writes through a block table
   int64_t tasks = 0;
   int kernel = 0;   // 0 none, 1 mfma, 2 generic
   int variant = 0;
@@ -361,6 +362,7 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   out.phase_entries = 0;
   out.phase_max = 0;
   out.positions = false;
+  out.paged = any_paged;
   for (int i = 0; i < n; ++i)
     if ((chunks[i].flags & KAMERA_POSITIONS) && chunks[i].num_tokens > 0) {
       out.phase_off[(size_t)i] = (int64_t)out.bytes;
@@ -554,6 +556,43 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
   return KAMERA_OK;
 }
 
+// Small dense batches (at most kInlineChunks chunks, no block tables, no per-token
+// tables): validated and packed as usual, then handed to the kernel as its argument, so
+// nothing is staged or copied in. Returns false when the batch does not qualify (the caller
+// then uploads it); otherwise the call's status is in *st.
+bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
+                   void* ws, size_t ws_size, void* stream, kamera_status* st_out) {
+  if (n < 1 || n > kInlineChunks || !chunks) return false;
+  for (int i = 0; i < n; ++i)
+    if (chunks[i].block_table || (chunks[i].flags & KAMERA_POSITIONS)) return false;
+  kamera_status& st_ret = *st_out;
+  thread_local std::vector<unsigned char> blob;
+  thread_local std::vector<int64_t> page_off;
+  thread_local std::vector<int64_t> phase_off;
+  Packed pk{blob, page_off, phase_off};
+  st_ret = pack_batch(L, chunks, n, pool, pk);
+  if (st_ret != KAMERA_OK) return true;
+  if (pk.paged || pk.positions) return false;
+  // the workspace is not used on this path, but the call's contract is the same on both
+  if (!ws) {
+    st_ret = fail(KAMERA_E_WORKSPACE, "workspace is NULL");
+  } else if (!aligned(ws, kAlign)) {
+    st_ret = fail(KAMERA_E_ALIGN, "workspace must be %zu-byte aligned", kAlign);
+  } else if (ws_size < pk.bytes) {
+    st_ret = fail(KAMERA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_size, pk.bytes);
+  }
+  if (st_ret != KAMERA_OK || pk.tasks == 0) return true;
+  InlineBatch b;
+  std::memset(&b, 0, sizeof(b));
+  std::memcpy(&b.hd, pk.blob.data(), sizeof(DevHeader));
+  std::memcpy(b.ch, pk.blob.data() + round_up(sizeof(DevHeader), kAlign), (size_t)n * sizeof(DevChunk));
+  hipError_t e;
+  if (pk.kernel == 1) e = launch_mfma(pk.variant, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);
+  else e = launch_generic(L->dtype, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);
+  if (e != hipSuccess) st_ret = fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -596,8 +635,9 @@ kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream) {
   const DevChunk* dc = reinterpret_cast<const DevChunk*>((const char*)plan->workspace +
                                                          round_up(sizeof(DevHeader), kAlign));
   hipError_t e;
-  if (plan->kernel == 1) e = launch_mfma(plan->variant, hd, dc, plan->num_tasks, (hipStream_t)stream);
-  else if (plan->kernel == 2) e = launch_generic(plan->reserved[0], hd, dc, plan->num_tasks, (hipStream_t)stream);
+  if (plan->kernel == 1) e = launch_mfma(plan->variant, hd, dc, plan->num_tasks, (hipStream_t)stream, nullptr);
+  else if (plan->kernel == 2)
+    e = launch_generic(plan->reserved[0], hd, dc, plan->num_tasks, (hipStream_t)stream, nullptr);
   else return fail(KAMERA_E_UNSUPPORTED, "plan names unknown kernel %d", plan->kernel);
   if (e != hipSuccess) return fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return KAMERA_OK;
@@ -606,6 +646,9 @@ kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream) {
 kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks,
                                        const kamera_pool* pool, void* workspace, size_t workspace_bytes,
                                        void* stream) {
+  g_last_error.clear();
+  kamera_status st0 = KAMERA_OK;
+  if (launch_inline(layout, chunks, num_chunks, pool, workspace, workspace_bytes, stream, &st0)) return st0;
   kamera_plan plan;
   kamera_status st = kamera_plan_upload(layout, chunks, num_chunks, pool, workspace, workspace_bytes, stream, &plan);
   if (st != KAMERA_OK) return st;

@@ -539,10 +539,9 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 }
 
 template <int NSLAB, int NKMAX, bool POS>
-__global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
-    const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
+__device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict__ hdr,
+                                                    const DevChunk* __restrict__ chunks, unsigned char* lds_all) {
   constexpr int kWaves = mfma_waves_per_block(NSLAB, NKMAX);
-  __shared__ __attribute__((aligned(16))) unsigned char lds_all[kWaves * Geo<NSLAB>::LDS];
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const DevHeader& hd = *hdr;
@@ -597,6 +596,23 @@ __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) v
                               lds_all + wave * Geo<NSLAB>::LDS);
 }
 
+// The batch description read from the workspace (plans, paged or re-anchored batches,
+// batches of more than kInlineChunks chunks) ...
+template <int NSLAB, int NKMAX, bool POS>
+__global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
+    const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
+  rehydrate_mfma_body<NSLAB, NKMAX, POS>(hdr, chunks, lds_all);
+}
+
+// ... or carried by the dispatch as the kernel's argument (small dense batches).
+template <int NSLAB, int NKMAX>
+__global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma_inline(
+    const InlineBatch batch) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
+  rehydrate_mfma_body<NSLAB, NKMAX, false>(&batch.hd, batch.ch, lds_all);
+}
+
 // ============================================================================
 // Generic path (fp32 or bf16, any even rotary width, any rank)
 // ============================================================================
@@ -627,9 +643,8 @@ __device__ __forceinline__ float add_patch(const DevChunk& ch, int layer, int te
 }
 
 template <typename T>
-__global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHeader* __restrict__ hdr,
-                                                                   const DevChunk* __restrict__ chunks) {
-  __shared__ float2 tab[256];
+__device__ __forceinline__ void rehydrate_generic_body(const DevHeader* __restrict__ hdr,
+                                                       const DevChunk* __restrict__ chunks, float2* tab) {
   const DevHeader& hd = *hdr;
   const int64_t task = blockIdx.x;
   if (task >= hd.total_tasks) return;  // uniform over the block
@@ -718,6 +733,19 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHead
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void rehydrate_generic(const DevHeader* __restrict__ hdr,
+                                                                   const DevChunk* __restrict__ chunks) {
+  __shared__ float2 tab[256];
+  rehydrate_generic_body<T>(hdr, chunks, tab);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void rehydrate_generic_inline(const InlineBatch batch) {
+  __shared__ float2 tab[256];
+  rehydrate_generic_body<T>(&batch.hd, batch.ch, tab);
+}
+
 // ============================================================================
 // Per-token cos/sin table of chunks with position offsets (QV-PIC Eq. 2: M-RoPE
 // applied with each token's own (t, h, w) position). Entry (t, i) of a chunk's
@@ -779,44 +807,58 @@ hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int 
   return hipGetLastError();
 }
 
+// `inl` non-null: the batch travels as the kernel argument (hdr and chunks unused)
 template <int NSLAB, int NKMAX, bool POS = false>
-static hipError_t launch_one(int64_t tasks, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks) {
+static hipError_t launch_one(int64_t tasks, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks,
+                             const InlineBatch* inl) {
   constexpr int w = mfma_waves_per_block(NSLAB, NKMAX);
   const int64_t blocks = (tasks + w - 1) / w;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0, stream,
-                     hdr, chunks);
+  if (inl == nullptr) {
+    hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0, stream,
+                       hdr, chunks);
+  } else if constexpr (!POS) {
+    hipLaunchKernelGGL((rehydrate_mfma_inline<NSLAB, NKMAX>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0,
+                       stream, *inl);
+  } else {
+    return hipErrorInvalidValue;  // per-token tables live in the workspace
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
-                       hipStream_t stream) {
+                       hipStream_t stream, const InlineBatch* inl) {
   if (tasks <= 0) return hipSuccess;
   switch (variant) {  // variant = (nslab - 1) * 4 + log2(nk_max)
-    case 0: return launch_one<1, 1>(tasks, stream, hdr, chunks);
-    case 1: return launch_one<1, 2>(tasks, stream, hdr, chunks);
-    case 2: return launch_one<1, 4>(tasks, stream, hdr, chunks);
-    case 3: return launch_one<1, 8>(tasks, stream, hdr, chunks);
-    case 4: return launch_one<2, 1>(tasks, stream, hdr, chunks);
-    case 5: return launch_one<2, 2>(tasks, stream, hdr, chunks);
-    case 6: return launch_one<2, 4>(tasks, stream, hdr, chunks);
+    case 0: return launch_one<1, 1>(tasks, stream, hdr, chunks, inl);
+    case 1: return launch_one<1, 2>(tasks, stream, hdr, chunks, inl);
+    case 2: return launch_one<1, 4>(tasks, stream, hdr, chunks, inl);
+    case 3: return launch_one<1, 8>(tasks, stream, hdr, chunks, inl);
+    case 4: return launch_one<2, 1>(tasks, stream, hdr, chunks, inl);
+    case 5: return launch_one<2, 2>(tasks, stream, hdr, chunks, inl);
+    case 6: return launch_one<2, 4>(tasks, stream, hdr, chunks, inl);
     // batches with per-token offsets (kVariantPositions + the variant above)
-    case 8: return launch_one<1, 1, true>(tasks, stream, hdr, chunks);
-    case 9: return launch_one<1, 2, true>(tasks, stream, hdr, chunks);
-    case 10: return launch_one<1, 4, true>(tasks, stream, hdr, chunks);
-    case 12: return launch_one<2, 1, true>(tasks, stream, hdr, chunks);
-    case 13: return launch_one<2, 2, true>(tasks, stream, hdr, chunks);
+    case 8: return launch_one<1, 1, true>(tasks, stream, hdr, chunks, inl);
+    case 9: return launch_one<1, 2, true>(tasks, stream, hdr, chunks, inl);
+    case 10: return launch_one<1, 4, true>(tasks, stream, hdr, chunks, inl);
+    case 12: return launch_one<2, 1, true>(tasks, stream, hdr, chunks, inl);
+    case 13: return launch_one<2, 2, true>(tasks, stream, hdr, chunks, inl);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
-                          hipStream_t stream) {
+                          hipStream_t stream, const InlineBatch* inl) {
   if (tasks <= 0) return hipSuccess;
   if (tasks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tasks), block(kBlockThreads);
-  if (dtype == 0) hipLaunchKernelGGL(rehydrate_generic<float>, grid, block, 0, stream, hdr, chunks);
-  else hipLaunchKernelGGL(rehydrate_generic<uint16_t>, grid, block, 0, stream, hdr, chunks);
+  if (inl != nullptr) {
+    if (dtype == 0) hipLaunchKernelGGL(rehydrate_generic_inline<float>, grid, block, 0, stream, *inl);
+    else hipLaunchKernelGGL(rehydrate_generic_inline<uint16_t>, grid, block, 0, stream, *inl);
+  } else {
+    if (dtype == 0) hipLaunchKernelGGL(rehydrate_generic<float>, grid, block, 0, stream, hdr, chunks);
+    else hipLaunchKernelGGL(rehydrate_generic<uint16_t>, grid, block, 0, stream, hdr, chunks);
+  }
   return hipGetLastError();
 }
 
