@@ -237,6 +237,22 @@ def test_partial_page_sharing_is_not_an_overlap():
     assert name == "KAMERA_E_OVERLAP", msg
 
 
+def test_kernel_argument_route_still_checks_the_workspace():
+    """A small dense batch is launched with the batch as the kernel's argument and the
+    workspace unused, yet the call's contract is the same as on the workspace route: the
+    workspace is checked (NULL, alignment, size) after the batch itself is validated."""
+    lay = gqa_layout()
+    name, _ = status_of(lambda: abi.rehydrate_batched(lay, [chunk()], None, (0, 1 << 20), 0))
+    assert name == "KAMERA_E_WORKSPACE"
+    name, _ = status_of(lambda: abi.rehydrate_batched(lay, [chunk()], None, (FAKE + 8, 1 << 20), 0))
+    assert name == "KAMERA_E_ALIGN"
+    need = abi.batch_workspace_bytes(lay, [chunk()])
+    name, msg = status_of(lambda: abi.rehydrate_batched(lay, [chunk()] * 3, None, (FAKE, need), 0))
+    assert name == "KAMERA_E_WORKSPACE" and "needed" in msg
+    name, _ = status_of(lambda: abi.rehydrate_batched(lay, [chunk(delta=1 << 31)], None, (0, 0), 0))
+    assert name == "KAMERA_E_DELTA"   # the batch is validated before the workspace
+
+
 def test_empty_batches_need_no_gpu():
     abi.rehydrate_batched(gqa_layout(), [], None, WS, 0)
     abi.rehydrate_batched(gqa_layout(), [chunk(num_tokens=0)], None, WS, 0)

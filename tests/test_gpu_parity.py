@@ -397,3 +397,37 @@ def test_plan_launch_in_a_captured_graph(positions):
         torch.cuda.synchronize()
         got = [t for buf in dw.dense for t in buf]
         assert all(torch.equal(a, b) for a, b in zip(eager, got)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("layout_kind,n", [("gqa128", 11), ("gqa128", 12), ("mla", 11), ("f32", 11), ("f32", 12)])
+def test_kernel_argument_route_boundary(layout_kind, n):
+    """One-shot calls on dense batches of up to 11 chunks pass the packed batch as the
+    kernel's argument; 12 chunks take the workspace. Both match the oracle, and a plan
+    (always the workspace route) relaunched on the same batch reproduces the call's bytes."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    say(f"[kernel-argument route] {layout_kind} chunks={n}")
+    T = [1, 16, 17, 33, 64, 90, 129, 5, 48, 70, 31, 15][:n]
+    deltas = [int(d) for d in np.random.default_rng(n).integers(-40000, 40000, size=n)]
+    if layout_kind == "mla":
+        lay = LayoutSpec(MLA, BF16, 2, latent_dim=512, rope_dim=64)
+        chunks = [ChunkSpec(index=i, num_tokens=T[i], delta=deltas[i], flags=PATCH, canon_id=i,
+                            factors=[factor(i, 0, 0, 0, 576, 32), factor(i, 1, 0, 512, 64, 16)], dst_buffer=i)
+                  for i in range(n)]
+    else:
+        dt = F32 if layout_kind == "f32" else BF16
+        lay = LayoutSpec(GQA, dt, 2, num_kv_heads=2, head_dim=128 if dt == BF16 else 64, rope_base=1e6)
+        chunks = gqa_chunks(n, T, deltas, 2, lay.head_dim, 16)
+    dw = DeviceWorkload(custom_workload(lay, chunks))
+    dw.workspace.fill_(0xA5)
+    dw.run()
+    torch.cuda.synchronize()
+    assert bool((dw.workspace == 0xA5).all()) == (n <= 11)   # the argument route writes no workspace
+    assert_parity(dw)
+    first = [t.clone() for buf in dw.dense for t in buf]
+    for buf in dw.dense:
+        for t in buf:
+            t.zero_()
+    abi.plan_launch(dw.plan())
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(first, [t for buf in dw.dense for t in buf]))
