@@ -47,7 +47,8 @@
  *     pinned, device-mapped host staging buffers per device; a small copy-in
  *     kernel on `stream` moves each packed batch into the workspace. A one-shot
  *     kamera_rehydrate_batched / kamera_rehydrate call on a small dense batch (at
- *     most 11 chunks, none with a block table or KAMERA_POSITIONS) instead passes
+ *     most 16 chunks, none with a block table or KAMERA_POSITIONS or with more than
+ *     two factors under KAMERA_PATCH) instead passes
  *     the packed batch as the kernel's argument and leaves the workspace untouched
  *     (it is still validated, so both routes accept the same arguments).
  *

@@ -99,13 +99,39 @@ struct alignas(16) DevHeader {
 };
 
 // A small dense batch travels as a kernel argument instead: the dispatch carries the header
-// and up to kInlineChunks chunk records, so the call needs neither the staging copy nor the
-// copy-in kernel (batches with block tables or per-token tables still use the workspace).
-constexpr int kInlineChunks = 11;
+// and up to kInlineChunks compact chunk records, so the call needs neither the staging copy
+// nor the copy-in kernel. Compact records hold what a dense chunk without per-token offsets
+// uses (no block table, no cos/sin table: both pointers are NULL) and at most kInlineFactors
+// factors; other batches use the workspace.
+constexpr int kInlineFactors = 2;
+struct DevChunkInline {
+  const void* src[2];
+  void* dst[2];
+  int64_t src_ls;
+  int64_t dst_ls;
+  int64_t delta;
+  int64_t task0;
+  int32_t T;
+  uint32_t flags;
+  int32_t slot0;
+  int32_t nfac;
+  int32_t ntb;
+  int32_t tb_tokens;
+  int32_t nstreams;
+  int32_t ngroups;
+  int32_t group0;
+  int32_t stream_tensor[2];
+  int32_t pad;
+  const int32_t* pages;  // always NULL here (dense destinations)
+  const float* phase;    // always NULL here (no per-token offsets)
+  DevFactor fac[kInlineFactors];
+};
+constexpr int kInlineChunks = 16;
 struct InlineBatch {
   DevHeader hd;
-  DevChunk ch[kInlineChunks];
+  DevChunkInline ch[kInlineChunks];
 };
-static_assert(sizeof(InlineBatch) <= 4096, "kernel arguments are limited to 4 KB");
+// kernel arguments, with the runtime's 256 bytes of implicit ones, stay within 4 KB
+static_assert(sizeof(InlineBatch) + 256 <= 4096, "kernel arguments are limited to 4 KB");
 
 }  // namespace kamera

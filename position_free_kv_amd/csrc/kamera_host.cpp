@@ -563,8 +563,11 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
 bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
                    void* ws, size_t ws_size, void* stream, kamera_status* st_out) {
   if (n < 1 || n > kInlineChunks || !chunks) return false;
-  for (int i = 0; i < n; ++i)
-    if (chunks[i].block_table || (chunks[i].flags & KAMERA_POSITIONS)) return false;
+  for (int i = 0; i < n; ++i) {
+    const kamera_chunk& c = chunks[i];
+    if (c.block_table || (c.flags & KAMERA_POSITIONS)) return false;
+    if ((c.flags & KAMERA_PATCH) && c.num_factors > kInlineFactors) return false;
+  }
   kamera_status& st_ret = *st_out;
   thread_local std::vector<unsigned char> blob;
   thread_local std::vector<int64_t> page_off;
@@ -585,7 +588,32 @@ bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n
   InlineBatch b;
   std::memset(&b, 0, sizeof(b));
   std::memcpy(&b.hd, pk.blob.data(), sizeof(DevHeader));
-  std::memcpy(b.ch, pk.blob.data() + round_up(sizeof(DevHeader), kAlign), (size_t)n * sizeof(DevChunk));
+  const DevChunk* dc = reinterpret_cast<const DevChunk*>(pk.blob.data() + round_up(sizeof(DevHeader), kAlign));
+  for (int i = 0; i < n; ++i) {  // the compact records: the fields the dense path reads
+    const DevChunk& d = dc[i];
+    DevChunkInline& e = b.ch[i];
+    for (int t = 0; t < 2; ++t) {
+      e.src[t] = d.src[t];
+      e.dst[t] = d.dst[t];
+      e.stream_tensor[t] = d.stream_tensor[t];
+    }
+    e.src_ls = d.src_ls;
+    e.dst_ls = d.dst_ls;
+    e.delta = d.delta;
+    e.task0 = d.task0;
+    e.T = d.T;
+    e.flags = d.flags;
+    e.slot0 = d.slot0;
+    e.nfac = d.nfac;
+    e.ntb = d.ntb;
+    e.tb_tokens = d.tb_tokens;
+    e.nstreams = d.nstreams;
+    e.ngroups = d.ngroups;
+    e.group0 = d.group0;
+    e.pages = nullptr;
+    e.phase = nullptr;
+    for (int f = 0; f < d.nfac; ++f) e.fac[f] = d.fac[f];  // nfac <= kInlineFactors (checked above)
+  }
   hipError_t e;
   if (pk.kernel == 1) e = launch_mfma(pk.variant, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);
   else e = launch_generic(L->dtype, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);

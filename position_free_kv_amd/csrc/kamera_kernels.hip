@@ -115,7 +115,8 @@ __device__ __forceinline__ int64_t phase_offset(const DevHeader& hd, int64_t t, 
   return (t >> 4) * 16 * hd.d_rot + ((k * 4 + lg) * 16 + (t & 15)) * 4 + 2 * (i & 1);
 }
 
-__device__ __forceinline__ int find_chunk(const DevChunk* __restrict__ chunks, int n, int64_t task) {
+template <typename C>  // the chunk record: DevChunk, or DevChunkInline for batches passed by value
+__device__ __forceinline__ int find_chunk(const C* __restrict__ chunks, int n, int64_t task) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -131,15 +132,15 @@ struct TaskCoord {
 // (chunk, layer, stream, token block, group) of a task:
 //   chunk-major:  task = task0 + ((stream * L + layer) * ntb + tb) * ngroups + g
 //   layer-major:  task = layer * layer_tasks + task0 + (stream * ntb + tb) * ngroups + g
-__device__ __forceinline__ TaskCoord decode_task(const DevHeader& hd, const DevChunk* __restrict__ chunks,
-                                                 int64_t task) {
+template <typename C>
+__device__ __forceinline__ TaskCoord decode_task(const DevHeader& hd, const C* __restrict__ chunks, int64_t task) {
   TaskCoord tc;
   int64_t r;
   if (hd.layer_tasks > 0) {
     tc.layer = (int)(task / hd.layer_tasks);
     const int64_t in_layer = task - (int64_t)tc.layer * hd.layer_tasks;
     tc.chunk = find_chunk(chunks, hd.nchunks, in_layer);
-    const DevChunk& ch = chunks[tc.chunk];
+    const C& ch = chunks[tc.chunk];
     r = in_layer - ch.task0;
     tc.g = ch.group0 + (int)(r % ch.ngroups);
     r /= ch.ngroups;
@@ -148,7 +149,7 @@ __device__ __forceinline__ TaskCoord decode_task(const DevHeader& hd, const DevC
     return tc;
   }
   tc.chunk = find_chunk(chunks, hd.nchunks, task);
-  const DevChunk& ch = chunks[tc.chunk];
+  const C& ch = chunks[tc.chunk];
   r = task - ch.task0;
   tc.g = ch.group0 + (int)(r % ch.ngroups);
   r /= ch.ngroups;
@@ -197,8 +198,8 @@ struct Geo {
   static constexpr int LDS = 16 * RS;          // bytes per wave
 };
 
-template <int NSLAB, int NK, bool POS>
-__device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& ch, int layer, int tensor,
+template <int NSLAB, int NK, bool POS, typename C>
+__device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int layer, int tensor,
                                           int colbase, int tok0, int ntiles, int rot, const int* kfac,
                                           const int* kstep, int lane, unsigned char* lds) {
   using G = Geo<NSLAB>;
@@ -514,14 +515,14 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const DevChunk& c
   }
 }
 
-template <int NSLAB, int NKMAX, bool POS>
-__device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const DevChunk& ch, int layer,
+template <int NSLAB, int NKMAX, bool POS, typename C>
+__device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const C& ch, int layer,
                                               int tensor, int colbase, int tok0, int ntiles, int rot,
                                               const int* kfac, const int* kstep, int lane, unsigned char* lds) {
 #define KAMERA_NK_CASE(N)                                                                                   \
   case N:                                                                                                  \
     if constexpr (N <= NKMAX)                                                                              \
-      mfma_task<NSLAB, N, POS>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds);  \
+      mfma_task<NSLAB, N, POS, C>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds); \
     break;
   switch (nk) {
     KAMERA_NK_CASE(0)
@@ -538,9 +539,9 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 #undef KAMERA_NK_CASE
 }
 
-template <int NSLAB, int NKMAX, bool POS>
-__device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict__ hdr,
-                                                    const DevChunk* __restrict__ chunks, unsigned char* lds_all) {
+template <int NSLAB, int NKMAX, bool POS, typename C>
+__device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict__ hdr, const C* __restrict__ chunks,
+                                                    unsigned char* lds_all) {
   constexpr int kWaves = mfma_waves_per_block(NSLAB, NKMAX);
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -564,7 +565,7 @@ __device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict_
   const int64_t task = blk * kWaves + wave;
   if (task >= hd.total_tasks) return;  // no workgroup barrier follows: waves are independent
   const TaskCoord tcd = decode_task(hd, chunks, task);
-  const DevChunk& ch = chunks[tcd.chunk];
+  const C& ch = chunks[tcd.chunk];
   const int g = tcd.g, tb = tcd.tb, layer = tcd.layer;
   const int tensor = ch.stream_tensor[tcd.stream];
   const int colbase = g * hd.group_cols;
@@ -592,7 +593,7 @@ __device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict_
     }
   }
   if ((ch.flags & 2u) && rot == ROT_NONE && nk == 0) return;  // in place and nothing changes
-  mfma_dispatch<NSLAB, NKMAX, POS>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
+  mfma_dispatch<NSLAB, NKMAX, POS, C>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
                               lds_all + wave * Geo<NSLAB>::LDS);
 }
 
@@ -602,7 +603,7 @@ template <int NSLAB, int NKMAX, bool POS>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
     const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
-  rehydrate_mfma_body<NSLAB, NKMAX, POS>(hdr, chunks, lds_all);
+  rehydrate_mfma_body<NSLAB, NKMAX, POS, DevChunk>(hdr, chunks, lds_all);
 }
 
 // ... or carried by the dispatch as the kernel's argument (small dense batches).
@@ -610,7 +611,7 @@ template <int NSLAB, int NKMAX>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma_inline(
     const InlineBatch batch) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
-  rehydrate_mfma_body<NSLAB, NKMAX, false>(&batch.hd, batch.ch, lds_all);
+  rehydrate_mfma_body<NSLAB, NKMAX, false, DevChunkInline>(&batch.hd, batch.ch, lds_all);
 }
 
 // ============================================================================
@@ -629,8 +630,8 @@ __device__ __forceinline__ void st<float>(void* p, int64_t i, float v) { ((float
 template <>
 __device__ __forceinline__ void st<uint16_t>(void* p, int64_t i, float v) { ((uint16_t*)p)[i] = f_to_bf(v); }
 
-template <typename T>
-__device__ __forceinline__ float add_patch(const DevChunk& ch, int layer, int tensor, int t, int col, float acc) {
+template <typename T, typename C>
+__device__ __forceinline__ float add_patch(const C& ch, int layer, int tensor, int t, int col, float acc) {
   for (int fi = 0; fi < ch.nfac; ++fi) {
     const DevFactor& f = ch.fac[fi];
     if (f.tensor != tensor || layer < f.layer0 || col < f.col0 || col >= f.col0 + f.width) continue;
@@ -642,14 +643,14 @@ __device__ __forceinline__ float add_patch(const DevChunk& ch, int layer, int te
   return acc;
 }
 
-template <typename T>
-__device__ __forceinline__ void rehydrate_generic_body(const DevHeader* __restrict__ hdr,
-                                                       const DevChunk* __restrict__ chunks, float2* tab) {
+template <typename T, typename C>
+__device__ __forceinline__ void rehydrate_generic_body(const DevHeader* __restrict__ hdr, const C* __restrict__ chunks,
+                                                       float2* tab) {
   const DevHeader& hd = *hdr;
   const int64_t task = blockIdx.x;
   if (task >= hd.total_tasks) return;  // uniform over the block
   const TaskCoord tcd = decode_task(hd, chunks, task);
-  const DevChunk& ch = chunks[tcd.chunk];
+  const C& ch = chunks[tcd.chunk];
   const int tb = tcd.tb, layer = tcd.layer;
   const int tensor = ch.stream_tensor[tcd.stream];
   const bool in_place = (ch.flags & 2u) != 0;

@@ -399,20 +399,29 @@ def test_plan_launch_in_a_captured_graph(positions):
         assert all(torch.equal(a, b) for a, b in zip(eager, got)), f"replay {rep}"
 
 
-@pytest.mark.parametrize("layout_kind,n", [("gqa128", 11), ("gqa128", 12), ("mla", 11), ("f32", 11), ("f32", 12)])
+@pytest.mark.parametrize("layout_kind,n", [("gqa128", 16), ("gqa128", 17), ("mla", 16), ("f32", 16), ("f32", 17),
+                                            ("three_factors", 2)])
 def test_kernel_argument_route_boundary(layout_kind, n):
-    """One-shot calls on dense batches of up to 11 chunks pass the packed batch as the
-    kernel's argument; 12 chunks take the workspace. Both match the oracle, and a plan
-    (always the workspace route) relaunched on the same batch reproduces the call's bytes."""
+    """One-shot calls on dense batches of up to 16 chunks with at most 2 factors each pass
+    the packed batch as the kernel's argument; 17 chunks, or a chunk with 3 factors, take the
+    workspace. Both routes match the oracle, and a plan (always the workspace route)
+    relaunched on the same batch reproduces the call's bytes."""
     from position_free_kv_amd import abi
     from workloads.device import DeviceWorkload
     say(f"[kernel-argument route] {layout_kind} chunks={n}")
-    T = [1, 16, 17, 33, 64, 90, 129, 5, 48, 70, 31, 15][:n]
+    T = [1, 16, 17, 33, 64, 90, 129, 5, 48, 70, 31, 15, 2, 100, 47, 80, 19][:n]
     deltas = [int(d) for d in np.random.default_rng(n).integers(-40000, 40000, size=n)]
+    by_argument = n <= 16 and layout_kind != "three_factors"
     if layout_kind == "mla":
         lay = LayoutSpec(MLA, BF16, 2, latent_dim=512, rope_dim=64)
         chunks = [ChunkSpec(index=i, num_tokens=T[i], delta=deltas[i], flags=PATCH, canon_id=i,
                             factors=[factor(i, 0, 0, 0, 576, 32), factor(i, 1, 0, 512, 64, 16)], dst_buffer=i)
+                  for i in range(n)]
+    elif layout_kind == "three_factors":
+        lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6)
+        chunks = [ChunkSpec(index=i, num_tokens=T[i] + 20, delta=deltas[i], flags=PATCH, canon_id=i,
+                            factors=[factor(i, 0, 0, 0, 256, 16), factor(i, 1, 1, 0, 256, 16),
+                                     factor(i, 2, 0, 128, 128, 8)], dst_buffer=i)
                   for i in range(n)]
     else:
         dt = F32 if layout_kind == "f32" else BF16
@@ -422,7 +431,7 @@ def test_kernel_argument_route_boundary(layout_kind, n):
     dw.workspace.fill_(0xA5)
     dw.run()
     torch.cuda.synchronize()
-    assert bool((dw.workspace == 0xA5).all()) == (n <= 11)   # the argument route writes no workspace
+    assert bool((dw.workspace == 0xA5).all()) == by_argument   # the argument route writes no workspace
     assert_parity(dw)
     first = [t.clone() for buf in dw.dense for t in buf]
     for buf in dw.dense:
