@@ -17,6 +17,7 @@ import gc
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,11 +39,20 @@ WORKLOADS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space: what the compiled kernels depend on."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Identity of the operator kernels' code (comments excluded), to tell whether stored
+    counter figures were taken on the code being run."""
     h = hashlib.sha256()
     for f in ("kamera_kernels.hip", "kamera_desc.h"):
-        with open(os.path.join(ROOT, "position_free_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "position_free_kv_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -597,8 +597,8 @@ __device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict_
                               lds_all + wave * Geo<NSLAB>::LDS);
 }
 
-// The batch description read from the workspace (plans, paged or re-anchored batches,
-// batches of more than kInlineChunks chunks) ...
+// The batch description read from the workspace (plans; paged or re-anchored batches;
+// batches of more than kInlineChunks chunks or with chunks of more than two factors) ...
 template <int NSLAB, int NKMAX, bool POS>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
     const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
