@@ -259,6 +259,34 @@ def abs_terms(x: np.ndarray, *, tensor: int, delta: int, rotate_this: bool, band
     return s_
 
 
+def angle_terms(x: np.ndarray, *, tensor: int, delta: int, rotate_this: bool, bands: Sequence[int],
+                d_rot: int, base: float, pairing: int, factors: Iterable[Factor] = (), patch: bool = True,
+                positions=None, sections: Sequence[int] = (0, 0, 0)) -> np.ndarray:
+    """A = (|a| + |b|) |phi| 2^-51 for both elements of every rotated pair, 0 elsewhere (fp64).
+
+    The angle phi = p theta_i is formed in fp64, which fixes it only to a few fp64 ulps of
+    |phi| (the product is rounded, and theta_i = base^(-2i/d_rot) from two correct fp64 pow
+    evaluations may differ by an ulp); 4 ulps, |phi| 2^-51, bound the difference of two such
+    evaluations, and a rotated output a c - b s or a s + b c moves by at most (|a| + |b|) |dphi|.
+    Same keywords as abs_terms (factors and patch do not enter).
+    """
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    A = np.zeros_like(ax)
+    if rotate_this:
+        th = inv_freq(d_rot, base)
+        if positions is not None:
+            pos = np.asarray(positions, dtype=np.int64).reshape(len(positions), -1)
+            phi = np.abs(pos[:, pair_sections(d_rot, sections)].astype(np.float64) * th[None, :])
+        else:
+            phi = np.abs(np.float64(delta) * th)[None, :]
+        p, q = pair_columns(d_rot, pairing)
+        for o in bands:
+            w = (ax[:, o + p] + ax[:, o + q]) * phi * 2.0 ** -51
+            A[:, o + p] = w
+            A[:, o + q] = w
+    return A
+
+
 # ----------------------------------------------------------------------------
 # Paged KV pool placement (KAMERA §6: the rebuilt KV is written into the pool)
 # ----------------------------------------------------------------------------

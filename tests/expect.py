@@ -13,7 +13,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 import oracle.kamera_oracle as O
-from workloads.configs import BF16, GQA, ChunkSpec, Workload
+from workloads.configs import BF16, GQA, POSITIONS, ChunkSpec, Workload
 
 
 @dataclass
@@ -23,6 +23,7 @@ class Expect:
     S: np.ndarray       # sum of |terms|
     n: int              # number of fp32 roundings allowed by the bound
     src: np.ndarray     # the stored input rows (storage dtype)
+    A: np.ndarray = None  # angle term of the bound (oracle.kamera_oracle.angle_terms)
 
 
 def source_rows(wl: Workload, ch: ChunkSpec, layer: int, tensor: int) -> np.ndarray:
@@ -58,12 +59,13 @@ def expect_block(wl: Workload, ch: ChunkSpec, layer: int, tensor: int,
     d_rot = O.rotary_width(lay.family, lay.head_dim, lay.rope_dim)
     rotate_this = tensor == 0          # K for GQA/MHA, the whole row for MLA
     pos = None
-    if ch.positions is not None:
+    if ch.positions is not None and ch.flags & POSITIONS:   # offsets without the flag are ignored
         pos = ch.positions if rows is None else ch.positions[np.asarray(rows)]
     kw = dict(tensor=tensor, delta=ch.delta, rotate_this=rotate_this, bands=bands, d_rot=d_rot,
               base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched, positions=pos,
               sections=lay.mrope_section)
     y = O.rehydrate_tensor(x, family=lay.family, **kw)
     S = O.abs_terms(x, **kw)
+    A = O.angle_terms(x, **kw)
     m_total = sum(f.u.shape[1] for f in facs if f.tensor == tensor) if ch.patched else 0
-    return Expect(y=y, r=O.round_to(y, lay.dtype), S=S, n=m_total + 4, src=src)
+    return Expect(y=y, r=O.round_to(y, lay.dtype), S=S, n=m_total + 4, src=src, A=A)

@@ -30,9 +30,9 @@ def compare(dw, ch: ChunkSpec, layer: int, tensor: int, rows: Optional[Sequence[
     e = expect_block(dw.wl, ch, layer, tensor, rows)
     g = dw.out_rows(ch, layer, tensor, rows)
     if dw.lay.dtype == BF16:
-        res = tol.check_bf16(g, e.y, e.r, e.S, e.n)
+        res = tol.check_bf16(g, e.y, e.r, e.S, e.n, e.A)
     else:
-        res = tol.check_f32(g, e.y, e.S, e.n)
+        res = tol.check_f32(g, e.y, e.S, e.n, e.A)
     res["where"] = (ch.index, layer, tensor)
     if res["fail"]:
         bad = np.argwhere(res["mask"])[:5]

@@ -178,3 +178,15 @@ def test_positions_plan_reuse_and_determinism():
         abi.plan_launch(plan)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(first, [t for buf in dw.dense for t in buf]))
+
+
+def test_offsets_without_the_flag_are_ignored():
+    """A chunk that hands over per-token offsets but not KAMERA_POSITIONS turns by its delta
+    (the offsets are ignored), on both call routes."""
+    say("[positions without the flag]")
+    for n in (2, 20):   # 2 chunks: kernel-argument route; 20: workspace route
+        lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6, mrope_section=(16, 24, 24))
+        chunks = [dataclasses.replace(c, positions=grid_positions(c.num_tokens, 5000 + 7 * c.index))
+                  for c in gqa_chunks(n, 40, [311 * (i + 1) for i in range(n)], 2, 128, 16)]
+        assert all(c.positions is not None and not c.flags & POSITIONS for c in chunks)
+        assert_parity(run_dw(custom_workload(lay, chunks)))

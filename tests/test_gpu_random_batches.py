@@ -1,7 +1,8 @@
 """Randomised parity: small batches drawn from a seeded generator, spanning the layout
 families (GQA with 64- and 128-wide heads, MLA, fp32), both pairings, 0 to 4 factors per
 chunk with assorted ranks, column ranges and first layers, chunk counts on both sides of the
-kernel-argument limit (16), empty chunks, deltas up to +-(2^31 - 1), and mixes of dense
+kernel-argument limit (16), empty chunks, deltas up to +-(2^31 - 1), per-token (t, h, w)
+offsets on some chunks (QV-PIC Eq. 2, under an M-RoPE section split), and mixes of dense
 destinations, paged destinations and in-place survivors. Every batch is compared with the
 oracle element by element (Kamera preprint Eq. 1; same bar as the other parity tests), and
 the pool slots no chunk owns must keep their sentinel.
@@ -11,7 +12,8 @@ import pytest
 import torch
 
 from tests.gpu_util import check_all, custom_workload, factor, pool_untouched_ok, say
-from workloads.configs import BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, ChunkSpec, LayoutSpec
+from workloads.configs import (BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, POSITIONS, ChunkSpec, LayoutSpec,
+                               mrope_sections)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,13 +34,16 @@ def draw_batch(seed: int):
     pairing = GPTJ if rng.random() < 0.3 else NEOX
     L = int(rng.integers(1, 4))
     P = 16
+    reanchor = rng.random() < 0.35   # some chunks turn token by token under an M-RoPE split
     if kind == "mla":
-        lay = LayoutSpec(MLA, BF16, L, latent_dim=512, rope_dim=64, pairing=pairing, page_size=P)
+        lay = LayoutSpec(MLA, BF16, L, latent_dim=512, rope_dim=64, pairing=pairing, page_size=P,
+                         mrope_section=(8, 12, 12) if reanchor else (0, 0, 0))
         tensors = [0]
     else:
         hd = 128 if kind == "gqa128" else 64
         lay = LayoutSpec(GQA, F32 if kind == "f32" else BF16, L, num_kv_heads=int(rng.integers(1, 5)), head_dim=hd,
-                         rope_base=float(rng.choice([1e4, 1e6])), pairing=pairing, page_size=P)
+                         rope_base=float(rng.choice([1e4, 1e6])), pairing=pairing, page_size=P,
+                         mrope_section=mrope_sections(hd) if reanchor else (0, 0, 0))
         tensors = [0, 1]
     F = lay.row_width
     n = int(rng.choice([1, 3, 8, 16, 17, 24]))
@@ -64,17 +69,24 @@ def draw_batch(seed: int):
                                layer0=int(rng.integers(0, L)) if rng.random() < 0.3 else 0))
         flags = PATCH if (facs and rng.random() < 0.85) else 0
         kw = dict(index=i, num_tokens=T, delta=delta, flags=flags, canon_id=i, factors=facs)
+        if reanchor and rng.random() < 0.5:
+            base = int(rng.integers(-70000, 70001))
+            pos = base + rng.integers(0, 4096, size=(T, 3))
+            if rng.random() < 0.2:
+                pos[: T // 2] = rng.integers(-(2 ** 31 - 1), 2 ** 31, size=(T // 2, 3))
+            kw.update(positions=np.ascontiguousarray(pos, dtype=np.int32), flags=flags | POSITIONS)
         if paged[i]:
             npg = -(-(slot0s[i] + T) // P)
             kw.update(block_table=pages[cursor:cursor + npg].copy(), slot0=slot0s[i])
             cursor += npg
             if rng.random() < 0.3:   # a survivor: the rows already in its pages turn in place
-                kw.update(flags=flags | IN_PLACE, role="survivor")
+                kw.update(flags=kw["flags"] | IN_PLACE, role="survivor")
         else:
             kw.update(dst_buffer=buf)
             buf += 1
         chunks.append(ChunkSpec(**kw))
-    desc = f"{kind} {'gptj' if pairing == GPTJ else 'neox'} L={L} chunks={n} paged={sum(paged)}"
+    npos = sum(c.positions is not None for c in chunks)
+    desc = f"{kind} {'gptj' if pairing == GPTJ else 'neox'} L={L} chunks={n} paged={sum(paged)} re-anchored={npos}"
     return custom_workload(lay, chunks, num_pages=num_pages if any(paged) else 0), desc
 
 

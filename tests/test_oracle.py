@@ -239,6 +239,36 @@ def test_orbit_pin_catches_planted_mistake(mutate):
 
 
 # ---------------------------------------------------------------- tolerance predicate
+def test_angle_term_bounds_the_fp64_angle_uncertainty():
+    """The tolerance's angle term A covers what an angle formed in fp64 leaves open: with
+    every theta_i moved by one fp64 ulp (two correct pow evaluations may differ so), the
+    rotated outputs at delta = 2^31 - 1 move by at most A, and by a visible share of it
+    (the bound is not vacuous). A vanishes where nothing turns."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((20, 128))
+    bands, d_rot, base = [0, 64], 64, 1e4
+    kw = dict(tensor=0, rotate_this=True, bands=bands, d_rot=d_rot, base=base, pairing=O.NEOX)
+    for delta in (2 ** 31 - 1, -(2 ** 31 - 1), 123457):
+        A = O.angle_terms(x, delta=delta, **kw)
+        y0 = O.rotate(x, delta, bands, d_rot, base, O.NEOX)
+        for direction in (np.inf, -np.inf):
+            th = np.nextafter(O.inv_freq(d_rot, base), direction)   # one ulp off, every pair
+            c, s = np.cos(np.float64(delta) * th), np.sin(np.float64(delta) * th)
+            y1 = np.array(x, copy=True)
+            p, q = O.pair_columns(d_rot, O.NEOX)
+            for o in bands:
+                y1[:, o + p] = x[:, o + p] * c - x[:, o + q] * s
+                y1[:, o + q] = x[:, o + p] * s + x[:, o + q] * c
+            moved = np.abs(y1 - y0)
+            assert np.all(moved <= A + 1e-15), (delta, float((moved - A).max()))
+            if abs(delta) > 2 ** 30:
+                assert moved.max() > 0.02 * A.max()
+    assert np.all(O.angle_terms(x, delta=0, **kw) == 0)
+    assert np.all(O.angle_terms(x, delta=5000, **dict(kw, rotate_this=False)) == 0)
+    uni = O.angle_terms(x, delta=0, positions=np.full((20, 3), 777), sections=(8, 12, 12), **kw)
+    assert np.array_equal(uni, O.angle_terms(x, delta=777, **kw))   # uniform offsets: the delta path
+
+
 def test_tolerance_predicate():
     y = np.array([1.0, -2.5, 3.0e-3, 100.0])
     r = O.round_bf16(y)

@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from position_free_kv_amd import abi
-from .configs import BF16, BF16_SENTINEL, F32_SENTINEL, GQA, ChunkSpec, Workload
+from .configs import BF16, BF16_SENTINEL, F32_SENTINEL, GQA, POSITIONS, ChunkSpec, Workload
 
 
 def _threads() -> int:
@@ -227,7 +227,7 @@ class DeviceWorkload:
                 total += L * 2 * T * cols * es
                 continue
             total += L * self.lay.num_tensors * 2 * T * F * es
-            if c.positions is not None:   # the (t, h, w) offsets, read once per chunk
+            if c.positions is not None and c.flags & POSITIONS:   # the (t, h, w) offsets, read once per chunk
                 total += T * 3 * 4
             if c.patched:
                 for f in c.factors:
