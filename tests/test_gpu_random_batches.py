@@ -17,7 +17,7 @@ from workloads.configs import (BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH,
 
 pytestmark = pytest.mark.gpu
 
-N_BATCHES = 32
+N_BATCHES = 64
 
 
 @pytest.fixture(scope="module", autouse=True)
