@@ -47,9 +47,9 @@
  *     pinned, device-mapped host staging buffers per device; a small copy-in
  *     kernel on `stream` moves each packed batch into the workspace. A one-shot
  *     kamera_rehydrate_batched / kamera_rehydrate call on a small dense batch (at
- *     most 16 chunks, none with a block table or KAMERA_POSITIONS or with more than
- *     two factors under KAMERA_PATCH) instead passes
- *     the packed batch as the kernel's argument and leaves the workspace untouched
+ *     most 16 chunks, none with a block table or with more than two factors under
+ *     KAMERA_PATCH) instead passes the packed batch as the kernels' argument; the
+ *     workspace then receives only the cos/sin tables of KAMERA_POSITIONS chunks
  *     (it is still validated, so both routes accept the same arguments).
  *
  * Errors

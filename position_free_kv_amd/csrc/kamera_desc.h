@@ -95,14 +95,14 @@ struct alignas(16) DevHeader {
   int32_t xcd_window_log2;  // MFMA path: log2 of the workgroups an XCD takes in a row (0: plain order)
   int64_t layer_tasks;  // > 0: layer-major task order, this many tasks per layer (task0 within a layer)
   int32_t mrope[3];     // rotary pairs following the t, h, w offsets (all 0: every pair follows t)
-  int32_t pad2;
+  int32_t phase_blocks; // per-token cos/sin table kernel: workgroups per chunk
 };
 
 // A small dense batch travels as a kernel argument instead: the dispatch carries the header
 // and up to kInlineChunks compact chunk records, so the call needs neither the staging copy
-// nor the copy-in kernel. Compact records hold what a dense chunk without per-token offsets
-// uses (no block table, no cos/sin table: both pointers are NULL) and at most kInlineFactors
-// factors; other batches use the workspace.
+// nor the copy-in kernel. Compact records hold what a dense chunk uses (no block table: that
+// pointer is NULL; per-token cos/sin tables still live in the workspace) and at most
+// kInlineFactors factors; other batches use the workspace.
 constexpr int kInlineFactors = 2;
 struct DevChunkInline {
   const void* src[2];
@@ -114,18 +114,20 @@ struct DevChunkInline {
   int32_t T;
   uint32_t flags;
   int32_t slot0;
-  int32_t nfac;
   int32_t ntb;
   int32_t tb_tokens;
-  int32_t nstreams;
-  int32_t ngroups;
-  int32_t group0;
-  int32_t stream_tensor[2];
-  int32_t pad;
-  const int32_t* pages;  // always NULL here (dense destinations)
-  const float* phase;    // always NULL here (no per-token offsets)
+  // small counts in 16 bits (column groups <= 2^20 / 64 by the layout checks)
+  int16_t nstreams;
+  int16_t ngroups;
+  int16_t group0;
+  int16_t stream_tensor[2];
+  int16_t nfac;
+  const int32_t* pages;      // always NULL here (dense destinations)
+  const int32_t* positions;  // per-token offsets (KAMERA_POSITIONS), caller's device memory
+  const float* phase;        // their cos/sin table in the workspace, or NULL
   DevFactor fac[kInlineFactors];
 };
+static_assert(sizeof(DevChunkInline) == 224, "compact chunk record layout");
 constexpr int kInlineChunks = 16;
 struct InlineBatch {
   DevHeader hd;

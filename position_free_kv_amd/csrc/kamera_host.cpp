@@ -21,8 +21,8 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
 hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunks, int64_t tasks,
                           hipStream_t stream, const InlineBatch* inl);
 hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
-hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t max_entries,
-                              hipStream_t stream);
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t per_chunk,
+                              hipStream_t stream, const InlineBatch* inl);
 }  // namespace kamera
 
 using namespace kamera;
@@ -163,6 +163,7 @@ struct Packed {
   size_t bytes = 0;                  // the whole workspace (tables included)
   int64_t phase_entries = 0;         // table entries (padded token, pair) of the batch
   int64_t phase_max = 0;             // the most entries of one chunk's table
+  int64_t phase_blocks = 0;          // table kernel: workgroups per chunk
   bool positions = false;
   bool paged = false;                // a chunk writes through a block table
   int64_t tasks = 0;
@@ -503,6 +504,8 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
     task *= L->num_layers;
   }
   hd->total_tasks = task;
+  out.phase_blocks = (out.phase_max + kBlockThreads - 1) / kBlockThreads;
+  hd->phase_blocks = (int32_t)std::min<int64_t>(out.phase_blocks, 0x7fffffff);  // the launcher rejects larger
   out.tasks = task;
   out.kernel = task == 0 ? 0 : (mfma ? 1 : 2);
   out.variant = 0;
@@ -542,7 +545,7 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
     if (pk.phase_entries > 0) {  // per-token cos/sin tables, computed once per upload
       const DevHeader* hd = reinterpret_cast<const DevHeader*>(ws);
       const DevChunk* dcd = reinterpret_cast<const DevChunk*>((const char*)ws + round_up(sizeof(DevHeader), kAlign));
-      const hipError_t e = launch_phase_table(hd, dcd, n, pk.phase_max, (hipStream_t)stream);
+      const hipError_t e = launch_phase_table(hd, dcd, n, pk.phase_blocks, (hipStream_t)stream, nullptr);
       if (e != hipSuccess) return fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
     }
   }
@@ -556,16 +559,17 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
   return KAMERA_OK;
 }
 
-// Small dense batches (at most kInlineChunks chunks, no block tables, no per-token
-// tables): validated and packed as usual, then handed to the kernel as its argument, so
-// nothing is staged or copied in. Returns false when the batch does not qualify (the caller
+// Small dense batches (at most kInlineChunks chunks, no block tables, at most
+// kInlineFactors factors each): validated and packed as usual, then handed to the kernels
+// as their argument, so nothing is staged or copied in (re-anchored chunks' cos/sin tables
+// are still computed into the workspace). Returns false when the batch does not qualify (the caller
 // then uploads it); otherwise the call's status is in *st.
 bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
                    void* ws, size_t ws_size, void* stream, kamera_status* st_out) {
   if (n < 1 || n > kInlineChunks || !chunks) return false;
   for (int i = 0; i < n; ++i) {
     const kamera_chunk& c = chunks[i];
-    if (c.block_table || (c.flags & KAMERA_POSITIONS)) return false;
+    if (c.block_table) return false;
     if ((c.flags & KAMERA_PATCH) && c.num_factors > kInlineFactors) return false;
   }
   kamera_status& st_ret = *st_out;
@@ -575,7 +579,7 @@ bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n
   Packed pk{blob, page_off, phase_off};
   st_ret = pack_batch(L, chunks, n, pool, pk);
   if (st_ret != KAMERA_OK) return true;
-  if (pk.paged || pk.positions) return false;
+  if (pk.paged) return false;
   // the workspace is not used on this path, but the call's contract is the same on both
   if (!ws) {
     st_ret = fail(KAMERA_E_WORKSPACE, "workspace is NULL");
@@ -595,7 +599,7 @@ bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n
     for (int t = 0; t < 2; ++t) {
       e.src[t] = d.src[t];
       e.dst[t] = d.dst[t];
-      e.stream_tensor[t] = d.stream_tensor[t];
+      e.stream_tensor[t] = (int16_t)d.stream_tensor[t];
     }
     e.src_ls = d.src_ls;
     e.dst_ls = d.dst_ls;
@@ -604,17 +608,25 @@ bool launch_inline(const kamera_layout* L, const kamera_chunk* chunks, int32_t n
     e.T = d.T;
     e.flags = d.flags;
     e.slot0 = d.slot0;
-    e.nfac = d.nfac;
+    e.nfac = (int16_t)d.nfac;              // <= kInlineFactors
     e.ntb = d.ntb;
     e.tb_tokens = d.tb_tokens;
-    e.nstreams = d.nstreams;
-    e.ngroups = d.ngroups;
-    e.group0 = d.group0;
+    e.nstreams = (int16_t)d.nstreams;      // 1 or 2
+    e.ngroups = (int16_t)d.ngroups;        // <= 2^20 / 64 (the row-width check)
+    e.group0 = (int16_t)d.group0;
     e.pages = nullptr;
-    e.phase = nullptr;
+    e.positions = d.positions;
+    e.phase = pk.phase_off[(size_t)i] < 0 ? nullptr
+                                         : reinterpret_cast<const float*>((char*)ws + pk.phase_off[(size_t)i]);
     for (int f = 0; f < d.nfac; ++f) e.fac[f] = d.fac[f];  // nfac <= kInlineFactors (checked above)
   }
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  if (pk.phase_entries > 0)  // per-token cos/sin tables into the workspace, from the same argument
+    e = launch_phase_table(nullptr, nullptr, n, pk.phase_blocks, (hipStream_t)stream, &b);
+  if (e != hipSuccess) {
+    st_ret = fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
+    return true;
+  }
   if (pk.kernel == 1) e = launch_mfma(pk.variant, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);
   else e = launch_generic(L->dtype, nullptr, nullptr, pk.tasks, (hipStream_t)stream, &b);
   if (e != hipSuccess) st_ret = fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));

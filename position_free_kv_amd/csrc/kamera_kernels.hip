@@ -607,11 +607,11 @@ __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) v
 }
 
 // ... or carried by the dispatch as the kernel's argument (small dense batches).
-template <int NSLAB, int NKMAX>
+template <int NSLAB, int NKMAX, bool POS>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma_inline(
     const InlineBatch batch) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
-  rehydrate_mfma_body<NSLAB, NKMAX, false, DevChunkInline>(&batch.hd, batch.ch, lds_all);
+  rehydrate_mfma_body<NSLAB, NKMAX, POS, DevChunkInline>(&batch.hd, batch.ch, lds_all);
 }
 
 // ============================================================================
@@ -755,12 +755,13 @@ __global__ __launch_bounds__(kBlockThreads) void rehydrate_generic_inline(const 
 // assigned to the t, h, w components in blocks of mrope[0], mrope[1], mrope[2]
 // pairs; all zero means every pair follows component t (1-D RoPE).
 // ============================================================================
-__global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __restrict__ hdr,
-                                                             const DevChunk* __restrict__ chunks, int blocks_per_chunk) {
-  __shared__ double theta[256];   // theta_i of the band's d_rot/2 <= 256 pairs, once per workgroup
+template <typename C>
+__device__ __forceinline__ void phase_table_body(const DevHeader* __restrict__ hdr, const C* __restrict__ chunks,
+                                                 double* theta) {
   const DevHeader& hd = *hdr;
+  const int blocks_per_chunk = hd.phase_blocks;
   // workgroup b covers entries [256 (b % blocks_per_chunk), ...) of chunk b / blocks_per_chunk
-  const DevChunk& ch = chunks[blockIdx.x / blocks_per_chunk];
+  const C& ch = chunks[blockIdx.x / blocks_per_chunk];
   const int np = hd.d_rot >> 1;
   const int64_t n_entries = ch.phase ? (int64_t)((ch.T + kTileTokens - 1) / kTileTokens) * kTileTokens * np : 0;
   const int64_t e = (int64_t)(blockIdx.x % blocks_per_chunk) * kBlockThreads + threadIdx.x;
@@ -775,6 +776,17 @@ __global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __
   float c, s;
   phase_at(theta[i], (int64_t)ch.positions[min(t, (int64_t)ch.T - 1) * 3 + comp], c, s);
   *(float2*)(ch.phase + phase_offset(hd, t, i)) = make_float2(c, s);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void phase_table(const DevHeader* __restrict__ hdr,
+                                                             const DevChunk* __restrict__ chunks) {
+  __shared__ double theta[256];   // theta_i of the band's d_rot/2 <= 256 pairs, once per workgroup
+  phase_table_body(hdr, chunks, theta);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void phase_table_inline(const InlineBatch batch) {
+  __shared__ double theta[256];
+  phase_table_body(&batch.hd, batch.ch, theta);
 }
 
 // ============================================================================
@@ -798,13 +810,17 @@ hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t max_entries,
-                              hipStream_t stream) {
-  if (max_entries <= 0 || nchunks <= 0) return hipSuccess;
-  const int64_t per_chunk = (max_entries + kBlockThreads - 1) / kBlockThreads;
-  if (per_chunk > 0x7fffffffLL || per_chunk * nchunks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(phase_table, dim3((unsigned)(per_chunk * nchunks)), dim3(kBlockThreads), 0, stream, hdr, chunks,
-                     (int)per_chunk);
+// per_chunk: the header's phase_blocks (workgroups per chunk), set by the host
+hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t per_chunk,
+                              hipStream_t stream, const InlineBatch* inl) {
+  if (per_chunk <= 0 || nchunks <= 0) return hipSuccess;
+  if (per_chunk * nchunks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (inl != nullptr)
+    hipLaunchKernelGGL(phase_table_inline, dim3((unsigned)(per_chunk * nchunks)), dim3(kBlockThreads), 0, stream,
+                       *inl);
+  else
+    hipLaunchKernelGGL(phase_table, dim3((unsigned)(per_chunk * nchunks)), dim3(kBlockThreads), 0, stream, hdr,
+                       chunks);
   return hipGetLastError();
 }
 
@@ -818,11 +834,9 @@ static hipError_t launch_one(int64_t tasks, hipStream_t stream, const DevHeader*
   if (inl == nullptr) {
     hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0, stream,
                        hdr, chunks);
-  } else if constexpr (!POS) {
-    hipLaunchKernelGGL((rehydrate_mfma_inline<NSLAB, NKMAX>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0,
-                       stream, *inl);
   } else {
-    return hipErrorInvalidValue;  // per-token tables live in the workspace
+    hipLaunchKernelGGL((rehydrate_mfma_inline<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0,
+                       stream, *inl);
   }
   return hipGetLastError();
 }

@@ -5,6 +5,8 @@ is within one bf16 step of the once-rounded fp64 result (P1) or within the fp32
 accumulation bound (P2); fp32 outputs meet P3. Indexing, untouched bytes and the
 identity case are bit-exact.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -400,12 +402,14 @@ def test_plan_launch_in_a_captured_graph(positions):
 
 
 @pytest.mark.parametrize("layout_kind,n", [("gqa128", 16), ("gqa128", 17), ("mla", 16), ("f32", 16), ("f32", 17),
-                                            ("three_factors", 2)])
+                                            ("three_factors", 2), ("positions", 16), ("positions", 17)])
 def test_kernel_argument_route_boundary(layout_kind, n):
     """One-shot calls on dense batches of up to 16 chunks with at most 2 factors each pass
     the packed batch as the kernel's argument; 17 chunks, or a chunk with 3 factors, take the
     workspace. Both routes match the oracle, and a plan (always the workspace route)
-    relaunched on the same batch reproduces the call's bytes."""
+    relaunched on the same batch reproduces the call's bytes. With per-token offsets the
+    argument route still computes the cos/sin tables into the workspace, but not the
+    packed batch at its start."""
     from position_free_kv_amd import abi
     from workloads.device import DeviceWorkload
     say(f"[kernel-argument route] {layout_kind} chunks={n}")
@@ -423,6 +427,11 @@ def test_kernel_argument_route_boundary(layout_kind, n):
                             factors=[factor(i, 0, 0, 0, 256, 16), factor(i, 1, 1, 0, 256, 16),
                                      factor(i, 2, 0, 128, 128, 8)], dst_buffer=i)
                   for i in range(n)]
+    elif layout_kind == "positions":
+        lay = LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6, mrope_section=(16, 24, 24))
+        chunks = [dataclasses.replace(c, positions=grid_positions(c.num_tokens, 300 * c.index - 2000),
+                                      flags=c.flags | POSITIONS) if c.index % 2 == 0 else c
+                  for c in gqa_chunks(n, T, deltas, 2, 128, 16)]
     else:
         dt = F32 if layout_kind == "f32" else BF16
         lay = LayoutSpec(GQA, dt, 2, num_kv_heads=2, head_dim=128 if dt == BF16 else 64, rope_base=1e6)
@@ -431,7 +440,9 @@ def test_kernel_argument_route_boundary(layout_kind, n):
     dw.workspace.fill_(0xA5)
     dw.run()
     torch.cuda.synchronize()
-    assert bool((dw.workspace == 0xA5).all()) == by_argument   # the argument route writes no workspace
+    # the argument route writes no packed batch (its header would sit at the workspace's start)
+    ws = dw.workspace if layout_kind != "positions" else dw.workspace[:256]
+    assert bool((ws == 0xA5).all()) == by_argument
     assert_parity(dw)
     first = [t.clone() for buf in dw.dense for t in buf]
     for buf in dw.dense:
