@@ -50,7 +50,11 @@
  *     most 16 chunks, none with a block table or with more than two factors under
  *     KAMERA_PATCH) instead passes the packed batch as the kernels' argument; the
  *     workspace then receives only the cos/sin tables of KAMERA_POSITIONS chunks
- *     (it is still validated, so both routes accept the same arguments).
+ *     (it is still validated, so both routes accept the same arguments). Such a
+ *     call makes no HIP call besides its kernel launches, so it may itself be
+ *     recorded in a captured graph; a call that stages its batch may not (a
+ *     replay would read a staging buffer that later calls reuse): record
+ *     kamera_plan_launch instead.
  *
  * Errors
  *   Every entry point returns a kamera_status. Arguments are validated on the
