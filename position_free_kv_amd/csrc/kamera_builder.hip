@@ -537,38 +537,75 @@ __global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const dou
 // diagonal entries or against 1e-17 ||H||_F, and the sweeps stop once a whole
 // sweep skips every pair.
 constexpr int kJacobiThreads = 1024;
-// work items of a round at the largest p: the 2 x 2 blocks of A and the (row, pair) items of E
-constexpr int kJacobiItems = ((kBuildMaxSubspace / 2) * (kBuildMaxSubspace / 2) +
-                              kBuildMaxSubspace * (kBuildMaxSubspace / 2) + kJacobiThreads - 1) / kJacobiThreads;
+constexpr int kJacobiPairs = kBuildMaxSubspace / 2;
+constexpr int kJacobiStride = kBuildMaxSubspace + 1;
+constexpr int kJacobiRows = 4;  // rows of E per work item
+static_assert(kJacobiPairs * (kJacobiPairs + 1) / 2 <= kJacobiThreads, "one block of A per thread");
+static_assert(kBuildMaxSubspace % kJacobiRows == 0 &&
+              kBuildMaxSubspace / kJacobiRows * kJacobiPairs <= kJacobiThreads, "one item of E per thread");
+
+// The two players of slot k in round r of the round-robin tournament of n players (n
+// even): slot 0 pits player n-1 against player r, slot k > 0 players r + k and r - k
+// modulo n - 1.
+__device__ __forceinline__ void tourney_pair(int n, int r, int k, int& lo, int& hi) {
+  int x = n - 1, y = r;
+  if (k != 0) {
+    x = r + k;
+    y = r + n - 1 - k;
+    if (x >= n - 1) x -= n - 1;  // both sums lie below 2 (n - 1)
+    if (y >= n - 1) y -= n - 1;
+  }
+  lo = min(x, y);
+  hi = max(x, y);
+}
+
 __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
-  __shared__ double A[kBuildMaxSubspace][kBuildMaxSubspace + 1];
-  __shared__ double E[kBuildMaxSubspace][kBuildMaxSubspace + 1];
-  __shared__ double cs[kBuildMaxSubspace / 2], sn[kBuildMaxSubspace / 2];
-  __shared__ int pp[kBuildMaxSubspace / 2], qq[kBuildMaxSubspace / 2];
+  // H is symmetric and so is every J^T H J: only the upper triangle of A (row <= column)
+  // is kept, entry (i, j) at (min(i, j), max(i, j)). Rows and columns past p (the bye, when
+  // p is odd, and the rows of E that fill the last item) hold zeros, which every rotation
+  // maps to zeros, so the items need no bounds tests.
+  __shared__ double A[kBuildMaxSubspace * kJacobiStride];
+  __shared__ double E[kBuildMaxSubspace * kJacobiStride];
+  __shared__ double2 rot[kJacobiPairs];  // (cos, sin) of the round's rotation in each slot
+  __shared__ int2 slot_pq[kJacobiPairs];  // the slot's two players (lo, hi)
   __shared__ int order[kBuildMaxSubspace];
   __shared__ int rotated, rot_stamp;
   __shared__ double red[kJacobiThreads / 64];
   const int p = a.p;
   const int n = p + (p & 1);  // an even number of players; index p is a bye when p is odd
+  auto at = [](int i, int j) { return min(i, j) * kJacobiStride + max(i, j); };
   double ss = 0.0;
-  for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
-    const int r = e / p, c = e % p;
-    const double v = 0.5 * (a.h[r * p + c] + a.h[c * p + r]);
-    A[r][c] = v;
-    E[r][c] = r == c ? 1.0 : 0.0;
+  for (int e = threadIdx.x; e < kBuildMaxSubspace * kJacobiStride; e += blockDim.x) {
+    const int r = e / kJacobiStride, c = e % kJacobiStride;
+    double v = 0.0;
+    if (r < p && c < p) v = 0.5 * (a.h[r * p + c] + a.h[c * p + r]);
+    A[e] = v;
+    E[e] = (r == c && r < p) ? 1.0 : 0.0;
     ss += v * v;
   }
   // entries below 1e-17 ||H||_F are left alone: rounding noise of that size
   // reappears with every rotation, so chasing it would never end
   const double floor_abs = fmax(1e-17 * sqrt(block_sum(ss, red)), 1e-300);
-  // A round: wave 0 derives the rotations of the round's n/2 disjoint pairs; then one flat
-  // pass applies A <- J^T A J and E <- E J. The pairs split the rows and the columns alike,
-  // so the 2 x 2 blocks (row pair k, column pair l) partition A and a block's new values
-  // depend only on its own four entries and the two rotations: a thread reads and writes
-  // whole blocks, in place, and no entry is touched by two threads. E is updated by
-  // (row, pair) items. Two barriers per round; every lane of every wave has work.
-  const int np2 = n / 2, nblk = np2 * np2, nitems = nblk + p * np2;
-  const uint32_t inv_np2 = ((1u << 20) + np2 - 1) / np2;  // b / np2 = (b * inv_np2) >> 20, exact for b < 2^14
+  // A round: wave 0 derives the rotations of the round's n/2 disjoint slots; then one flat
+  // pass applies A <- J^T A J and E <- E J. The slots split the rows and the columns alike,
+  // so the 2 x 2 blocks (row slot k, column slot l) partition A; a block's new values
+  // depend only on its own four entries and the two rotations, and block (l, k) is the
+  // transpose of block (k, l), so thread w < n/2 (n/2 + 1) / 2 takes block (k, l) with
+  // k <= l and w = l (l + 1) / 2 + k. Thread w < (rows / 4) n/2 takes rows 4 (w / (n/2)) to
+  // 4 (w / (n/2)) + 3 of E for slot w % (n/2). No entry is touched by two threads and every
+  // item runs without branches, so its LDS reads issue together. Two barriers per round.
+  const int np2 = n / 2, nblk = np2 * (np2 + 1) / 2;
+  const int nitem = (p + kJacobiRows - 1) / kJacobiRows * np2;
+  const int w = threadIdx.x;
+  int bk = 0, bl = 0;  // this thread's block of A
+  if (w < nblk) {      // the float root is off by at most one
+    int l = (int)((sqrtf((float)(8 * w + 1)) - 1.0f) * 0.5f);
+    if ((l + 1) * (l + 2) / 2 <= w) ++l;
+    if (l * (l + 1) / 2 > w) --l;
+    bk = w - l * (l + 1) / 2;
+    bl = l;
+  }
+  const int erow = w / max(np2, 1) * kJacobiRows, eslot = w % max(np2, 1);  // this thread's item of E
   if (threadIdx.x == 0) rot_stamp = 0;  // published by the first sweep's barriers
   for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
     __syncthreads();
@@ -581,18 +618,11 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
       // value seen differs from the round's stamp, so no reset (and no race on one) is needed.
       const int stamp = sweep * n + round + 1;
       for (int k = threadIdx.x; k < np2; k += blockDim.x) {
-        int x, y;
-        if (k == 0) {
-          x = n - 1;
-          y = round;
-        } else {
-          x = (round + k) % (n - 1);
-          y = (round + n - 1 - k) % (n - 1);
-        }
-        const int lo = min(x, y), hi = max(x, y);
+        int lo, hi;
+        tourney_pair(n, round, k, lo, hi);
         double c = 1.0, s = 0.0;
         if (hi < p) {
-          const double apq = A[lo][hi], app = A[lo][lo], aqq = A[hi][hi];
+          const double apq = A[at(lo, hi)], app = A[at(lo, lo)], aqq = A[at(hi, hi)];
           if (fabs(apq) > floor_abs && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
             // t = tan of the rotation angle, the smaller root of t^2 + 2 th t - 1 = 0 with
             // th = (aqq - app) / (2 apq), written without th: one square root, one division
@@ -610,43 +640,39 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
             rot_stamp = stamp;
           }
         }
-        pp[k] = lo;
-        qq[k] = hi;
-        cs[k] = c;
-        sn[k] = s;
+        rot[k] = make_double2(c, s);
+        slot_pq[k] = make_int2(lo, hi);
       }
       __syncthreads();
       if (rot_stamp != stamp) continue;  // uniform: nothing turns this round
-      // a compile-time trip count (the largest p's items) so the items' LDS reads overlap
+      if (w < nblk) {
+        // (a diagonal block, k == l, reads and writes its off-diagonal entry twice, as
+        // (pk, qk) and as (qk, pk); the second write holds the same value up to rounding)
+        const double2 rk = rot[bk], rl = rot[bl];
+        const int2 sk = slot_pq[bk], sl = slot_pq[bl];
+        const int pk = sk.x, qk = sk.y, pl = sl.x, ql = sl.y;
+        const int o00 = at(pk, pl), o01 = at(pk, ql), o10 = at(qk, pl), o11 = at(qk, ql);
+        const double x00 = A[o00], x01 = A[o01], x10 = A[o10], x11 = A[o11];
+        const double r00 = rk.x * x00 - rk.y * x10, r10 = rk.y * x00 + rk.x * x10;   // rows (pk, qk)
+        const double r01 = rk.x * x01 - rk.y * x11, r11 = rk.y * x01 + rk.x * x11;
+        A[o00] = rl.x * r00 - rl.y * r01;                                            // columns (pl, ql)
+        A[o01] = rl.y * r00 + rl.x * r01;
+        A[o10] = rl.x * r10 - rl.y * r11;
+        A[o11] = rl.y * r10 + rl.x * r11;
+      }
+      if (w < nitem) {
+        const double2 r = rot[eslot];
+        const int lo = slot_pq[eslot].x, hi = slot_pq[eslot].y;
+        double u[kJacobiRows], v[kJacobiRows];
 #pragma unroll
-      for (int it = 0; it < kJacobiItems; ++it) {
-        const int w = threadIdx.x + it * kJacobiThreads;
-        if (w < nblk) {
-          const int k = (int)(((uint32_t)w * inv_np2) >> 20), l = w - k * np2;
-          const double sk = sn[k], sl = sn[l];
-          if (sk != 0.0 || sl != 0.0) {
-            const int pk = pp[k], qk = qq[k], pl = pp[l], ql = qq[l];
-            const bool hk = qk < p, hl = ql < p;  // a pair with the bye has one row / column
-            const double ck = cs[k], cl = cs[l];
-            const double x00 = A[pk][pl], x01 = hl ? A[pk][ql] : 0.0;
-            const double x10 = hk ? A[qk][pl] : 0.0, x11 = (hk && hl) ? A[qk][ql] : 0.0;
-            const double r00 = ck * x00 - sk * x10, r10 = sk * x00 + ck * x10;   // rows (pk, qk)
-            const double r01 = ck * x01 - sk * x11, r11 = sk * x01 + ck * x11;
-            A[pk][pl] = cl * r00 - sl * r01;                                     // columns (pl, ql)
-            if (hl) A[pk][ql] = sl * r00 + cl * r01;
-            if (hk) A[qk][pl] = cl * r10 - sl * r11;
-            if (hk && hl) A[qk][ql] = sl * r10 + cl * r11;
-          }
-        } else if (w < nitems) {
-          const int e = w - nblk, row = (int)(((uint32_t)e * inv_np2) >> 20), l = e - row * np2;
-          const double s = sn[l];
-          if (s != 0.0) {  // s == 0 also for every pair with the bye
-            const int lo = pp[l], hi = qq[l];
-            const double c = cs[l];
-            const double u = E[row][lo], v = E[row][hi];
-            E[row][lo] = c * u - s * v;
-            E[row][hi] = s * u + c * v;
-          }
+        for (int i = 0; i < kJacobiRows; ++i) {
+          u[i] = E[(erow + i) * kJacobiStride + lo];
+          v[i] = E[(erow + i) * kJacobiStride + hi];
+        }
+#pragma unroll
+        for (int i = 0; i < kJacobiRows; ++i) {
+          E[(erow + i) * kJacobiStride + lo] = r.x * u[i] - r.y * v[i];
+          E[(erow + i) * kJacobiStride + hi] = r.y * u[i] + r.x * v[i];
         }
       }
       __syncthreads();
@@ -657,15 +683,15 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   for (int i = threadIdx.x; i < p; i += blockDim.x) {  // rank by eigenvalue, descending; ties by index
     int rank = 0;
     for (int j = 0; j < p; ++j)
-      if (A[j][j] > A[i][i] || (A[j][j] == A[i][i] && j < i)) ++rank;
+      if (A[at(j, j)] > A[at(i, i)] || (A[at(j, j)] == A[at(i, i)] && j < i)) ++rank;
     order[rank] = i;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
     const int r = e / p, k = e % p;
-    a.evec[r * p + k] = E[r][order[k]];
+    a.evec[r * p + k] = E[r * kJacobiStride + order[k]];
   }
-  for (int k = threadIdx.x; k < p; k += blockDim.x) a.lam[k] = A[order[k]][order[k]];
+  for (int k = threadIdx.x; k < p; k += blockDim.x) a.lam[k] = A[at(order[k], order[k])];
 }
 
 // V_m[i][k] = sum_j Q[j][i] E[j][k]; sigma_k = sqrt(max(lambda_k, 0)).
