@@ -542,7 +542,7 @@ constexpr int kJacobiStride = kBuildMaxSubspace + 1;
 constexpr int kJacobiRows = 4;  // rows of E per work item
 static_assert(kJacobiPairs * (kJacobiPairs + 1) / 2 <= kJacobiThreads, "one block of A per thread");
 static_assert(kBuildMaxSubspace % kJacobiRows == 0 &&
-              kBuildMaxSubspace / kJacobiRows * kJacobiPairs <= kJacobiThreads, "one item of E per thread");
+              64 + kBuildMaxSubspace / kJacobiRows * kJacobiPairs <= kJacobiThreads, "one item of E per thread");
 
 // The two players of slot k in round r of the round-robin tournament of n players (n
 // even): slot 0 pits player n-1 against player r, slot k > 0 players r + k and r - k
@@ -566,8 +566,8 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   // maps to zeros, so the items need no bounds tests.
   __shared__ double A[kBuildMaxSubspace * kJacobiStride];
   __shared__ double E[kBuildMaxSubspace * kJacobiStride];
-  __shared__ double2 rot[kJacobiPairs];  // (cos, sin) of the round's rotation in each slot
-  __shared__ int2 slot_pq[kJacobiPairs];  // the slot's two players (lo, hi)
+  __shared__ double2 rot[2][kJacobiPairs];  // (cos, sin) of each slot, for rounds of either parity
+  __shared__ int2 slot_pq[2][kJacobiPairs];  // the slot's two players (lo, hi)
   __shared__ int order[kBuildMaxSubspace];
   __shared__ int rotated, rot_stamp;
   __shared__ double red[kJacobiThreads / 64];
@@ -586,17 +586,18 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
   // entries below 1e-17 ||H||_F are left alone: rounding noise of that size
   // reappears with every rotation, so chasing it would never end
   const double floor_abs = fmax(1e-17 * sqrt(block_sum(ss, red)), 1e-300);
-  // A round: wave 0 derives the rotations of the round's n/2 disjoint slots; then one flat
-  // pass applies A <- J^T A J and E <- E J. The slots split the rows and the columns alike,
-  // so the 2 x 2 blocks (row slot k, column slot l) partition A; a block's new values
-  // depend only on its own four entries and the two rotations, and block (l, k) is the
-  // transpose of block (k, l), so thread w < n/2 (n/2 + 1) / 2 takes block (k, l) with
-  // k <= l and w = l (l + 1) / 2 + k. Thread w < (rows / 4) n/2 takes rows 4 (w / (n/2)) to
-  // 4 (w / (n/2)) + 3 of E for slot w % (n/2). No entry is touched by two threads and every
+  // Round g: wave 0 derives the rotations of the round's n/2 disjoint slots while the other
+  // waves apply round g - 1's rotations to E (E <- E J; the rotations only read A); then
+  // one flat pass applies A <- J^T A J. The slots split the rows and the columns alike, so
+  // the 2 x 2 blocks (row slot k, column slot l) partition A; a block's new values depend
+  // only on its own four entries and the two rotations, and block (l, k) is the transpose
+  // of block (k, l), so thread w < n/2 (n/2 + 1) / 2 takes block (k, l) with k <= l and
+  // w = l (l + 1) / 2 + k. Thread 64 + v, v < (rows / 4) n/2, takes rows 4 (v / (n/2)) to
+  // 4 (v / (n/2)) + 3 of E for slot v % (n/2). No entry is touched by two threads and every
   // item runs without branches, so its LDS reads issue together. Two barriers per round.
   const int np2 = n / 2, nblk = np2 * (np2 + 1) / 2;
   const int nitem = (p + kJacobiRows - 1) / kJacobiRows * np2;
-  const int w = threadIdx.x;
+  const int w = threadIdx.x, v = threadIdx.x - 64;
   int bk = 0, bl = 0;  // this thread's block of A
   if (w < nblk) {      // the float root is off by at most one
     int l = (int)((sqrtf((float)(8 * w + 1)) - 1.0f) * 0.5f);
@@ -605,51 +606,82 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
     bk = w - l * (l + 1) / 2;
     bl = l;
   }
-  const int erow = w / max(np2, 1) * kJacobiRows, eslot = w % max(np2, 1);  // this thread's item of E
+  const bool has_e = v >= 0 && v < nitem;
+  const int erow = max(v, 0) / max(np2, 1) * kJacobiRows, eslot = max(v, 0) % max(np2, 1);  // its item of E
+  auto update_e = [&](int b) {  // E <- E J with the rotations recorded in buffer b
+    const double2 r = rot[b][eslot];
+    const int lo = slot_pq[b][eslot].x, hi = slot_pq[b][eslot].y;
+    double u[kJacobiRows], x[kJacobiRows];
+#pragma unroll
+    for (int i = 0; i < kJacobiRows; ++i) {
+      u[i] = E[(erow + i) * kJacobiStride + lo];
+      x[i] = E[(erow + i) * kJacobiStride + hi];
+    }
+#pragma unroll
+    for (int i = 0; i < kJacobiRows; ++i) {
+      E[(erow + i) * kJacobiStride + lo] = r.x * u[i] - r.y * x[i];
+      E[(erow + i) * kJacobiStride + hi] = r.y * u[i] + r.x * x[i];
+    }
+  };
+  bool pending = false;  // uniform: the last round turned, and E has yet to follow
+  int g = 0;             // rounds so far; the rotation buffers alternate with its parity
   if (threadIdx.x == 0) rot_stamp = 0;  // published by the first sweep's barriers
   for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
     __syncthreads();
     if (threadIdx.x == 0) rotated = 0;
     __syncthreads();
-    for (int round = 0; round < n - 1; ++round) {
+    for (int round = 0; round < n - 1; ++round, ++g) {
+      const int b = g & 1;
       // A round that turns no pair skips its pass. The rotating pairs write the round's own
       // stamp: a later round can overwrite it only after every thread has read it (a round
       // that turns something has a second barrier), and in a round that turns nothing any
       // value seen differs from the round's stamp, so no reset (and no race on one) is needed.
       const int stamp = sweep * n + round + 1;
-      for (int k = threadIdx.x; k < np2; k += blockDim.x) {
+      if (pending && has_e) update_e(b ^ 1);
+      for (int k = threadIdx.x; k < np2; k += blockDim.x) {  // k < n/2 <= 40: wave 0 only
         int lo, hi;
         tourney_pair(n, round, k, lo, hi);
-        double c = 1.0, s = 0.0;
-        if (hi < p) {
-          const double apq = A[at(lo, hi)], app = A[at(lo, lo)], aqq = A[at(hi, hi)];
-          if (fabs(apq) > floor_abs && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq))) {
-            // t = tan of the rotation angle, the smaller root of t^2 + 2 th t - 1 = 0 with
-            // th = (aqq - app) / (2 apq), written without th: one square root, one division
-            // (the entries are Gram sums of bounded data, far below 1e154, so a^2 + b^2
-            // cannot overflow); c = 1/sqrt(1 + t^2) by v_rsq_f64 and two Newton steps
-            const double da = aqq - app, db = 2.0 * apq;
-            const double t = copysign(1.0, da) * db / (fabs(da) + sqrt(fma(da, da, db * db)));
-            const double u = fma(t, t, 1.0);
-            double y = __builtin_amdgcn_rsq(u);
-            y = y * fma(-0.5 * u * y, y, 1.5);
-            y = y * fma(-0.5 * u * y, y, 1.5);
-            c = y;
-            s = t * y;
-            rotated = 1;
-            rot_stamp = stamp;
-          }
+        // the bye's row and column are zeros: apq = 0 never turns
+        const double apq = A[at(lo, hi)], app = A[at(lo, lo)], aqq = A[at(hi, hi)];
+        const bool turn = fabs(apq) > floor_abs && fabs(apq) > kBuildJacobiTol * sqrt(fabs(app * aqq));
+        // The rotation that zeroes apq, by two reciprocal square roots (v_rsq_f64 and two
+        // Newton steps each) in place of a square root and a division: with
+        // 1/r = 1/sqrt(da^2 + db^2), cos 2th = |da|/r and sin 2th = sign(da) db/r, so
+        // cos th = sqrt(h) with h = (1 + cos 2th)/2, and sin th = sin 2th/(2 cos th); the
+        // smaller angle, |th| <= pi/4. Computed without a branch (the test above runs
+        // beside it) and discarded when apq is below the thresholds. The entries are Gram
+        // sums of bounded data, so da^2 + db^2 neither overflows nor, when apq passes the
+        // floor, vanishes.
+        const double da = aqq - app, db = 2.0 * apq;
+        const double u = fma(da, da, db * db);
+        double r = __builtin_amdgcn_rsq(u);
+        r = r * fma(-0.5 * u * r, r, 1.5);
+        r = r * fma(-0.5 * u * r, r, 1.5);
+        const double h = fma(0.5 * fabs(da), r, 0.5);
+        double y = __builtin_amdgcn_rsq(h);
+        y = y * fma(-0.5 * h * y, y, 1.5);
+        y = y * fma(-0.5 * h * y, y, 1.5);
+        const double c = turn ? h * y : 1.0;
+        const double s = turn ? copysign(0.5, da) * db * r * y : 0.0;
+        if (turn) {
+          rotated = 1;
+          rot_stamp = stamp;
         }
-        rot[k] = make_double2(c, s);
-        slot_pq[k] = make_int2(lo, hi);
+        rot[b][k] = make_double2(c, s);
+        slot_pq[b][k] = make_int2(lo, hi);
       }
       __syncthreads();
-      if (rot_stamp != stamp) continue;  // uniform: nothing turns this round
+      // Buffer b ^ 1, read by the E items before this barrier, is next written in round
+      // g + 1, after it. A round that turns nothing skips its pass and its second barrier:
+      // a wave that reads the stamp late may then see round g + 1's, which differs from
+      // this round's as well.
+      pending = rot_stamp == stamp;
+      if (!pending) continue;
       if (w < nblk) {
         // (a diagonal block, k == l, reads and writes its off-diagonal entry twice, as
         // (pk, qk) and as (qk, pk); the second write holds the same value up to rounding)
-        const double2 rk = rot[bk], rl = rot[bl];
-        const int2 sk = slot_pq[bk], sl = slot_pq[bl];
+        const double2 rk = rot[b][bk], rl = rot[b][bl];
+        const int2 sk = slot_pq[b][bk], sl = slot_pq[b][bl];
         const int pk = sk.x, qk = sk.y, pl = sl.x, ql = sl.y;
         const int o00 = at(pk, pl), o01 = at(pk, ql), o10 = at(qk, pl), o11 = at(qk, ql);
         const double x00 = A[o00], x01 = A[o01], x10 = A[o10], x11 = A[o11];
@@ -660,25 +692,11 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_k(BuildArgs a) {
         A[o10] = rl.x * r10 - rl.y * r11;
         A[o11] = rl.y * r10 + rl.x * r11;
       }
-      if (w < nitem) {
-        const double2 r = rot[eslot];
-        const int lo = slot_pq[eslot].x, hi = slot_pq[eslot].y;
-        double u[kJacobiRows], v[kJacobiRows];
-#pragma unroll
-        for (int i = 0; i < kJacobiRows; ++i) {
-          u[i] = E[(erow + i) * kJacobiStride + lo];
-          v[i] = E[(erow + i) * kJacobiStride + hi];
-        }
-#pragma unroll
-        for (int i = 0; i < kJacobiRows; ++i) {
-          E[(erow + i) * kJacobiStride + lo] = r.x * u[i] - r.y * v[i];
-          E[(erow + i) * kJacobiStride + hi] = r.y * u[i] + r.x * v[i];
-        }
-      }
       __syncthreads();
     }
     if (!rotated) break;
   }
+  if (pending && has_e) update_e((g - 1) & 1);  // the last round's rotations
   __syncthreads();
   for (int i = threadIdx.x; i < p; i += blockDim.x) {  // rank by eigenvalue, descending; ties by index
     int rank = 0;
