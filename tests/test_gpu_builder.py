@@ -196,6 +196,18 @@ def test_exact_when_subspace_spans_everything():
     check_case(case, rank=32, iterations=0, sub_tol=1e-9, sig_tol=1e-9)
 
 
+@pytest.mark.parametrize("num_tokens,col0,width,rank", [(37, 0, 128, 16), (300, 40, 33, 33), (1, 0, 64, 1),
+                                                        (5, 7, 2, 2), (200, 0, 79, 24)])
+def test_exact_at_odd_and_tiny_subspaces(num_tokens, col0, width, rank):
+    """p = min(80, width, T) = 37, 33, 1, 2, 79: the block spans the row space, so the result is
+    the exact SVD; an odd p gives the eigensolver's round-robin tournament a bye (an empty
+    player), and p <= 2 leaves it one pair or none."""
+    case = BuilderCase(gqa(F32, 2, 64), tensor=0, num_tokens=num_tokens, delta=-77, col0=col0, width=width,
+                       spectrum="gaussian", seed=19 + num_tokens)
+    say(f"[builder] exact case T={num_tokens} width={width} (p={min(80, width, num_tokens)}) rank={rank}")
+    check_case(case, rank=rank, iterations=1, sub_tol=1e-9, sig_tol=1e-9)
+
+
 def test_flat_gaussian_spectrum():
     """No spectral gap: subspace iteration approaches the optimum more slowly (16 iterations, p = 80)."""
     case = BuilderCase(gqa(F32, 4, 128), tensor=0, num_tokens=1024, delta=321, col0=0, width=512,
