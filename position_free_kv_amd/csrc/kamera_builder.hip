@@ -408,21 +408,27 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
       // on with a harmless value, so no step branches on it. What a lane computes above its
       // own diagonal or in columns at and past kb is never stored (rows past p hold zeros),
       // so the updates need no guard.
+      auto pivot = [&](int k) {
+        const double d0 = readlane_f64(r[k], k);                // the pivot
+        const bool ok = d0 > ratio * readlane_f64(dgl, k) && d0 > 0x1p-1000 && d0 < 1e300;
+        bad |= !ok;
+        const double d = ok ? d0 : 1.0;
+        double y = __builtin_amdgcn_rsq(d);                     // 1/sqrt(d), refined twice
+        y = y * fma(-0.5 * d * y, y, 1.5);
+        y = y * fma(-0.5 * d * y, y, 1.5);
+        const double lik = r[k] * y;                            // L[i][k] for the lanes below the pivot
+        r[k] = lane == k ? d * y : lik;
 #pragma unroll
-      for (int k = 0; k < kCholB; ++k) {
-        if (k < kb) {                                           // uniform
-          const double d0 = readlane_f64(r[k], k);              // the pivot
-          const bool ok = d0 > ratio * readlane_f64(dgl, k) && d0 > 0x1p-1000 && d0 < 1e300;
-          bad |= !ok;
-          const double d = ok ? d0 : 1.0;
-          double y = __builtin_amdgcn_rsq(d);                   // 1/sqrt(d), refined twice
-          y = y * fma(-0.5 * d * y, y, 1.5);
-          y = y * fma(-0.5 * d * y, y, 1.5);
-          const double lik = r[k] * y;                          // L[i][k] for the lanes below the pivot
-          r[k] = lane == k ? d * y : lik;
+        for (int j = k + 1; j < kCholB; ++j) r[j] = fma(-lik, readlane_f64(r[k], j), r[j]);
+      };
+      if (kb == kCholB) {  // uniform: a full block runs as one straight line, so the compiler
+                           // can start each pivot while the previous one's updates issue
 #pragma unroll
-          for (int j = k + 1; j < kCholB; ++j) r[j] = fma(-lik, readlane_f64(r[k], j), r[j]);
-        }
+        for (int k = 0; k < kCholB; ++k) pivot(k);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kCholB; ++k)
+          if (k < kb) pivot(k);                                 // uniform
       }
       if (!bad) {
 #pragma unroll
