@@ -19,7 +19,8 @@
 //   each pass is B = X X^T (dots_k), B = L L^T (chol_k, one workgroup, LDS) and
 //   X <- L^-1 X (trsm_k).
 //   A block whose pivots collapse anyway (rank-deficient Z, e.g. Delta = 0)
-//   sets a flag and is orthonormalised by CGS2 instead (orth_k, one workgroup)
+//   sets a flag and is orthonormalised by CGS2 instead (by the first workgroup of
+//   the orthonormalisation's last trsm_k)
 //   zt_k      Z = Q G (rows of Q times the symmetric G)
 //   dots_k    H = Q Z^T = Q G Q^T (p x p)
 //   jacobi_k  eigenpairs of H: parallel cyclic Jacobi (Brent & Luk 1985
@@ -37,8 +38,6 @@ namespace kamera {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kOrthThreads = 1024;
-constexpr int kOrthWaves = kOrthThreads / 64;
 
 __device__ __forceinline__ double load_x(const void* p, int dtype, int64_t i) {
   if (dtype == 1) return (double)__uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
@@ -262,13 +261,10 @@ __global__ __launch_bounds__(kThreads) void zred_k(BuildArgs a) {
 // Q = rows of Z orthonormalised by classical Gram-Schmidt with one
 // re-orthogonalisation pass (CGS2). A row that is numerically in the span of
 // the previous ones (rank-deficient Delta, or Delta = 0) is replaced by a fresh
-// pseudo-random row and orthonormalised again.
-__global__ __launch_bounds__(kOrthThreads) void orth_k(BuildArgs a) {
-  __shared__ double red[kOrthWaves];
-  __shared__ double coef[kBuildMaxSubspace];
-  if (*a.flag == 0) return;  // Cholesky QR succeeded
+// pseudo-random row and orthonormalised again. Run by one whole workgroup.
+__device__ void cgs2_block(const BuildArgs& a, double* red, double* coef) {
   const int W = a.W, p = a.p;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int j = 0; j < p; ++j) {
     double* qj = a.q + (int64_t)j * W;
     for (int attempt = 0; attempt < 4; ++attempt) {
@@ -282,7 +278,7 @@ __global__ __launch_bounds__(kOrthThreads) void orth_k(BuildArgs a) {
       }
       n0 = block_sum(n0, red);  // its barriers also publish the row written above
       for (int pass = 0; pass < 2; ++pass) {
-        for (int k = wave; k < j; k += kOrthWaves) {
+        for (int k = wave; k < j; k += waves) {
           const double* qk = a.q + (int64_t)k * W;
           double d = 0.0;
           for (int i = lane; i < W; i += 64) d = fma(qk[i], qj[i], d);
@@ -499,12 +495,23 @@ __global__ __launch_bounds__(kCholThreads) void chol_k(BuildArgs a, int pass) {
 // All of a column is read before any of it is written, so src == dst is allowed.
 constexpr int kTrsmWaves = 8;
 
-__global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const double* src, double* dst) {
+// With `fallback` set (the last solve of an orthonormalisation) and the flag raised, the
+// first workgroup orthonormalises Z by CGS2 instead and the others return.
+__global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const double* src, double* dst,
+                                                        int fallback) {
   __shared__ double Lt[kBuildMaxSubspace][kBuildMaxSubspace + 1];  // Lt[k][r] = L[r][k], r > k
   __shared__ double inv[kBuildMaxSubspace];
-  if (*a.flag) return;  // uniform: the fallback orthonormalises this block
+  __shared__ double red[kTrsmWaves];
   const int p = a.p, W = a.W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The flag, L and this wave's column are requested together (one memory round trip,
+  // not three); the flag is only tested once they are in flight.
+  const int flagged = *a.flag;
+  const int i = blockIdx.x * kTrsmWaves + wave;
+  const int r0 = lane, r1 = lane + 64, r1c = min(r1, kBuildMaxSubspace);
+  const bool col = i < W;  // uniform over the wave
+  double acc0 = col && r0 < p ? src[(int64_t)r0 * W + i] : 0.0;
+  double acc1 = col && r1 < p ? src[(int64_t)r1 * W + i] : 0.0;
   // compile-time trip counts: all of a thread's loads are in flight together (a runtime
   // loop would wait for each load before the next)
 #pragma unroll
@@ -520,12 +527,12 @@ __global__ __launch_bounds__(kTrsmWaves * 64) void trsm_k(BuildArgs a, const dou
     inv[r] = r < p ? 1.0 / a.lf[r * p + r] : 0.0;
     Lt[r][kBuildMaxSubspace] = 0.0;  // the padding column: what lanes past the last row read
   }
+  if (flagged) {  // uniform over the workgroup
+    if (fallback && blockIdx.x == 0) cgs2_block(a, red, inv);  // inv: scratch for the CGS2 coefficients
+    return;
+  }
   __syncthreads();
-  const int i = blockIdx.x * kTrsmWaves + wave;
-  if (i >= W) return;  // uniform over the wave
-  const int r0 = lane, r1 = lane + 64, r1c = min(r1, kBuildMaxSubspace);
-  double acc0 = r0 < p ? src[(int64_t)r0 * W + i] : 0.0;
-  double acc1 = r1 < p ? src[(int64_t)r1 * W + i] : 0.0;
+  if (!col) return;     // uniform over the wave
 #pragma unroll
   for (int k = 0; k < kBuildMaxSubspace; ++k) {  // past p: q_k = 0 and the rows stay as they are
     const double qk = readlane_f64(k < 64 ? acc0 : acc1, k & 63) * inv[k];
@@ -803,13 +810,13 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
   auto orthonormalise = [&](bool last) {
     hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.z, (const double*)a.z, a.bz);
     hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, 0);
-    hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.z, a.q);
+    hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.z, a.q, last ? 0 : 1);
     for (int pass = 1; last && pass <= 2; ++pass) {
       hipLaunchKernelGGL(dots_k, dgrid, blk, 0, st, a, (const double*)a.q, (const double*)a.q, a.bz);
       hipLaunchKernelGGL(chol_k, dim3(1), dim3(kCholThreads), 0, st, a, pass);
-      hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.q, a.q);
+      hipLaunchKernelGGL(trsm_k, tgrid, dim3(kTrsmWaves * 64), 0, st, a, (const double*)a.q, a.q,
+                         pass == 2 ? 1 : 0);
     }
-    hipLaunchKernelGGL(orth_k, dim3(1), dim3(kOrthThreads), 0, st, a);
   };
   orthonormalise(false);
   const dim3 zgrid(blocks_for(a.W, kZCols), a.ksplit);
