@@ -152,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void delta_k(BuildArgs a) {
 
 // G = Delta^T Delta. One 32 x 32 tile (bi <= bj) per workgroup; the mirror tile is
 // written from the same sums, so G is exactly symmetric.
+static_assert(32 * 32 % kThreads == 0, "gram_k's staging covers a 32 x 32 tile exactly");
 __global__ __launch_bounds__(kThreads) void gram_k(BuildArgs a) {
   __shared__ double ti[32][33], tj[32][33];
   const int tiles = (a.W + 31) / 32;
@@ -163,14 +164,31 @@ __global__ __launch_bounds__(kThreads) void gram_k(BuildArgs a) {
   const int bj = bi + rem;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // ty in [0, 8): rows 4ty..4ty+3
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int t0 = 0; t0 < a.T; t0 += 32) {
-    for (int k = threadIdx.x; k < 32 * 32; k += blockDim.x) {
-      const int r = k >> 5, col = k & 31, t = t0 + r;
+  // The next 32 rows' loads are issued before the current ones are multiplied, all of
+  // them together: entries outside Delta read element 0 instead (in bounds) and are
+  // replaced by zeros when stored.
+  constexpr int kGL = 32 * 32 / kThreads;
+  double vi[kGL], vj[kGL];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < kGL; ++q) {
+      const int k = threadIdx.x + q * kThreads, r = k >> 5, col = k & 31, t = t0 + r;
       const int ci = bi * 32 + col, cj = bj * 32 + col;
-      ti[r][col] = (t < a.T && ci < a.W) ? a.delta[(int64_t)t * a.W + ci] : 0.0;
-      tj[r][col] = (t < a.T && cj < a.W) ? a.delta[(int64_t)t * a.W + cj] : 0.0;
+      vi[q] = a.delta[(t < a.T && ci < a.W) ? (int64_t)t * a.W + ci : 0];
+      vj[q] = a.delta[(t < a.T && cj < a.W) ? (int64_t)t * a.W + cj : 0];
+    }
+  };
+  fetch(0);
+  for (int t0 = 0; t0 < a.T; t0 += 32) {
+#pragma unroll
+    for (int q = 0; q < kGL; ++q) {
+      const int k = threadIdx.x + q * kThreads, r = k >> 5, col = k & 31, t = t0 + r;
+      const int ci = bi * 32 + col, cj = bj * 32 + col;
+      ti[r][col] = (t < a.T && ci < a.W) ? vi[q] : 0.0;
+      tj[r][col] = (t < a.T && cj < a.W) ? vj[q] : 0.0;
     }
     __syncthreads();
+    if (t0 + 32 < a.T) fetch(t0 + 32);  // uniform
     for (int r = 0; r < 32; ++r) {
       const double vj = tj[r][tx];
 #pragma unroll
@@ -201,6 +219,8 @@ __global__ __launch_bounds__(kThreads) void start_k(BuildArgs a) {
 // for 80 rows. With more than one slice the partial products go to zpart and zred_k adds them
 // in slice order (deterministic).
 constexpr int kZCols = 64, kZChunk = 32;
+static_assert(kBuildMaxSubspace * kZChunk % kThreads == 0 && kZChunk * kZCols % kThreads == 0,
+              "the staging loops cover the LDS chunks exactly");
 __global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
   __shared__ double qs[kBuildMaxSubspace][kZChunk + 1];
   __shared__ double gs[kZChunk][kZCols + 1];
@@ -215,13 +235,29 @@ __global__ __launch_bounds__(kThreads) void zt_k(BuildArgs a) {
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
   for (int jc = j0; jc < j1; jc += kZChunk) {
     const int kn = min(kZChunk, j1 - jc);
-    for (int e = tid; e < kBuildMaxSubspace * kZChunk; e += kThreads) {
-      const int r = e / kZChunk, k = e % kZChunk;
-      qs[r][k] = (r < a.p && k < kn) ? a.q[(int64_t)r * a.W + jc + k] : 0.0;
+    // Every load of the chunk is issued before the first is waited for: entries outside
+    // Q or G read element 0 instead (in bounds) and are replaced by zeros afterwards.
+    constexpr int kQL = kBuildMaxSubspace * kZChunk / kThreads, kGL = kZChunk * kZCols / kThreads;
+    double qv[kQL], gv[kGL];
+#pragma unroll
+    for (int t = 0; t < kQL; ++t) {
+      const int e = tid + t * kThreads, r = e / kZChunk, k = e % kZChunk;
+      qv[t] = a.q[(r < a.p && k < kn) ? (int64_t)r * a.W + jc + k : 0];
     }
-    for (int e = tid; e < kZChunk * kZCols; e += kThreads) {
-      const int k = e / kZCols, c = e % kZCols;
-      gs[k][c] = (k < kn && c0 + c < a.W) ? a.gram[(int64_t)(jc + k) * a.W + c0 + c] : 0.0;
+#pragma unroll
+    for (int t = 0; t < kGL; ++t) {
+      const int e = tid + t * kThreads, k = e / kZCols, c = e % kZCols;
+      gv[t] = a.gram[(k < kn && c0 + c < a.W) ? (int64_t)(jc + k) * a.W + c0 + c : 0];
+    }
+#pragma unroll
+    for (int t = 0; t < kQL; ++t) {
+      const int e = tid + t * kThreads, r = e / kZChunk, k = e % kZChunk;
+      qs[r][k] = (r < a.p && k < kn) ? qv[t] : 0.0;
+    }
+#pragma unroll
+    for (int t = 0; t < kGL; ++t) {
+      const int e = tid + t * kThreads, k = e / kZCols, c = e % kZCols;
+      gs[k][c] = (k < kn && c0 + c < a.W) ? gv[t] : 0.0;
     }
     __syncthreads();
 #pragma unroll 4
@@ -254,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void zred_k(BuildArgs a) {
   const int64_t n = (int64_t)a.p * a.W;
   if (e >= n) return;
   double v = 0.0;
-  for (int s = 0; s < a.ksplit; ++s) v += a.zpart[(int64_t)s * n + e];
+#pragma unroll 8
+  for (int s = 0; s < a.ksplit; ++s) v += a.zpart[(int64_t)s * n + e];  // unrolled: the loads overlap, the sum keeps its order
   a.z[e] = v;
 }
 
@@ -732,7 +769,8 @@ __global__ __launch_bounds__(kThreads) void finish_k(BuildArgs a) {
   if (e >= (int64_t)a.W * a.m) return;
   const int i = (int)(e / a.m), k = (int)(e % a.m);
   double s = 0.0;
-  for (int j = 0; j < a.p; ++j) s = fma(a.q[(int64_t)j * a.W + i], a.evec[j * a.p + k], s);
+#pragma unroll 8
+  for (int j = 0; j < a.p; ++j) s = fma(a.q[(int64_t)j * a.W + i], a.evec[j * a.p + k], s);  // loads overlap
   a.vm[e] = s;
   store_x(a.v_out, a.dtype, e, s);
 }
@@ -744,7 +782,8 @@ __global__ __launch_bounds__(kThreads) void usig_k(BuildArgs a) {
   const int t = (int)(e / a.m), k = (int)(e % a.m);
   const double* d = a.delta + (int64_t)t * a.W;
   double s = 0.0;
-  for (int w = 0; w < a.W; ++w) s = fma(d[w], a.vm[(int64_t)w * a.m + k], s);
+#pragma unroll 8
+  for (int w = 0; w < a.W; ++w) s = fma(d[w], a.vm[(int64_t)w * a.m + k], s);  // loads overlap, order kept
   store_x(a.u_out, a.dtype, e, s);
 }
 
