@@ -206,6 +206,69 @@ __global__ __launch_bounds__(kThreads) void gram_k(BuildArgs a) {
   }
 }
 
+// G for wide rows (many tiles, so one wave per tile still fills the chip): one wave per 32 x 32
+// tile of the upper triangle, lane (ty, tx) of an 8 x 8 grid accumulating rows 4 ty .. 4 ty + 3
+// and columns 4 tx .. 4 tx + 3 of the tile, which reads 8 LDS values per 16 fmas (gram_k: 5 per
+// 4). Each output is the same sum over t, in the same order, as in gram_k.
+constexpr int kGramWideTiles = 2048;  // upper-triangle tiles from which this kernel is used
+__global__ __launch_bounds__(64) void gram_wide_k(BuildArgs a) {
+  __shared__ __align__(16) double ti[32][36], tj[32][36];  // rows of 288 B: 16-byte aligned pairs
+  const int tiles = (a.W + 31) / 32;
+  int bi = 0, rem = blockIdx.x;  // blockIdx.x enumerates the upper triangle row by row
+  while (rem >= tiles - bi) {
+    rem -= tiles - bi;
+    ++bi;
+  }
+  const int bj = bi + rem;
+  const int lane = threadIdx.x, ty = lane >> 3, tx = lane & 7;
+  double acc[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+  for (int t0 = 0; t0 < a.T; t0 += 32) {
+    // all 32 loads of the chunk in flight together; entries outside Delta read element 0
+    // (in bounds) and are stored as zeros
+    double vi[16], vj[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int k = lane + 64 * q, r = k >> 5, col = k & 31, t = t0 + r;
+      const int ci = bi * 32 + col, cj = bj * 32 + col;
+      vi[q] = a.delta[(t < a.T && ci < a.W) ? (int64_t)t * a.W + ci : 0];
+      vj[q] = a.delta[(t < a.T && cj < a.W) ? (int64_t)t * a.W + cj : 0];
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int k = lane + 64 * q, r = k >> 5, col = k & 31, t = t0 + r;
+      const int ci = bi * 32 + col, cj = bj * 32 + col;
+      ti[r][col] = (t < a.T && ci < a.W) ? vi[q] : 0.0;
+      tj[r][col] = (t < a.T && cj < a.W) ? vj[q] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      const double2 x01 = *(const double2*)&ti[r][4 * ty], x23 = *(const double2*)&ti[r][4 * ty + 2];
+      const double2 y01 = *(const double2*)&tj[r][4 * tx], y23 = *(const double2*)&tj[r][4 * tx + 2];
+      const double x[4] = {x01.x, x01.y, x23.x, x23.y}, y[4] = {y01.x, y01.y, y23.x, y23.y};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = bi * 32 + 4 * ty + u, j = bj * 32 + 4 * tx + v;
+      if (i < a.W && j < a.W) {
+        a.gram[(int64_t)i * a.W + j] = acc[u][v];
+        a.gram[(int64_t)j * a.W + i] = acc[u][v];
+      }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void start_k(BuildArgs a) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e < (int64_t)a.p * a.W) a.z[e] = hash_uniform((uint64_t)e);
@@ -838,7 +901,9 @@ hipError_t launch_builder(const BuildArgs& a, hipStream_t st) {
   const int64_t tw = (int64_t)a.T * a.W;
   hipLaunchKernelGGL(delta_k, dim3(std::min<unsigned>(blocks_for(tw, kThreads), 8192u)), blk, 0, st, a);
   const int tiles = (a.W + 31) / 32;
-  hipLaunchKernelGGL(gram_k, dim3(tiles * (tiles + 1) / 2), blk, 0, st, a);
+  const int gtiles = tiles * (tiles + 1) / 2;
+  if (gtiles >= kGramWideTiles) hipLaunchKernelGGL(gram_wide_k, dim3(gtiles), dim3(64), 0, st, a);
+  else hipLaunchKernelGGL(gram_k, dim3(gtiles), blk, 0, st, a);
   hipLaunchKernelGGL(start_k, dim3(blocks_for((int64_t)a.p * a.W, kThreads)), blk, 0, st, a);
   const dim3 dgrid(blocks_for((int64_t)a.p * a.p, kThreads / 64));
   const dim3 tgrid(blocks_for(a.W, kTrsmWaves));
