@@ -9,6 +9,7 @@
 // G = Delta^T Delta, everything in fp64:
 //   delta_k   Delta [T][W] for the patched columns [col0, col0 + W)
 //   gram_k    G [W][W] (upper 32 x 32 tiles, mirrored)
+//             (gram_wide_k for wide rows: one wave per tile, 4 x 4 outputs per lane)
 //   start_k   a deterministic pseudo-random start block Z0 [p][W]
 //   orthonormalisation of the block Z (p x W) into Q, once for the range
 //   finder and once per power step: shifted CholeskyQR (Fukaya, Kannan,
