@@ -196,6 +196,15 @@ def test_exact_when_subspace_spans_everything():
     check_case(case, rank=32, iterations=0, sub_tol=1e-9, sig_tol=1e-9)
 
 
+def test_exact_wide_ragged_row():
+    """Width 2050 (65 column tiles, the last 2 columns wide: the Gram product takes its
+    wide-row kernel) with T = 60: p = 60 spans the row space, so the result is the exact SVD."""
+    case = BuilderCase(gqa(F32, 17, 128), tensor=0, num_tokens=60, delta=4321, col0=100, width=2050,
+                       spectrum="gaussian", seed=23)
+    say("[builder] exact case T=60 width=2050 (wide-row Gram kernel, ragged last tile)")
+    check_case(case, rank=20, iterations=1, sub_tol=1e-9, sig_tol=1e-9)
+
+
 @pytest.mark.parametrize("num_tokens,col0,width,rank", [(37, 0, 128, 16), (300, 40, 33, 33), (1, 0, 64, 1),
                                                         (5, 7, 2, 2), (200, 0, 79, 24)])
 def test_exact_at_odd_and_tiny_subspaces(num_tokens, col0, width, rank):
