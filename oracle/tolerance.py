@@ -39,15 +39,22 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def _binade(x: np.ndarray) -> np.ndarray:
+    """e with |x| = f 2^e, 1/2 <= f < 1, clamped at the lowest normal binade of fp32 and bf16
+    (both have 8 exponent bits); zero belongs to that lowest binade, whose spacing is the
+    smallest subnormal."""
+    f, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.where(f == 0, -125, np.maximum(e, -125))
+
+
 def ulp_bf16(x: np.ndarray) -> np.ndarray:
-    """Spacing of the bf16 grid just above |x| (2^-133 in the subnormal range)."""
-    _, e = np.frexp(np.asarray(x, dtype=np.float64))
-    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+    """Spacing of the bf16 grid in the binade of |x| (2^-133 for subnormals and zero)."""
+    return np.ldexp(1.0, _binade(x) - 8)
 
 
 def ulp_f32(x: np.ndarray) -> np.ndarray:
-    _, e = np.frexp(np.asarray(x, dtype=np.float64))
-    return np.ldexp(1.0, np.maximum(e, -125) - 24)
+    """Spacing of the fp32 grid in the binade of |x| (2^-149 for subnormals and zero)."""
+    return np.ldexp(1.0, _binade(x) - 24)
 
 
 def gamma(n: int) -> float:

@@ -11,6 +11,8 @@ App. A (rotate first, then add U @ V^T; factors kept as U*Sigma, V^T).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 try:
@@ -320,3 +322,211 @@ ORACLE_PINS = [pin_theta_geometric, pin_pairs_from_pages, pin_complex_multiply, 
                pin_norm_and_inverse, pin_identity, pin_large_delta_phase, pin_patch_is_matmul,
                pin_full_rank_reconstructs, pin_survivor_rotation_only, pin_paging_bruteforce,
                pin_bf16_rounding, pin_reanchor]
+
+
+# --------------------------------------------------------------------- error-bound terms
+def _brute_abs_terms(x, *, bands, d_rot, base, pairing, rotate_this, delta=0, positions=None,
+                     sections=(0, 0, 0), factors=(), tensor=0):
+    """Pure-Python walk over every output element: list the terms that the definition
+    adds up for it and sum their magnitudes. The frequencies and phases come from the
+    math module, the rotary partner and the position component of a pair are found by
+    walking the band, and every factor covering the column contributes its m products."""
+    T, F = len(x), len(x[0])
+    half = d_rot // 2
+    freqs = [math.pow(base, -2.0 * i / d_rot) for i in range(half)]
+
+    def component(i):
+        if not any(sections):
+            return 0
+        if i < sections[0]:
+            return 0
+        return 1 if i < sections[0] + sections[1] else 2
+
+    out = [[0.0] * F for _ in range(T)]
+    for t in range(T):
+        for f in range(F):
+            terms = [x[t][f]]
+            if rotate_this:
+                for o in bands:
+                    j = f - o
+                    if not 0 <= j < d_rot:
+                        continue
+                    if pairing == 0:                      # NeoX: halves of the band
+                        i, first = (j, True) if j < half else (j - half, False)
+                        pa, pb = o + i, o + i + half
+                    else:                                 # GPT-J: neighbours
+                        i, first = j // 2, j % 2 == 0
+                        pa, pb = o + 2 * i, o + 2 * i + 1
+                    p = delta if positions is None else positions[t][component(i)]
+                    c, s = math.cos(p * freqs[i]), math.sin(p * freqs[i])
+                    a, b = x[t][pa], x[t][pb]
+                    terms = [a * c, -b * s] if first else [a * s, b * c]
+            for fac in factors:
+                if fac.tensor != tensor or not fac.col0 <= f < fac.col0 + fac.vt.shape[1]:
+                    continue
+                terms += [fac.u[t][k] * fac.vt[k][f - fac.col0] for k in range(fac.u.shape[1])]
+            out[t][f] = sum(abs(v) for v in terms)
+    return np.array(out)
+
+
+def pin_abs_terms_bruteforce(o):
+    """The error bound's S (sum of |terms| of each output) against a brute-force listing of
+    every term: GQA with NeoX and GPT-J pairs and two factors on K, V with none rotated, an
+    MLA-shaped row with two overlapping factors (whole row and rope band), per-token offsets
+    with three sections, and the patch switched off."""
+    rng = np.random.default_rng(77)
+    T, H, d = 6, 2, 8
+    k = rng.standard_normal((T, H * d))
+    fk = [o.Factor(0, 0, rng.standard_normal((T, 3)), rng.standard_normal((3, H * d))),
+          o.Factor(0, 4, rng.standard_normal((T, 2)), rng.standard_normal((2, 6))),
+          o.Factor(1, 0, rng.standard_normal((T, 3)), rng.standard_normal((3, H * d)))]
+    bands = [0, d]
+    cases = []
+    for pairing in (0, 1):
+        for tensor, rot in ((0, True), (1, False)):
+            cases.append(dict(x=k, tensor=tensor, rotate_this=rot, delta=-4321, bands=bands, d_rot=d, base=1e4,
+                              pairing=pairing, factors=fk, patch=True))
+    cases.append(dict(x=k, tensor=0, rotate_this=True, delta=99991, bands=bands, d_rot=d, base=1e6, pairing=0,
+                      factors=fk, patch=False))
+    row = rng.standard_normal((T, 16))                  # latent 8 + rope band 8 at column 8
+    fm = [o.Factor(0, 0, rng.standard_normal((T, 4)), rng.standard_normal((4, 16))),
+          o.Factor(0, 8, rng.standard_normal((T, 3)), rng.standard_normal((3, 8)))]
+    cases.append(dict(x=row, tensor=0, rotate_this=True, delta=65536, bands=[8], d_rot=8, base=1e4, pairing=0,
+                      factors=fm, patch=True))
+    pos = np.stack([rng.integers(-3000, 3000, T), rng.integers(0, 64, T), rng.integers(0, 64, T)], 1)
+    cases.append(dict(x=k, tensor=0, rotate_this=True, delta=0, bands=bands, d_rot=d, base=1e6, pairing=0,
+                      factors=fk, patch=True, positions=pos, sections=(1, 1, 2)))
+    for cs in cases:
+        kw = dict(cs)
+        x = kw.pop("x")
+        patch = kw.pop("patch")
+        got = o.abs_terms(x, **kw, patch=patch)
+        want = _brute_abs_terms(x.tolist(), bands=kw["bands"], d_rot=kw["d_rot"], base=kw["base"],
+                                pairing=kw["pairing"], rotate_this=kw["rotate_this"], delta=kw["delta"],
+                                positions=None if kw.get("positions") is None else kw["positions"].tolist(),
+                                sections=kw.get("sections", (0, 0, 0)),
+                                factors=kw["factors"] if patch else (), tensor=kw["tensor"])
+        assert got.shape == want.shape
+        assert np.max(np.abs(got - want) / want) <= 1e-13, {k_: v for k_, v in kw.items() if k_ != "factors"}
+
+
+ORACLE_PINS.append(pin_abs_terms_bruteforce)
+
+
+# --------------------------------------------------------------------- tolerance predicates
+# These take the tolerance module t (and the oracle o for S), so planted mistakes in
+# either module can be run against them.
+def _bf16_code_values():
+    """All positive finite bf16 codes and their values, decoded from the bit fields
+    directly (sign 1, exponent 8, fraction 7; exponent 0 = subnormal)."""
+    codes = np.arange(0x7F80, dtype=np.int64)            # +0 .. largest finite
+    ex, fr = codes >> 7, codes & 0x7F
+    vals = np.where(ex == 0, np.ldexp(fr.astype(np.float64), -133),
+                    np.ldexp((128 + fr).astype(np.float64), (ex - 134).astype(np.int64)))
+    return codes, vals
+
+
+def pin_ulp_spacing(t, o=None):
+    """ulp_bf16 at every bf16 value is the gap to the next code (exhaustive, zero and
+    subnormals included), and inside each binade stays that gap; ulp_f32 equals numpy's
+    float32 spacing over every binade, subnormals and zero included."""
+    codes, vals = _bf16_code_values()
+    gap = vals[1:] - vals[:-1]                            # value(code + 1) - value(code)
+    assert np.array_equal(t.ulp_bf16(vals[:-1]), gap)
+    assert np.array_equal(t.ulp_bf16(-vals[:-1]), gap)
+    inside = vals[:-1] + 0.25 * gap                       # between two codes: same binade
+    assert np.array_equal(t.ulp_bf16(inside), gap)
+    # float32: powers of two, their neighbours and random values of every exponent
+    e = np.arange(-149, 128)
+    p2 = np.ldexp(np.float32(1), e).astype(np.float32)
+    rnd = np.random.default_rng(3).integers(0, 0x7F800000, size=200000, dtype=np.int64).astype(np.uint32)
+    f = np.concatenate([p2, np.nextafter(p2, np.float32(0)), np.nextafter(p2, np.float32(np.inf)),
+                        rnd.view(np.float32), np.float32([0.0, 1e-45, 1.17549435e-38])])
+    f = f[np.isfinite(f) & (f < np.float32(3.4e38))]
+    want = np.spacing(f).astype(np.float64)
+    assert np.array_equal(t.ulp_f32(f.astype(np.float64)), want)
+    assert np.array_equal(t.ulp_f32(-f.astype(np.float64)), want)
+
+
+def _c1_block(o, seed=5):
+    """A single-layer fp32 GQA block of the small workload's shape: 256 tokens, 2 heads x 64,
+    delta in [0, 4096], a rank-8 factor on the rotated keys."""
+    rng = np.random.default_rng(seed)
+    T, H, d, m = 256, 2, 64, 8
+    x = rng.standard_normal((T, H * d)).astype(np.float32).astype(np.float64)
+    u = (0.5 * rng.standard_normal((T, m))).astype(np.float32).astype(np.float64)
+    vt = (rng.standard_normal((m, H * d)) / np.sqrt(T)).astype(np.float32).astype(np.float64)
+    delta = int(rng.integers(0, 4097))
+    kw = dict(tensor=0, delta=delta, rotate_this=True, bands=[0, d], d_rot=d, base=1e4, pairing=0,
+              factors=[o.Factor(0, 0, u, vt)], patch=True)
+    y = o.rehydrate_tensor(x, family=o.GQA, **kw)
+    S = o.abs_terms(x, **kw)
+    return x, u, vt, delta, y, S, m
+
+
+def _fp32_evaluation(x, u, vt, delta, d=64, base=1e4):
+    """The same block evaluated the way a device in fp32 would, but independently: cos and
+    sin rounded once to float32, the pair rotation and every patch term in float32 products
+    and sums (no fused multiply-add), terms added in order."""
+    x32, u32, vt32 = x.astype(np.float32), u.astype(np.float32), vt.astype(np.float32)
+    half = d // 2
+    th = np.array([math.pow(base, -2.0 * i / d) for i in range(half)])
+    c = np.array([math.cos(delta * v) for v in th], dtype=np.float32)
+    s = np.array([math.sin(delta * v) for v in th], dtype=np.float32)
+    y = x32.copy()
+    for o_ in range(0, x.shape[1], d):
+        a, b = x32[:, o_:o_ + half], x32[:, o_ + half:o_ + d]
+        y[:, o_:o_ + half] = a * c - b * s
+        y[:, o_ + half:o_ + d] = a * s + b * c
+    for j in range(u.shape[1]):
+        y = y + u32[:, j:j + 1] * vt32[j:j + 1, :]
+    return y
+
+
+def pin_check_f32(t, o):
+    """P3 on a block of the fp32 workload's shape: accepts the oracle's own rounding and an
+    independent float32 evaluation; rejects a planted relative error of 2^-12 on nearly every
+    element; with S = 0 and no angle term, half an fp32 ulp passes and two ulps do not."""
+    x, u, vt, delta, y, S, m = _c1_block(o)
+    n = m + 4
+    assert t.check_f32(o.round_f32(y), y, S, n)["fail"] == 0
+    g = _fp32_evaluation(x, u, vt, delta)
+    res = t.check_f32(g, y, S, n)
+    assert res["fail"] == 0, res["fail"]
+    off_ulp = np.abs(g.astype(np.float64) - y) > 0.5 * np.spacing(np.abs(y).astype(np.float32))
+    assert off_ulp.sum() > 0.01 * y.size          # the evaluation really does differ by more than rounding
+    bad = t.check_f32(o.round_f32(y * (1 + 2.0 ** -12)), y, S, n)
+    assert bad["fail"] >= 0.97 * y.size, bad["fail"]
+    # S = 0, A = 0: exact half-ulp rule against the float32 grid
+    f = np.random.default_rng(9).standard_normal(4096).astype(np.float32)
+    f = f[np.abs(f) > 1e-3]
+    yv = f.astype(np.float64) + 0.25 * np.spacing(np.abs(f)).astype(np.float64)   # inside the ulp above f
+    zero = np.zeros_like(yv)
+    assert t.check_f32(f, yv, zero, 1)["fail"] == 0                                 # |g - y| = ulp/4
+    two = np.nextafter(np.nextafter(f, np.float32(np.inf)), np.float32(np.inf))      # two codes up
+    assert t.check_f32(two, yv, zero, 1)["fail"] == len(f)
+    tiny = np.array([0.0, 2.0 ** -140])                                             # at and near zero
+    assert t.check_f32(np.float32([2.0 ** -149, 0.0]), tiny, np.zeros(2), 1)["fail"] == 2
+
+
+def pin_check_bf16(t, o):
+    """P1/P2 on a bf16 block: accepts the oracle's rounding and an fp32 evaluation rounded to
+    bf16 (a second rounding: one code off at most); rejects a planted relative error of 2^-6
+    (three or more bf16 codes) on nearly every element; a zero output for a small non-zero
+    value is not covered by the zero's own spacing."""
+    x, u, vt, delta, y, S, m = _c1_block(o, seed=6)
+    n = m + 4
+    r = o.round_bf16(y)
+    assert t.check_bf16(r, y, r, S, n)["fail"] == 0
+    g32 = _fp32_evaluation(x, u, vt, delta)
+    g = o.round_bf16(g32.astype(np.float64))
+    res = t.check_bf16(g, y, r, S, n)
+    assert res["fail"] == 0 and res["exact"] > 0.9 * y.size
+    bad = t.check_bf16(o.round_bf16(y * (1 + 2.0 ** -6)), y, r, S, n)
+    assert bad["fail"] >= 0.97 * y.size, bad["fail"]
+    yv = np.array([1e-6, -3e-5])
+    rv = o.round_bf16(yv)
+    assert t.check_bf16(np.zeros(2, np.uint16), yv, rv, np.abs(yv), 1)["fail"] == 2
+
+
+TOLERANCE_PINS = [pin_ulp_spacing, pin_check_f32, pin_check_bf16]

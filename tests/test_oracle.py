@@ -8,7 +8,7 @@ import pytest
 import oracle.builder_oracle as builder
 import oracle.kamera_oracle as O
 from oracle import tolerance as tol
-from tests.oracle_pins import ORACLE_PINS, pin_builder_planted, pin_orbit_mean
+from tests.oracle_pins import ORACLE_PINS, TOLERANCE_PINS, pin_builder_planted, pin_orbit_mean
 
 ORACLE_PATH = os.path.join(os.path.dirname(O.__file__), "kamera_oracle.py")
 
@@ -16,6 +16,11 @@ ORACLE_PATH = os.path.join(os.path.dirname(O.__file__), "kamera_oracle.py")
 @pytest.mark.parametrize("pin", ORACLE_PINS, ids=lambda p: p.__name__)
 def test_oracle_pin(pin):
     pin(O)
+
+
+@pytest.mark.parametrize("pin", TOLERANCE_PINS, ids=lambda p: p.__name__)
+def test_tolerance_pin(pin):
+    pin(tol, O)
 
 
 def test_builder_pin():
@@ -142,10 +147,43 @@ def _mut_first_token_positions(m):
     m.token_phases = lambda pos, d, b, sec: orig(np.repeat(np.asarray(pos)[:1], len(pos), 0), d, b, sec)
 
 
+def _mut_abs_terms_scaled(m):
+    orig = m.abs_terms
+    m.abs_terms = lambda x, **kw: orig(x, **kw) * 1000.0
+
+
+def _mut_abs_terms_no_patch(m):
+    orig = m.abs_terms
+    m.abs_terms = lambda x, **kw: orig(x, **dict(kw, patch=False))
+
+
+def _mut_abs_terms_signed(m):
+    """|sum of terms| instead of the sum of |terms|: a bound that shrinks where terms cancel."""
+    def at(x, **kw):
+        kw.pop("family", None)
+        return np.abs(m.rehydrate_tensor(x, family=m.GQA, **kw))
+    m.abs_terms = at
+
+
+def _mut_abs_terms_cos_only(m):
+    """The rotated pair's sin terms dropped from S."""
+    orig_phases = m.phases
+    orig = m.abs_terms
+
+    def at(x, **kw):
+        m.phases = lambda d, r, b: (orig_phases(d, r, b)[0], 0.0 * orig_phases(d, r, b)[1])
+        try:
+            return orig(x, **kw)
+        finally:
+            m.phases = orig_phases
+    m.abs_terms = at
+
+
 MUTANTS = [_mut_sign, _mut_cos_sin_swapped, _mut_pairing, _mut_theta_half, _mut_theta_shift,
            _mut_theta_f32, _mut_patch_before_rotate, _mut_patch_rank_reversed, _mut_round_truncate,
            _mut_round_double, _mut_page_no_slot0, _mut_v_rotated, _mut_mla_latent_band,
-           _mut_sections_off_by_one, _mut_sections_all_t, _mut_theta_within_section, _mut_first_token_positions]
+           _mut_sections_off_by_one, _mut_sections_all_t, _mut_theta_within_section, _mut_first_token_positions,
+           _mut_abs_terms_scaled, _mut_abs_terms_no_patch, _mut_abs_terms_signed, _mut_abs_terms_cos_only]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__[5:])
@@ -285,3 +323,57 @@ def test_tolerance_predicate():
     assert res["fail"] == 0 and res["p2_only"] == 1
     assert tol.bf16_ord(np.array([0x0000, 0x8000], np.uint16)).tolist() == [0, 0]
     assert tol.bf16_ord(np.array([0x8001], np.uint16))[0] == -1
+
+
+# ---------------------------------------------------------------- planted mistakes in the tolerance
+TOL_PATH = os.path.join(os.path.dirname(tol.__file__), "tolerance.py")
+
+
+def _fresh_tolerance():
+    spec = importlib.util.spec_from_file_location("tolerance_mutant", TOL_PATH)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _tmut_ulp_f32_is_bf16(t):
+    t.ulp_f32 = t.ulp_bf16
+
+
+def _tmut_gamma_bf16_unit(t):
+    t.U32 = 2.0 ** -8
+
+
+def _tmut_zero_ulp_from_frexp(t):
+    """Zero's spacing taken from frexp's exponent 0 (2^-8 and 2^-24) instead of the smallest subnormal."""
+    t._binade = lambda x: np.maximum(np.frexp(np.asarray(x, dtype=np.float64))[1], -125)
+
+
+def _tmut_f32_ignores_S(t):
+    orig = t.check_f32
+    t.check_f32 = lambda g, y, S, n, A=None: orig(g, y, np.zeros_like(np.asarray(S)), n, A)
+
+
+def _tmut_ulp_bf16_doubled(t):
+    orig = t.ulp_bf16
+    t.ulp_bf16 = lambda x: 2.0 * orig(x)
+
+
+def _tmut_p1_two_codes(t):
+    orig = t.bf16_ord
+    t.bf16_ord = lambda bits: orig(bits) // 2
+
+
+@pytest.mark.parametrize("mutate", [_tmut_ulp_f32_is_bf16, _tmut_gamma_bf16_unit, _tmut_zero_ulp_from_frexp,
+                                    _tmut_f32_ignores_S, _tmut_ulp_bf16_doubled, _tmut_p1_two_codes],
+                         ids=lambda f: f.__name__[6:])
+def test_tolerance_pins_catch_planted_mistake(mutate):
+    t = _fresh_tolerance()
+    mutate(t)
+    caught = []
+    for pin in TOLERANCE_PINS:
+        try:
+            pin(t, O)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {mutate.__name__}"
