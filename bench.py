@@ -2,9 +2,10 @@
 
 One step = one kamera_rehydrate_batched call over the whole workload (every
 chunk, every layer, K and V), inputs already resident in HBM. The default
-workload is the GQA vision-language-7B-like batch: 28 layers, 4 KV heads x
-128, bf16, 8 video segments of 1024 tokens with their own delta, rank-32
-patches on K and V.
+workload is the largest one that fits a single GPU: the MHA 7B reorder batch
+(32 layers, 32 heads x 128, bf16, all 6 orderings of three 2048-token chunks
+plus a fixed fourth, 24 rehydrations with rank-32 K and V patches; 52 GB moved
+per step).
 
 Prints one JSON line: whole-job tokens/s (rehydrated tokens per second of wall
 time), the dominant kernel's roofline figures measured with HIP events on the
@@ -69,9 +70,20 @@ def measured_traffic(cfg: str):
 
 
 # ----------------------------------------------------------------------------- CPU oracle leg
+# (chunk, layer) units timed on the oracle by default: about 10-40 CPU-s of work each
+CPU_UNITS = {"C1": 32768, "C2": 448, "C3": 448, "C4": 16, "C5": 576}
+CPU_PROCS_MAX = 16       # the host share of one GPU
+PLAN_WARMUP = 3          # untimed launches of the uploaded plan before its timed launches
+KERNEL_LAUNCHES = 100    # the kernel average covers at least this many launches
+PATTERN_WARMUP = 5
+
+
 def _oracle_units(args):
-    """Worker: draw its (chunk, layer) inputs first, then time only the oracle on them."""
-    cfg, units = args
+    """Worker: draw its (chunk, layer) inputs first, then time only the oracle on them.
+    Out-of-place GQA/MHA chunks: K and V rehydrated; MLA chunks: the 576-wide row;
+    in-place survivors: R(delta) on K (the MLA rope band); each result rounded once to
+    the storage dtype, and paged chunks' (page, offset) slots computed."""
+    cfg, units, make_kw = args
     import torch
     from threadpoolctl import threadpool_limits
     torch.set_num_threads(1)          # one thread per worker process: no oversubscription
@@ -79,42 +91,78 @@ def _oracle_units(args):
     import oracle.kamera_oracle as O
     from tests.expect import oracle_factors
     from workloads import make_workload
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, **make_kw)
     lay = wl.layout
     prepared = []
     for ci, layer in units:
         ch = wl.chunks[ci]
-        k = O.upcast(wl.canonical(ch.canon_id, layer, 0), lay.dtype)
-        v = O.upcast(wl.canonical(ch.canon_id, layer, 1), lay.dtype)
-        prepared.append((ch, k, v, oracle_factors(wl, ch, layer)))
+        if ch.in_place:
+            xs = [O.upcast(wl.pool_rows(ch, layer, 0), lay.dtype)]
+        else:
+            xs = [O.upcast(wl.canonical(ch.canon_id, layer, t), lay.dtype) for t in range(lay.num_tensors)]
+        prepared.append((ch, xs, oracle_factors(wl, ch, layer) if ch.patched else []))
+    geo = dict(num_kv_heads=lay.num_kv_heads, head_dim=lay.head_dim, latent_dim=lay.latent_dim,
+               rope_dim=lay.rope_dim)
     t0 = time.perf_counter()
-    for ch, k, v, facs in prepared:
-        yk, yv = O.rehydrate_gqa(k, v, ch.delta, num_kv_heads=lay.num_kv_heads, head_dim=lay.head_dim,
+    tokens = 0.0
+    for ch, xs, facs in prepared:
+        if ch.in_place:
+            ys = [O.relocate(xs[0], ch.delta, family=lay.family, base=lay.rope_base, pairing=lay.pairing, **geo)]
+        elif lay.family == O.MLA:
+            ys = [O.rehydrate_mla(xs[0], ch.delta, latent_dim=lay.latent_dim, rope_dim=lay.rope_dim,
+                                  base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched)]
+        else:
+            ys = O.rehydrate_gqa(xs[0], xs[1], ch.delta, num_kv_heads=lay.num_kv_heads, head_dim=lay.head_dim,
                                  base=lay.rope_base, pairing=lay.pairing, factors=facs, patch=ch.patched)
-        O.round_to(yk, lay.dtype)
-        O.round_to(yv, lay.dtype)
-    return time.perf_counter() - t0, len(prepared)
+        for y in ys:
+            O.round_to(y, lay.dtype)
+        if ch.block_table is not None:
+            O.page_slots(ch.num_tokens, ch.block_table, ch.slot0, lay.page_size)
+        tokens += ch.num_tokens / lay.num_layers   # a token is rehydrated once all its layers are done
+    return time.perf_counter() - t0, len(prepared), tokens
 
 
-def cpu_baseline(cfg: str, wl, sample_units: int):
+def _cpu_share() -> int:
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return max(1, min(CPU_PROCS_MAX, avail))
+
+
+def cpu_baseline(cfg: str, wl, sample_units: int, make_kw: dict):
+    """The fp64 oracle on a bounded sample of the workload's (chunk, layer) units, spread
+    evenly over the chunks and layers: once over a pool of one process per available host
+    CPU (at most the 16 that one GPU's share holds), once in a single process on one
+    process's share of the sample."""
     import multiprocessing as mp
-    cores = max(1, min(16, os.cpu_count() or 1))
+    procs = _cpu_share()
     all_units = [(ci, layer) for ci in range(len(wl.chunks)) for layer in range(wl.layout.num_layers)]
-    units = [all_units[i % len(all_units)] for i in range(sample_units)]
-    parts = [(cfg, units[i::cores]) for i in range(cores) if units[i::cores]]
+    if sample_units <= len(all_units):
+        pick = [int(round(i * (len(all_units) - 1) / max(1, sample_units - 1))) for i in range(sample_units)]
+        units = [all_units[i] for i in pick]
+    else:
+        units = [all_units[i % len(all_units)] for i in range(sample_units)]
+    parts = [(cfg, units[i::procs], make_kw) for i in range(procs) if units[i::procs]]
     ctx = mp.get_context("fork")
     with ctx.Pool(len(parts)) as pool:
         res = pool.map(_oracle_units, parts)
     wall = max(r[0] for r in res)
     cpu_s = sum(r[0] for r in res)
     n_units = sum(r[1] for r in res)
-    T = wl.chunks[0].num_tokens
-    tokens = n_units * T / wl.layout.num_layers     # a token is rehydrated once all its layers are done
+    tokens = sum(r[2] for r in res)
+    with ctx.Pool(1) as pool:
+        one = pool.map(_oracle_units, [parts[0]])[0]
+    kinds = sorted({"in-place survivors (K rotated)" if wl.chunks[ci].in_place else
+                    ("MLA rows" if wl.layout.family == 1 else "K and V") for ci, _ in units})
     return {"value": tokens / wall, "unit": "tokens/s", "cores": len(parts), "kind": "oracle",
-            "sample": f"{n_units} (chunk, layer) units of {T} tokens (K and V, fp64, rounded to "
-                      f"{'fp32' if wl.layout.dtype == 0 else 'bf16'}) of the "
-                      f"{cfg} workload, spread over {len(parts)} processes; {wall:.1f} s wall, {cpu_s:.1f} CPU-s, "
-                      f"input drawing excluded"}
+            "host_cpus": os.cpu_count(), "cpus_available": len(os.sched_getaffinity(0)),
+            "one_process": {"value": one[2] / one[0], "unit": "tokens/s", "units": one[1], "wall_s": one[0]},
+            "sample": f"{n_units} (chunk, layer) units ({', '.join(kinds)}; fp64, rounded to "
+                      f"{'fp32' if wl.layout.dtype == 0 else 'bf16'}) of the {cfg} workload, spread evenly over "
+                      f"its chunks and layers, run over {len(parts)} processes: {wall:.1f} s wall, {cpu_s:.1f} CPU-s; "
+                      f"tokens = units x chunk tokens / layers; input drawing excluded; one process alone on "
+                      f"{one[1]} of the units: {one[0]:.1f} s"}
 
 
 # ----------------------------------------------------------------------------- patch builder
@@ -211,12 +259,13 @@ def builder_main(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C4", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-units", type=int, default=None,
-                    help="(chunk, layer) units timed on the CPU oracle (the workload's units repeat as needed); "
-                         "default: about 10-15 CPU-s of oracle work (448 for C2, 32768 for C1)")
+                    help="(chunk, layer) units timed on the CPU oracle, spread evenly over the workload "
+                         "(repeated as needed); default: about 10-40 CPU-s of oracle work (%s)" %
+                         ", ".join(f"{k} {v}" for k, v in CPU_UNITS.items()))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
     ap.add_argument("--rank", type=int, default=None, help="override the patch rank m of the workload")
@@ -227,6 +276,9 @@ def main() -> int:
     ap.add_argument("--positions", action="store_true",
                     help="re-anchor every rehydrated chunk token by token with (t, h, w) M-RoPE ids "
                          "(64-token frames on an 8 x 8 grid at the chunk's start) instead of one delta")
+    ap.add_argument("--page-order", choices=("random", "physical"), default="random",
+                    help="paged workloads: the seeded random block table (default), or the same chunks with "
+                         "their pages numbered in physical order (consecutive page ids, chunk after chunk)")
     ap.add_argument("--builder", action="store_true",
                     help="time the patch builder (kamera_build_patch) on one chunk-layer of --config instead")
     ap.add_argument("--builder-iterations", type=int, default=16)
@@ -243,18 +295,22 @@ def main() -> int:
         return builder_main(args)
 
     from workloads import make_workload
-    wl = make_workload(args.config, rank=args.rank)
-    variant = args.deep_half or args.shared_basis or args.positions
-    if variant:
-        wl = make_workload(args.config, rank=args.rank, shared_basis=args.shared_basis, positions=args.positions,
-                           patch_layer0=wl.layout.num_layers // 2 if args.deep_half else None)
+    make_kw = dict(rank=args.rank)
+    if args.page_order != "random":
+        make_kw["page_order"] = args.page_order
+    wl = make_workload(args.config, **make_kw)
+    variant = args.deep_half or args.shared_basis or args.positions or args.page_order != "random"
+    if args.deep_half or args.shared_basis or args.positions:
+        make_kw.update(shared_basis=args.shared_basis, positions=args.positions,
+                       patch_layer0=wl.layout.num_layers // 2 if args.deep_half else None)
+        wl = make_workload(args.config, **make_kw)
     # The CPU oracle leg forks worker processes, so it runs before this process
     # touches the GPU (forking a process whose HIP runtime threads are live can deadlock).
     cpu = None
-    if not args.no_cpu and not variant and wl.layout.family == 0 and not any(c.in_place for c in wl.chunks):
+    if not args.no_cpu and not variant:
         t_cpu = time.perf_counter()
-        units = args.cpu_units if args.cpu_units is not None else {"C1": 32768}.get(args.config, 448)
-        cpu = cpu_baseline(args.config, wl, units)
+        units = args.cpu_units if args.cpu_units is not None else CPU_UNITS[args.config]
+        cpu = cpu_baseline(args.config, wl, units, make_kw)
         print(f"# cpu oracle leg done in {time.perf_counter() - t_cpu:.1f} s", file=sys.stderr, flush=True)
 
     import torch
@@ -288,19 +344,23 @@ def main() -> int:
     wall_s = time.perf_counter() - t0
     call_ms_gpu = e0.elapsed_time(e1) / args.steps
 
-    # ---- the kernel alone: same batch, uploaded once, launched K times on the same stream
+    # ---- the kernel alone: same batch, uploaded once, launched back to back on the
+    # same stream (after untimed launches of its own), at least KERNEL_LAUNCHES times
     plan = dw.plan(stream)
+    for _ in range(PLAN_WARMUP):
+        abi.plan_launch(plan, stream)
     torch.cuda.synchronize()
+    n_kernel = max(args.steps, KERNEL_LAUNCHES)
     e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e2.record(stream)
-    for _ in range(args.steps):
+    for _ in range(n_kernel):
         abi.plan_launch(plan, stream)
     e3.record(stream)
     torch.cuda.synchronize()
-    kernel_us = e2.elapsed_time(e3) / args.steps * 1e3
+    kernel_us = e2.elapsed_time(e3) / n_kernel * 1e3
 
     # ---- per-launch spread: each launch between its own pair of events
-    n_dist = min(args.steps, 200)
+    n_dist = min(max(args.steps, KERNEL_LAUNCHES), 200)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
     for ea, eb in evs:
         ea.record(stream)
@@ -316,7 +376,7 @@ def main() -> int:
     cbytes = dw.copy_bytes()
     if cbytes > 0:
         cplan = abi.plan_upload(dw.layout, dw.copy_descs(), dw.pool_desc, dw.workspace, stream)
-        for _ in range(5):
+        for _ in range(PATTERN_WARMUP):
             abi.plan_launch(cplan, stream)
         e6, e7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e6.record(stream)
@@ -369,7 +429,8 @@ def main() -> int:
                    + (" (deep-half patches: layers L/2..L-1 only)" if args.deep_half else "")
                    + (" (one V basis per layer shared by all chunks)" if args.shared_basis else "")
                    + (" (per-token (t, h, w) re-anchoring, M-RoPE sections %s)" % (wl.layout.mrope_section,)
-                      if args.positions else ""),
+                      if args.positions else "")
+                   + (" (block table in physical page order)" if args.page_order == "physical" else ""),
                    "name": args.config, "chunks": len(wl.chunks),
                    "tokens": tokens, "layers": wl.layout.num_layers, "row_width": wl.layout.row_width},
         "roofline": dict({"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -377,7 +438,11 @@ def main() -> int:
                          **({"note": "the whole workload is 0.55 MB: the launch is latency-bound and the fraction "
                                      "of HBM peak is not a measure of the kernel"} if args.config == "C1" else {})),
         "kernel_us": kernel_us,
+        "kernel_launches_timed": n_kernel,
         "kernel_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        # operator launches in this run, in order: whole calls, plan launches, same-pattern copy
+        "launches": {"calls": args.warmup + args.steps, "plan": PLAN_WARMUP + n_kernel + n_dist,
+                     "pattern": (PATTERN_WARMUP + n_dist) if cbytes > 0 else 0},
         "pattern_copy_GBps": pattern_gbps,
         "frac_of_pattern_copy": (achieved / pattern_gbps) if pattern_gbps else None,
         "call_us_gpu": call_ms_gpu * 1e3,

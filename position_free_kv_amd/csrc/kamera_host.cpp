@@ -220,15 +220,14 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   // -------------------------------------------------------------- per-chunk checks
   bool mfma = mfma_layout_ok(L);
   int need_ksteps = 0;  // MFMA path: most 32-wide k-steps covering any column group
-  // Pool slots written by this batch: one bit per slot, kept per page as a mask
-  // (pages of up to 64 slots), so the overlap check costs O(pages), not O(tokens).
-  thread_local std::vector<uint64_t> page_mask;
-  thread_local std::vector<uint8_t> slot_used;
-  const bool mask_mode = P <= 64;
-  if (any_paged) {
-    if (mask_mode) page_mask.assign((size_t)pool->num_pages, 0);
-    else slot_used.assign((size_t)pool->num_pages * P, 0);
-  }
+  // Pool slots written by this batch: the slot range [lo, hi) each chunk covers in each of
+  // its pages, sorted by page, so the overlap check costs O(B log B) in the batch's B page
+  // entries, whatever the pool's size.
+  struct SlotRange {
+    int32_t page, lo, hi, chunk;
+  };
+  thread_local std::vector<SlotRange> ranges;
+  ranges.clear();
 
   for (int i = 0; i < n; ++i) {
     const kamera_chunk& c = chunks[i];
@@ -276,26 +275,10 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
           return fail(KAMERA_E_PAGE, "chunk %d: block_table[%lld] = %d outside [0, %d)", i, (long long)k, pg,
                       pool->num_pages);
       }
-      if (mask_mode) {
-        for (int64_t k = 0; k < np; ++k) {
-          const int64_t lo = std::max<int64_t>(c.slot0 - k * P, 0);
-          const int64_t hi = std::min<int64_t>(c.slot0 + T - k * P, P);
-          const uint64_t m = (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)) << lo;
-          uint64_t& pm = page_mask[(size_t)c.block_table[k]];
-          if (pm & m)
-            return fail(KAMERA_E_OVERLAP, "chunk %d: pool page %d has slots already written in this batch", i,
-                        c.block_table[k]);
-          pm |= m;
-        }
-      } else {
-        for (int64_t t = 0; t < T; ++t) {
-          const int64_t s = c.slot0 + t;
-          const size_t slot = (size_t)c.block_table[s / P] * P + (size_t)(s % P);
-          if (slot_used[slot])
-            return fail(KAMERA_E_OVERLAP, "chunk %d token %lld: pool page %d offset %lld already written in this batch",
-                        i, (long long)t, c.block_table[s / P], (long long)(s % P));
-          slot_used[slot] = 1;
-        }
+      for (int64_t k = 0; k < np; ++k) {
+        const int64_t lo = std::max<int64_t>(c.slot0 - k * P, 0);
+        const int64_t hi = std::min<int64_t>(c.slot0 + T - k * P, P);
+        ranges.push_back(SlotRange{c.block_table[k], (int32_t)lo, (int32_t)hi, i});
       }
       if (mfma && (!aligned(pool->k_pool, 16) || (pool->v_pool && !aligned(pool->v_pool, 16)) ||
                    pool->layer_stride % 8))
@@ -345,6 +328,27 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
             need_ksteps = std::max(need_ksteps, ks);
           }
       }
+    }
+  }
+  if (ranges.size() > 1) {
+    std::sort(ranges.begin(), ranges.end(), [](const SlotRange& a, const SlotRange& b) {
+      return a.page != b.page ? a.page < b.page : a.lo < b.lo;
+    });
+    size_t open = 0;  // the entry of the current page reaching furthest
+    for (size_t j = 1; j < ranges.size(); ++j) {
+      if (ranges[j].page != ranges[open].page) {
+        open = j;
+        continue;
+      }
+      if (ranges[j].lo < ranges[open].hi) {
+        const int c0 = std::min(ranges[open].chunk, ranges[j].chunk), c1 = std::max(ranges[open].chunk, ranges[j].chunk);
+        if (c0 == c1)
+          return fail(KAMERA_E_OVERLAP, "chunk %d writes slot %d of pool page %d twice (its block table repeats the page)",
+                      c0, ranges[j].lo, ranges[j].page);
+        return fail(KAMERA_E_OVERLAP, "chunks %d and %d both write slot %d of pool page %d", c0, c1, ranges[j].lo,
+                    ranges[j].page);
+      }
+      if (ranges[j].hi > ranges[open].hi) open = j;
     }
   }
   // 128-wide groups keep at most 4 k-steps of V operands in registers; with per-token
@@ -517,6 +521,46 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   return KAMERA_OK;
 }
 
+// The packed batch's block-table and cos/sin-table offsets turned into device addresses
+// inside the workspace `ws` it will be copied to.
+void bind_workspace(Packed& pk, int n, void* ws) {
+  const size_t pages_off = round_up(sizeof(DevHeader), kAlign) + round_up((size_t)n * sizeof(DevChunk), kAlign);
+  DevChunk* dc = reinterpret_cast<DevChunk*>(pk.blob.data() + round_up(sizeof(DevHeader), kAlign));
+  for (int i = 0; i < n; ++i)
+    dc[i].pages = pk.page_off[(size_t)i] < 0
+                      ? nullptr
+                      : reinterpret_cast<const int32_t*>((char*)ws + pages_off +
+                                                         (size_t)pk.page_off[(size_t)i] * sizeof(int32_t));
+  for (int i = 0; i < n; ++i)
+    dc[i].phase = pk.phase_off[(size_t)i] < 0 ? nullptr
+                                              : reinterpret_cast<const float*>((char*)ws + pk.phase_off[(size_t)i]);
+}
+
+const DevHeader* ws_header(const void* ws) { return reinterpret_cast<const DevHeader*>(ws); }
+const DevChunk* ws_chunks(const void* ws) {
+  return reinterpret_cast<const DevChunk*>((const char*)ws + round_up(sizeof(DevHeader), kAlign));
+}
+
+// After the packed batch has reached the workspace: the per-token cos/sin tables (when the
+// batch has re-anchored chunks) are computed there, on the same stream.
+kamera_status launch_phase_tables(const Packed& pk, int n, void* ws, void* stream) {
+  if (pk.phase_entries <= 0) return KAMERA_OK;
+  const hipError_t e = launch_phase_table(ws_header(ws), ws_chunks(ws), n, pk.phase_blocks, (hipStream_t)stream,
+                                          nullptr);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
+kamera_status launch_main(int kernel, int variant, int dtype, int64_t tasks, const void* ws, void* stream) {
+  if (tasks <= 0 || kernel == 0) return KAMERA_OK;
+  hipError_t e;
+  if (kernel == 1) e = launch_mfma(variant, ws_header(ws), ws_chunks(ws), tasks, (hipStream_t)stream, nullptr);
+  else if (kernel == 2) e = launch_generic(dtype, ws_header(ws), ws_chunks(ws), tasks, (hipStream_t)stream, nullptr);
+  else return fail(KAMERA_E_UNSUPPORTED, "plan names unknown kernel %d", kernel);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return KAMERA_OK;
+}
+
 kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, int32_t n, const kamera_pool* pool,
                           void* ws, size_t ws_size, void* stream, kamera_plan* plan) {
   thread_local std::vector<unsigned char> blob;
@@ -528,26 +572,12 @@ kamera_status upload_plan(const kamera_layout* L, const kamera_chunk* chunks, in
   if (!ws) return fail(KAMERA_E_WORKSPACE, "workspace is NULL");
   if (!aligned(ws, kAlign)) return fail(KAMERA_E_ALIGN, "workspace must be %zu-byte aligned", kAlign);
   if (ws_size < pk.bytes) return fail(KAMERA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_size, pk.bytes);
-  // turn page-table offsets into device addresses inside the workspace
-  const size_t pages_off = round_up(sizeof(DevHeader), kAlign) + round_up((size_t)n * sizeof(DevChunk), kAlign);
-  DevChunk* dc = reinterpret_cast<DevChunk*>(pk.blob.data() + round_up(sizeof(DevHeader), kAlign));
-  for (int i = 0; i < n; ++i)
-    dc[i].pages = pk.page_off[(size_t)i] < 0
-                      ? nullptr
-                      : reinterpret_cast<const int32_t*>((char*)ws + pages_off +
-                                                         (size_t)pk.page_off[(size_t)i] * sizeof(int32_t));
-  for (int i = 0; i < n; ++i)
-    dc[i].phase = pk.phase_off[(size_t)i] < 0 ? nullptr
-                                              : reinterpret_cast<const float*>((char*)ws + pk.phase_off[(size_t)i]);
+  bind_workspace(pk, n, ws);
   if (pk.tasks > 0) {
     st = upload(pk.blob.data(), pk.upload_bytes, ws, (hipStream_t)stream);
     if (st != KAMERA_OK) return st;
-    if (pk.phase_entries > 0) {  // per-token cos/sin tables, computed once per upload
-      const DevHeader* hd = reinterpret_cast<const DevHeader*>(ws);
-      const DevChunk* dcd = reinterpret_cast<const DevChunk*>((const char*)ws + round_up(sizeof(DevHeader), kAlign));
-      const hipError_t e = launch_phase_table(hd, dcd, n, pk.phase_blocks, (hipStream_t)stream, nullptr);
-      if (e != hipSuccess) return fail(KAMERA_E_HIP, "phase table launch failed: %s", hipGetErrorString(e));
-    }
+    st = launch_phase_tables(pk, n, ws, stream);  // computed once per upload
+    if (st != KAMERA_OK) return st;
   }
   std::memset(plan, 0, sizeof(*plan));
   plan->workspace = ws;
@@ -671,16 +701,7 @@ kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream) {
   if (!plan) return fail(KAMERA_E_NULL, "plan is NULL");
   if (plan->num_tasks <= 0 || plan->kernel == 0) return KAMERA_OK;
   if (!plan->workspace) return fail(KAMERA_E_WORKSPACE, "plan has no workspace");
-  const DevHeader* hd = reinterpret_cast<const DevHeader*>(plan->workspace);
-  const DevChunk* dc = reinterpret_cast<const DevChunk*>((const char*)plan->workspace +
-                                                         round_up(sizeof(DevHeader), kAlign));
-  hipError_t e;
-  if (plan->kernel == 1) e = launch_mfma(plan->variant, hd, dc, plan->num_tasks, (hipStream_t)stream, nullptr);
-  else if (plan->kernel == 2)
-    e = launch_generic(plan->reserved[0], hd, dc, plan->num_tasks, (hipStream_t)stream, nullptr);
-  else return fail(KAMERA_E_UNSUPPORTED, "plan names unknown kernel %d", plan->kernel);
-  if (e != hipSuccess) return fail(KAMERA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return KAMERA_OK;
+  return launch_main(plan->kernel, plan->variant, plan->reserved[0], plan->num_tasks, plan->workspace, stream);
 }
 
 kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera_chunk* chunks, int32_t num_chunks,

@@ -4,16 +4,17 @@ Produce the raw output with three runs of the committed bench (one for the
 kernel trace, one per counter, as rocprofv3 collects counters in runs of their
 own), then summarise:
 
-    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c2 -- \\
-        python3 bench.py --config C2 --steps 200 --warmup 20 --no-cpu > OUT/trace.log
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o c2 -- \\
-        python3 bench.py --config C2 --steps 5 --warmup 1 --no-cpu
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/prof_write -o c2 -- \\
-        python3 bench.py --config C2 --steps 5 --warmup 1 --no-cpu
-    python3 profile_summary.py OUT C2
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o c4 -- \\
+        python3 bench.py --config C4 --steps 50 --warmup 5 --no-cpu > OUT/trace.log
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/prof_fetch -o c4 -- \\
+        python3 bench.py --config C4 --steps 5 --warmup 1 --no-cpu > OUT/fetch.log
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/prof_write -o c4 -- \\
+        python3 bench.py --config C4 --steps 5 --warmup 1 --no-cpu > OUT/write.log
+    python3 profile_summary.py OUT C4
 
-(the -o prefix is the workload name in lower case; OUT/trace.log holds the traced
-run's bench.py JSON line). For per-token re-anchoring, trace
+(the -o prefix is the workload name in lower case; OUT/trace.log, OUT/fetch.log and
+OUT/write.log hold each run's bench.py JSON line, which counts the operator
+launches of the run: whole calls, plan launches, then the same-pattern copy). For per-token re-anchoring, trace
 `bench.py --config C2 --positions ...` the same way and summarise with
 `python3 profile_summary.py OUT C2 --positions`: the summary then covers the
 variant that reads the per-token cos/sin table, and counter runs are optional
@@ -29,7 +30,6 @@ import csv
 import json
 import os
 import sys
-from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL = "kamera::rehydrate_mfma"
@@ -41,40 +41,44 @@ def _rows(path):
         return list(csv.DictReader(fh))
 
 
-def _per_kernel(rows):
-    agg = defaultdict(list)
-    for r in rows:
-        agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-    return agg
+COPY_LAUNCHES = 13   # bench.py's 1 GiB device copy: 3 untimed + 10 timed, the run's last GPU work
 
 
-def _copy_kib(agg):
-    """Counter of the bench's 1 GiB copy: the copy kernel with the largest grid."""
-    cands = [(g, v) for (k, g), v in agg.items() if "copyBuffer" in k or "copy" in k.lower() and "kamera" not in k]
-    g, v = max(cands, key=lambda x: x[0])
+def _copy_kib(rows):
+    """Counter of the bench's 1 GiB copy: the last COPY_LAUNCHES copy-kernel dispatches of the
+    run (host-to-device staging copies use the same kernel and grid earlier in the run)."""
+    cands = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+    v = [float(r["Counter_Value"]) for r in cands[-COPY_LAUNCHES:]]
+    if max(v) > 1.01 * min(v):
+        raise ValueError(f"the last {COPY_LAUNCHES} copy dispatches disagree: {min(v)} .. {max(v)} KiB")
     return sum(v) / len(v)
 
 
-def _kernel_kib(agg):
-    vals = [v for (k, g), vs in agg.items() if KERNEL in k for v in vs]
+def _own(rows, bench: dict, positions: bool):
+    """The workload's own dispatches of one instantiation, in dispatch order: bench.py ends
+    with its same-pattern copy (the same chunks at delta 0 without a patch, a lighter load),
+    launched through the plain instantiation; those last launches are not the workload's."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    drop = 0 if positions else bench["launches"]["pattern"]
+    return rows[:len(rows) - drop] if drop else rows
+
+
+def _kernel_kib(rows, name: str, bench: dict, positions: bool):
+    own = _own([r for r in rows if r["Kernel_Name"].split("(")[0] == name.split("(")[0]], bench, positions)
+    vals = [float(r["Counter_Value"]) for r in own]
     return sum(vals) / len(vals), len(vals)
 
 
-def _own_average_us(out: str, pre: str, name: str, bench: dict):
-    """Average duration of the workload's own launches of `name`. bench.py launches the
-    uploaded plan K + min(K, 200) times, then runs its same-pattern copy (5 + min(K, 200)
-    launches of the same instantiation at delta 0 without a patch, a lighter load): the
-    first K + min(K, 200) dispatches in time order are the workload's (whole calls that
-    use the same instantiation come before them and are the workload's too)."""
+def _own_average_us(out: str, pre: str, name: str, bench: dict, positions: bool):
+    """Average duration of the workload's own launches of `name` (whole calls and plan
+    launches through that instantiation)."""
     rows = [r for r in _rows(os.path.join(out, "prof_trace", f"{pre}_kernel_trace.csv")) if r["Kernel_Name"] == name]
-    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    own = bench["steps"] + min(bench["steps"], 200)
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[:own]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in _own(rows, bench, positions)]
     return sum(durs) / len(durs), len(durs)
 
 
-def _bench_line(out: str) -> dict:
-    with open(os.path.join(out, "trace.log")) as fh:
+def _bench_line(out: str, log: str = "trace.log") -> dict:
+    with open(os.path.join(out, log)) as fh:
         return json.loads(next(ln for ln in fh if ln.startswith("{")))
 
 
@@ -86,7 +90,7 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
     # reads per-token tables (template flag true); the same-pattern copy in that
     # run is the plain variant and is listed but not summarised
     main_row = next(r for r in stats if KERNEL in r["Name"] and (not positions or ", true>" in r["Name"]))
-    avg_us, n_own = _own_average_us(out, pre, main_row["Name"], bench)
+    avg_us, n_own = _own_average_us(out, pre, main_row["Name"], bench, positions)
     alg = bench["algorithmic_bytes"]
     suffix = "_positions" if positions else ""
     flag = " --positions" if positions else ""
@@ -102,7 +106,7 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
         "## kernel trace (rocprofv3 --kernel-trace --stats)",
         "",
         f"command: rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_trace -o {pre} -- "
-        f"python3 bench.py --config {cfg}{flag} --steps 200 --warmup 20 --no-cpu",
+        f"python3 bench.py --config {cfg}{flag} --steps {bench['steps']} --warmup {bench['warmup']} --no-cpu",
         "",
         "| kernel | calls | average us | min us | max us | share of GPU time |",
         "|---|---|---|---|---|---|",
@@ -121,12 +125,12 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
         f"average ({alg / (avg_us * 1e-6) / 8e12:.1%} of 8000 GB/s)",
     ]
     if have_pmc:
-        fetch = _per_kernel(_rows(os.path.join(out, "prof_fetch", f"{pre}_counter_collection.csv")))
-        write = _per_kernel(_rows(os.path.join(out, "prof_write", f"{pre}_counter_collection.csv")))
+        fetch = _rows(os.path.join(out, "prof_fetch", f"{pre}_counter_collection.csv"))
+        write = _rows(os.path.join(out, "prof_write", f"{pre}_counter_collection.csv"))
         f_copy, w_copy = _copy_kib(fetch), _copy_kib(write)
         f_scale, w_scale = (COPY_BYTES / 1024) / f_copy, (COPY_BYTES / 1024) / w_copy
-        f_k, nf = _kernel_kib(fetch)
-        w_k, nw = _kernel_kib(write)
+        f_k, nf = _kernel_kib(fetch, main_row["Name"], _bench_line(out, "fetch.log"), positions)
+        w_k, nw = _kernel_kib(write, main_row["Name"], _bench_line(out, "write.log"), positions)
         fetch_b = f_k * 1024 * f_scale
         write_b = w_k * 1024 * w_scale
         lines += [
@@ -134,7 +138,8 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
             "## HBM bytes (rocprofv3 --pmc, one counter per run)",
             "",
             f"commands: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUT/prof_fetch|prof_write "
-            f"-o {pre} -- python3 bench.py --config {cfg}{flag} --steps 5 --warmup 1 --no-cpu",
+            f"-o {pre} -- python3 bench.py --config {cfg}{flag} --steps 5 --warmup 1 --no-cpu "
+            f"(the workload's own dispatches of the summarised kernel)",
             "",
             "| counter | plain 1 GiB copy (KiB/dispatch) | scale to bytes | kernel (KiB/dispatch, mean of n) "
             "| kernel bytes |",

@@ -378,3 +378,26 @@ def test_in_place_patch_needs_v_pool_only_for_v_factors():
                    k_src=None, v_src=None, k_dst=None, v_dst=None, factors=[kf, vf])
     name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [with_v], pool, tiny, 0))
     assert name == "KAMERA_E_NULL" and "v_pool" in msg, msg
+
+
+def test_overlap_check_scales_with_the_batch_not_the_pool():
+    """Overlapping pool slots are found from the batch's own page entries: a pool of 2^30
+    pages costs no more than a small one, a repeated page inside one chunk's table is an
+    overlap, and chunks sharing a page on disjoint slots are not."""
+    big_pool = abi.make_pool(FAKE + 0x4000000, FAKE + 0x8000000, num_pages=1 << 30)
+    a = chunk(num_tokens=40, block_table=np.array([5, 1 << 29, 7]), slot0=3, k_dst=None, v_dst=None)
+    b = chunk(num_tokens=20, block_table=np.array([(1 << 30) - 1, 7]), slot0=0, k_dst=None, v_dst=None)
+    t0 = time.perf_counter()
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, b], big_pool, (WS[0], 1), 0))
+    assert time.perf_counter() - t0 < 0.5
+    assert name == "KAMERA_E_OVERLAP" and "chunks 0 and 1" in msg and "page 7" in msg, msg
+    rep = chunk(num_tokens=40, block_table=np.array([4, 6, 4]), slot0=0, k_dst=None, v_dst=None)
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [rep], big_pool, (WS[0], 1), 0))
+    assert name == "KAMERA_E_OVERLAP" and "twice" in msg, msg
+    c = chunk(num_tokens=3, block_table=np.array([7]), slot0=8, k_dst=None, v_dst=None)   # after a's slots 0..10
+    d = chunk(num_tokens=10, block_table=np.array([9, 7]), slot0=10, k_dst=None, v_dst=None)
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, c, d], big_pool, (WS[0], 1), 0))
+    assert name == "KAMERA_E_OVERLAP", msg
+    e = chunk(num_tokens=5, block_table=np.array([7]), slot0=11, k_dst=None, v_dst=None)  # slots 11..15: free
+    name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, e], big_pool, (WS[0], 1), 0))
+    assert name == "KAMERA_E_WORKSPACE", msg

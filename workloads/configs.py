@@ -236,7 +236,7 @@ def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Op
                   tokens: Optional[int] = None, rank: Optional[int] = None,
                   patch: bool = True, max_tokens: Optional[int] = None,
                   patch_layer0: Optional[int] = None, shared_basis: bool = False,
-                  positions: bool = False) -> Workload:
+                  positions: bool = False, page_order: str = "random") -> Workload:
     """Build config `name` (C1..C5). Keyword overrides shrink it for fast tests;
     patch_layer0 makes every factor start at that layer (e.g. L // 2: the deep-half
     patches of the preprint's Table 2, layers below it carry no patch); shared_basis
@@ -244,9 +244,13 @@ def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Op
     deficit's directions are shared across items, only the coefficients U differ);
     positions re-anchors every rehydrated chunk token by token with three-section
     (t, h, w) ids of 64-token frames placed at the chunk's start (QV-PIC Eq. 2: keys
-    stored unrotated, M-RoPE applied with the request positions); survivors keep delta."""
+    stored unrotated, M-RoPE applied with the request positions); survivors keep delta.
+    page_order "physical" gives a paged workload consecutive page ids, chunk after chunk,
+    instead of its seeded random block table (same chunks, same pool size)."""
+    if page_order not in ("random", "physical"):
+        raise ValueError(page_order)
     wl = _make_workload(name, num_layers=num_layers, num_chunks=num_chunks, tokens=tokens, rank=rank,
-                        patch=patch, max_tokens=max_tokens)
+                        patch=patch, max_tokens=max_tokens, page_order=page_order)
     if positions:
         import dataclasses
         wl.layout = dataclasses.replace(wl.layout, mrope_section=mrope_sections(wl.layout.d_rot))
@@ -269,7 +273,7 @@ def make_workload(name: str, *, num_layers: Optional[int] = None, num_chunks: Op
 
 
 def _make_workload(name: str, *, num_layers: Optional[int], num_chunks: Optional[int], tokens: Optional[int],
-                   rank: Optional[int], patch: bool, max_tokens: Optional[int]) -> Workload:
+                   rank: Optional[int], patch: bool, max_tokens: Optional[int], page_order: str) -> Workload:
     root = _ROOT[name]
     if name == "C1":
         lay = LayoutSpec(GQA, F32, num_layers or 1, num_kv_heads=2, head_dim=64, rope_base=10000.0)
@@ -354,6 +358,8 @@ def _make_workload(name: str, *, num_layers: Optional[int], num_chunks: Optional
         pages_needed = [int(-(-int(L_) // P)) for L_ in lens]
         num_pages = int(np.ceil(1.25 * sum(pages_needed)))
         table = np.random.default_rng([root, _P_TABLE]).permutation(num_pages).astype(np.int32)
+        if page_order == "physical":
+            table = np.arange(num_pages, dtype=np.int32)
         F = lay.row_width
         chunks, cursor, pos = [], 0, 0
         for i in range(n):
