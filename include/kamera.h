@@ -227,6 +227,26 @@ kamera_status kamera_plan_upload(const kamera_layout* layout, const kamera_chunk
                                  size_t workspace_bytes, void* stream, kamera_plan* plan);
 kamera_status kamera_plan_launch(const kamera_plan* plan, void* stream);
 
+/* Allocation-free form of kamera_rehydrate_batched, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Arguments, validation, semantics and results are
+ * those of kamera_rehydrate_batched (the same kernels run), but the workspace is a
+ * device array inside the library, one per GPU, of KAMERA_NOALLOC_SCRATCH_BYTES bytes,
+ * held from the first call on that GPU until the process ends. The packed batch travels
+ * to it as kernel arguments (small launches on `stream`), so the call allocates nothing
+ * (no hipMalloc, no pinned staging, no copy engine) and never blocks the host.
+ *   - A batch whose packed chunks, block tables and per-token cos/sin tables need more
+ *     than KAMERA_NOALLOC_SCRATCH_BYTES (kamera_batch_workspace_bytes tells) is rejected
+ *     with KAMERA_E_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU reuses the same array: calls enqueued on one stream are
+ *     ordered and safe; calls whose work may overlap in time on one GPU (other streams,
+ *     other threads) race and must not be issued.
+ *   - KAMERA_E_HIP after a successful validation can follow partly enqueued work (an
+ *     earlier launch of the same call). */
+enum { KAMERA_NOALLOC_SCRATCH_BYTES = 4194304 };
+kamera_status kamera_rehydrate_batched_noalloc(const kamera_layout* layout, const kamera_chunk* chunks,
+                                               int32_t num_chunks, const kamera_pool* pool, void* stream);
+
 /* Patch builder (the compile step; preprint §2 Eq. 2 and App. A): forms the deficit
  *     Delta = x_cond - R(delta) x_canon
  * on columns [col0, col0 + width) of one layer's rows of one tensor and returns its

@@ -25,12 +25,13 @@ MAX_RANK = 256
 BUILD_MAX_RANK = 64
 BUILD_MAX_SUBSPACE = 80
 BUILD_MAX_ORBIT = 32
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAMERA_E_RANK",
           "KAMERA_E_DELTA", "KAMERA_E_PAGE", "KAMERA_E_OVERLAP", "KAMERA_E_ALIGN",
           "KAMERA_E_WORKSPACE", "KAMERA_E_UNSUPPORTED", "KAMERA_E_HIP"]
 EXPORTED = ["kamera_workspace_bytes", "kamera_batch_workspace_bytes", "kamera_relocate", "kamera_rehydrate",
-            "kamera_rehydrate_batched",
+            "kamera_rehydrate_batched", "kamera_rehydrate_batched_noalloc",
             "kamera_plan_upload", "kamera_plan_launch", "kamera_status_string", "kamera_last_error",
             "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch", "kamera_build_orbit_patch"]
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.kamera_rehydrate.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), ctypes.POINTER(Pool), vp, sz, vp]
         L.kamera_rehydrate_batched.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), i32,
                                                ctypes.POINTER(Pool), vp, sz, vp]
+        L.kamera_rehydrate_batched_noalloc.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), i32,
+                                                       ctypes.POINTER(Pool), vp]
         L.kamera_plan_upload.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(Chunk), i32, ctypes.POINTER(Pool),
                                          vp, sz, vp, ctypes.POINTER(Plan)]
         L.kamera_plan_launch.argtypes = [ctypes.POINTER(Plan), vp]
@@ -105,7 +108,8 @@ def lib() -> ctypes.CDLL:
         L.kamera_build_orbit_patch.argtypes = [ctypes.POINTER(Layout), i32, i32, ctypes.POINTER(vp),
                                                ctypes.POINTER(i64), vp, i64, i32, i32, i32, i32, vp, vp, vp, vp,
                                                sz, vp]
-        for fn in ("kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched", "kamera_plan_upload",
+        for fn in ("kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
+                   "kamera_rehydrate_batched_noalloc", "kamera_plan_upload",
                    "kamera_plan_launch", "kamera_build_patch", "kamera_build_orbit_patch"):
             getattr(L, fn).restype = ctypes.c_int
         L.kamera_status_string.argtypes = [ctypes.c_int]
@@ -257,6 +261,13 @@ def rehydrate_batched(layout: Layout, chunks: Sequence, pool: Optional[Pool], wo
     wp, wb = _ws(workspace)
     _check(lib().kamera_rehydrate_batched(ctypes.byref(layout), arr, n, ctypes.byref(pool) if pool else None,
                                           wp, wb, _stream(stream)))
+
+
+def rehydrate_batched_noalloc(layout: Layout, chunks: Sequence, pool: Optional[Pool], stream=None) -> None:
+    """kamera_rehydrate_batched without a workspace: the library's per-device scratch array serves."""
+    arr, n = _chunk_array(chunks)
+    _check(lib().kamera_rehydrate_batched_noalloc(ctypes.byref(layout), arr, n, ctypes.byref(pool) if pool else None,
+                                                  _stream(stream)))
 
 
 class PreparedBatch:

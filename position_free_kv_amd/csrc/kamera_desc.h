@@ -136,4 +136,9 @@ struct InlineBatch {
 // kernel arguments, with the runtime's 256 bytes of implicit ones, stay within 4 KB
 static_assert(sizeof(InlineBatch) + 256 <= 4096, "kernel arguments are limited to 4 KB");
 
+// Scratch array of the allocation-free entry point (one per device, in kamera_kernels.hip):
+// it stands in for the caller's workspace, so it holds at most this many bytes of packed
+// batch, block tables and per-token cos/sin tables.
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+
 }  // namespace kamera

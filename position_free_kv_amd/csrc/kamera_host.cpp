@@ -23,6 +23,8 @@ hipError_t launch_generic(int dtype, const DevHeader* hdr, const DevChunk* chunk
 hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t per_chunk,
                               hipStream_t stream, const InlineBatch* inl);
+hipError_t scratch_address(void** out);
+hipError_t launch_fill_by_argument(void* dst, const void* src, size_t bytes, hipStream_t stream);
 }  // namespace kamera
 
 using namespace kamera;
@@ -714,6 +716,38 @@ kamera_status kamera_rehydrate_batched(const kamera_layout* layout, const kamera
   kamera_status st = kamera_plan_upload(layout, chunks, num_chunks, pool, workspace, workspace_bytes, stream, &plan);
   if (st != KAMERA_OK) return st;
   return kamera_plan_launch(&plan, stream);
+}
+
+static_assert(KAMERA_NOALLOC_SCRATCH_BYTES == kNoallocScratchBytes, "scratch limit of the ABI and the library");
+
+kamera_status kamera_rehydrate_batched_noalloc(const kamera_layout* layout, const kamera_chunk* chunks,
+                                               int32_t num_chunks, const kamera_pool* pool, void* stream) {
+  g_last_error.clear();
+  thread_local std::vector<unsigned char> blob;
+  thread_local std::vector<int64_t> page_off;
+  thread_local std::vector<int64_t> phase_off;
+  Packed pk{blob, page_off, phase_off};
+  kamera_status st = pack_batch(layout, chunks, num_chunks, pool, pk);
+  if (st != KAMERA_OK) return st;
+  if (pk.bytes > kNoallocScratchBytes)
+    return fail(KAMERA_E_WORKSPACE,
+                "the batch needs %zu bytes of scratch (packed chunks, block tables, cos/sin tables); "
+                "kamera_rehydrate_batched_noalloc holds at most %zu: split the batch, or pass a workspace to "
+                "kamera_rehydrate_batched",
+                pk.bytes, kNoallocScratchBytes);
+  if (pk.tasks == 0) return KAMERA_OK;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "device address of the scratch array: %s", hipGetErrorString(e));
+  // a small dense batch goes as the kernels' argument (only cos/sin tables use the scratch)
+  kamera_status st0 = KAMERA_OK;
+  if (launch_inline(layout, chunks, num_chunks, pool, ws, kNoallocScratchBytes, stream, &st0)) return st0;
+  bind_workspace(pk, num_chunks, ws);
+  const hipError_t ef = launch_fill_by_argument(ws, pk.blob.data(), pk.upload_bytes, (hipStream_t)stream);
+  if (ef != hipSuccess) return fail(KAMERA_E_HIP, "scratch fill launch failed: %s", hipGetErrorString(ef));
+  st = launch_phase_tables(pk, num_chunks, ws, stream);
+  if (st != KAMERA_OK) return st;
+  return launch_main(pk.kernel, pk.variant, layout->dtype, pk.tasks, ws, stream);
 }
 
 kamera_status kamera_rehydrate(const kamera_layout* layout, const kamera_chunk* chunk, const kamera_pool* pool,

@@ -31,6 +31,10 @@
 //   per task with that same column map.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
 
 #include "kamera_desc.h"
 
@@ -796,6 +800,73 @@ __global__ __launch_bounds__(kBlockThreads) void copy_in(const u32x4* __restrict
                                                          int64_t n16) {
   const int64_t i = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   if (i < n16) dst[i] = src[i];
+}
+
+// ============================================================================
+// Scratch of the allocation-free entry point (kamera_rehydrate_batched_noalloc)
+// ============================================================================
+// Stands in for the caller's workspace: packed batch (header, chunk records, block
+// tables) and the per-token cos/sin tables of re-anchored chunks. Each GPU the library
+// runs on holds its own copy until the process ends. Every call on a device uses it from
+// offset 0, so calls that overlap in time on one device race; calls on one stream are
+// ordered. Nothing in it has to start at zero: a call writes every byte the kernels read
+// (the whole packed region, and every entry of every table it reads).
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per device with that
+// device current. (In host code the array's own name is a host-side stand-in, never a
+// device address: only this address may reach a kernel or a copy.)
+constexpr int kScratchDevices = 64;
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kScratchDevices];
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Host bytes moved into device memory by the launch itself: the kernel's argument carries
+// up to kFill16 16-byte words and one thread stores each, so no staging buffer, host
+// allocation or copy engine is involved.
+constexpr int kFill16 = 232;
+struct FillArg {
+  u32x4 data[kFill16];
+  u32x4* dst;
+  uint32_t n16;
+  uint32_t pad;
+};
+static_assert(sizeof(FillArg) + 256 <= 4096, "kernel arguments are limited to 4 KB");
+static_assert(kFill16 <= kBlockThreads, "one thread per word");
+
+__global__ __launch_bounds__(kBlockThreads) void fill_by_argument(const FillArg a) {
+  if (threadIdx.x < a.n16) a.dst[threadIdx.x] = a.data[threadIdx.x];
+}
+
+// `bytes` a multiple of 16; src host memory (read during the call), dst device memory
+hipError_t launch_fill_by_argument(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  FillArg a;
+  memset(&a, 0, sizeof(a));
+  for (size_t off = 0; off < bytes; off += (size_t)kFill16 * 16) {
+    const size_t n = std::min(bytes - off, (size_t)kFill16 * 16);
+    memcpy(a.data, (const unsigned char*)src + off, n);
+    a.dst = (u32x4*)((unsigned char*)dst + off);
+    a.n16 = (uint32_t)(n / 16);
+    hipLaunchKernelGGL(fill_by_argument, dim3(1), dim3(kBlockThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ============================================================================

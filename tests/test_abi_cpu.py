@@ -380,6 +380,21 @@ def test_in_place_patch_needs_v_pool_only_for_v_factors():
     assert name == "KAMERA_E_NULL" and "v_pool" in msg, msg
 
 
+def test_noalloc_rejects_batches_beyond_its_scratch():
+    """The allocation-free entry point validates the batch like kamera_rehydrate_batched, then
+    rejects one whose packed form and cos/sin tables exceed its fixed scratch, before any HIP
+    call (so the fake addresses are never touched)."""
+    lay = gqa_layout(mrope_section=(16, 24, 24))
+    name, _ = status_of(lambda: abi.rehydrate_batched_noalloc(lay, [chunk(delta=1 << 31)], None, 0))
+    assert name == "KAMERA_E_DELTA"
+    big = chunk(num_tokens=10000, flags=abi.POSITIONS, positions=FAKE + 0x900000)   # 5 MB of cos/sin table
+    assert abi.batch_workspace_bytes(lay, [big]) > abi.NOALLOC_SCRATCH_BYTES
+    name, msg = status_of(lambda: abi.rehydrate_batched_noalloc(lay, [big], None, 0))
+    assert name == "KAMERA_E_WORKSPACE" and "at most" in msg, msg
+    name, _ = status_of(lambda: abi.rehydrate_batched_noalloc(lay, [], None, 0))   # nothing to do
+    assert name == "KAMERA_OK"
+
+
 def test_overlap_check_scales_with_the_batch_not_the_pool():
     """Overlapping pool slots are found from the batch's own page entries: a pool of 2^30
     pages costs no more than a small one, a repeated page inside one chunk's table is an

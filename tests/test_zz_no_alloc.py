@@ -1,0 +1,81 @@
+"""kamera_rehydrate_batched_noalloc against kamera_rehydrate_batched (same kernels, so the
+outputs must be byte-identical), through the C ABI, two calls in a row, the second on a
+smaller batch: a paged deque batch with in-place survivors (packed batch filled into the
+library's scratch by kernel arguments), a small dense batch (the kernel-argument route), and
+re-anchored batches whose per-token cos/sin tables live in the scratch."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import say
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from position_free_kv_amd import abi
+    abi.lib()   # fails loudly when the HIP library is missing
+    yield
+
+
+def _outputs(dw):
+    """Every destination byte of the workload: dense buffers and pool pages."""
+    out = [t.clone() for bufs in dw.dense for t in bufs]
+    if dw.pool is not None:
+        out += [t.clone() for t in dw.pool]
+    return out
+
+
+def _restore(dw, snap):
+    k = 0
+    for bufs in dw.dense:
+        for t in bufs:
+            t.copy_(snap[k])
+            k += 1
+    if dw.pool is not None:
+        for t in dw.pool:
+            t.copy_(snap[k])
+            k += 1
+
+
+def _same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+CASES = [
+    ("deque paged, in place", dict(name="C5", num_layers=3, num_chunks=12, max_tokens=300), [0, 1, 2, 3, 4]),
+    ("dense small batch", dict(name="C2", num_layers=2, num_chunks=3, tokens=200), [1]),
+    ("dense re-anchored", dict(name="C2", num_layers=2, num_chunks=2, tokens=160, positions=True), [0]),
+    ("deque re-anchored", dict(name="C5", num_layers=2, num_chunks=8, max_tokens=260, positions=True), [2, 5, 6]),
+    ("MLA rows", dict(name="C3", num_layers=2, num_chunks=18, tokens=64), [3, 4]),
+]
+
+
+@pytest.mark.parametrize("label,kw,subset", CASES, ids=[c[0] for c in CASES])
+def test_noalloc_matches_workspace_entry_point(label, kw, subset):
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    kw = dict(kw)
+    wl = make_workload(kw.pop("name"), **kw)
+    dw = DeviceWorkload(wl, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    fresh = _outputs(dw)
+    for call, idx in enumerate([list(range(len(wl.chunks))), subset]):
+        descs = [dw.descs[i] for i in idx]
+        need = abi.batch_workspace_bytes(dw.layout, descs)
+        say(f"[noalloc] {label}: call {call}, {len(descs)} chunks, {need} bytes of scratch")
+        assert need <= abi.NOALLOC_SCRATCH_BYTES
+        _restore(dw, fresh)
+        abi.rehydrate_batched(dw.layout, descs, dw.pool_desc, dw.workspace, stream)
+        torch.cuda.synchronize()
+        want = _outputs(dw)
+        assert not _same(want, fresh), "the batch changed nothing"
+        _restore(dw, fresh)
+        abi.rehydrate_batched_noalloc(dw.layout, descs, dw.pool_desc, stream)
+        torch.cuda.synchronize()
+        got = _outputs(dw)
+        assert _same(got, want), f"{label}: call {call} differs from kamera_rehydrate_batched"
+    say(f"[noalloc] {label}: both calls byte-identical")
