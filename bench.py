@@ -276,6 +276,9 @@ def main() -> int:
     ap.add_argument("--positions", action="store_true",
                     help="re-anchor every rehydrated chunk token by token with (t, h, w) M-RoPE ids "
                          "(64-token frames on an 8 x 8 grid at the chunk's start) instead of one delta")
+    ap.add_argument("--patch-unit", choices=("auto", "mfma", "valu"), default="auto",
+                    help="unit that adds the patch in the bf16 kernel: the library's choice (auto, the matrix "
+                         "cores), the matrix cores, or VALU dot products (128-wide heads, rank <= 64)")
     ap.add_argument("--page-order", choices=("random", "physical"), default="random",
                     help="paged workloads: the seeded random block table (default), or the same chunks with "
                          "their pages numbered in physical order (consecutive page ids, chunk after chunk)")
@@ -299,7 +302,8 @@ def main() -> int:
     if args.page_order != "random":
         make_kw["page_order"] = args.page_order
     wl = make_workload(args.config, **make_kw)
-    variant = args.deep_half or args.shared_basis or args.positions or args.page_order != "random"
+    variant = (args.deep_half or args.shared_basis or args.positions or args.page_order != "random"
+               or args.patch_unit != "auto")
     if args.deep_half or args.shared_basis or args.positions:
         make_kw.update(shared_basis=args.shared_basis, positions=args.positions,
                        patch_layer0=wl.layout.num_layers // 2 if args.deep_half else None)
@@ -321,19 +325,23 @@ def main() -> int:
     abi.lib()
     t_stage = time.perf_counter()
     dw = DeviceWorkload(wl)
+    dw.layout.patch_unit = {"auto": abi.PATCH_UNIT_AUTO, "mfma": abi.PATCH_UNIT_MFMA,
+                            "valu": abi.PATCH_UNIT_VALU}[args.patch_unit]
     print(f"# staged {args.config} in {time.perf_counter() - t_stage:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
     batch = dw.prepared(stream)   # arguments marshalled once; every call validates, uploads, launches
-    for _ in range(args.warmup):
-        batch.call()
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    # ---- whole calls (validation + descriptor upload + kernel): the step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Collected before the warmup, not after it: a pause between the warmup and the timed
+    # steps leaves the GPU idle long enough to lower its clocks, and the first timed
+    # launches then run up to 12% slower (seen in kernel traces of this loop).
     gc.collect()
     gc.disable()   # no collector pauses inside the timed loops
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        batch.call()
+    print(f"# warmup issued ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # ---- whole calls (validation + descriptor upload + kernel): the step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
@@ -373,9 +381,11 @@ def main() -> int:
     # ---- the same chunks at delta 0 without a patch: a plain copy through the
     # kernel's own access pattern, the practical ceiling for this workload's layout
     pattern_gbps = None
+    pattern_variant = None
     cbytes = dw.copy_bytes()
     if cbytes > 0:
         cplan = abi.plan_upload(dw.layout, dw.copy_descs(), dw.pool_desc, dw.workspace, stream)
+        pattern_variant = cplan.variant
         for _ in range(PATTERN_WARMUP):
             abi.plan_launch(cplan, stream)
         e6, e7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -430,7 +440,8 @@ def main() -> int:
                    + (" (one V basis per layer shared by all chunks)" if args.shared_basis else "")
                    + (" (per-token (t, h, w) re-anchoring, M-RoPE sections %s)" % (wl.layout.mrope_section,)
                       if args.positions else "")
-                   + (" (block table in physical page order)" if args.page_order == "physical" else ""),
+                   + (" (block table in physical page order)" if args.page_order == "physical" else "")
+                   + (f" (patch on the {args.patch_unit.upper()})" if args.patch_unit != "auto" else ""),
                    "name": args.config, "chunks": len(wl.chunks),
                    "tokens": tokens, "layers": wl.layout.num_layers, "row_width": wl.layout.row_width},
         "roofline": dict({"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -442,7 +453,8 @@ def main() -> int:
         "kernel_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         # operator launches in this run, in order: whole calls, plan launches, same-pattern copy
         "launches": {"calls": args.warmup + args.steps, "plan": PLAN_WARMUP + n_kernel + n_dist,
-                     "pattern": (PATTERN_WARMUP + n_dist) if cbytes > 0 else 0},
+                     "pattern": (PATTERN_WARMUP + n_dist) if cbytes > 0 else 0,
+                     "plan_variant": plan.variant, "pattern_variant": pattern_variant},
         "pattern_copy_GBps": pattern_gbps,
         "frac_of_pattern_copy": (achieved / pattern_gbps) if pattern_gbps else None,
         "call_us_gpu": call_ms_gpu * 1e3,
@@ -450,6 +462,7 @@ def main() -> int:
         "kernel_tokens_per_s": tokens / (kernel_us * 1e-6),
         "torch_copy_GBps": copy_gbps,
         "kernel_source_hash": kernel_source_hash(),
+        "argv": sys.argv[1:],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

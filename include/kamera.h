@@ -102,6 +102,18 @@ enum {
 
 enum { KAMERA_MAX_FACTORS = 4, KAMERA_MAX_RANK = 256 };
 
+/* Unit that adds the rank-m patch in the bf16 kernel (64- or 128-wide heads, or MLA rows
+ * with a 64-wide rope band); every other layout runs a plain fp32 FMA kernel.
+ *   AUTO  the library's choice: the matrix cores (v_mfma_f32_16x16x32_bf16), measured as
+ *         fast or faster than the VALU form at every rank (1 to 64) on the 28-layer
+ *         4 x 128 GQA batch;
+ *   MFMA  the matrix cores; KAMERA_E_UNSUPPORTED if the batch cannot run on that kernel;
+ *   VALU  vector ALU dot products (v_dot2c_f32_bf16 with row broadcasts of the V factor),
+ *         built for bf16 GQA/MHA with 128-wide heads, at most 64 ranks per column group and
+ *         no KAMERA_POSITIONS chunk; else KAMERA_E_UNSUPPORTED.
+ * The two units accumulate in a different order; both meet the same tolerance. */
+enum { KAMERA_PATCH_UNIT_AUTO = 0, KAMERA_PATCH_UNIT_MFMA = 1, KAMERA_PATCH_UNIT_VALU = 2 };
+
 typedef struct kamera_layout {
   int32_t family;        /* KAMERA_GQA or KAMERA_MLA                                      */
   int32_t dtype;         /* KAMERA_BF16 or KAMERA_F32 (all tensors of a call share it)    */
@@ -112,7 +124,7 @@ typedef struct kamera_layout {
   int32_t rope_dim;      /* MLA: k_rope width, even, >= 2                                 */
   int32_t pairing;       /* KAMERA_NEOX or KAMERA_GPTJ                                    */
   int32_t page_size;     /* tokens per pool page (>= 1); used by paged destinations       */
-  int32_t reserved;      /* must be 0                                                     */
+  int32_t patch_unit;    /* KAMERA_PATCH_UNIT_*: which unit adds the patch (see below)     */
   double rope_base;      /* RoPE base (> 0, finite), e.g. 1e4 or 1e6                      */
   int32_t mrope_section[3];  /* KAMERA_POSITIONS chunks: rotary pairs driven by the t, h and w
                                 offsets, blocked in that order (sum = d_rot / 2, e.g. 16, 24, 24

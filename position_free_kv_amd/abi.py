@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("KAMERA_LIBRARY") or os.path.join(_HERE, "libkamera.so
 GQA, MLA = 0, 1
 F32, BF16 = 0, 1
 NEOX, GPTJ = 0, 1
+PATCH_UNIT_AUTO, PATCH_UNIT_MFMA, PATCH_UNIT_VALU = 0, 1, 2
 PATCH, IN_PLACE, POSITIONS = 1, 2, 4
 MAX_FACTORS = 4
 MAX_RANK = 256
@@ -40,7 +41,7 @@ class Layout(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int32), ("dtype", ctypes.c_int32), ("num_layers", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("latent_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("pairing", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("page_size", ctypes.c_int32), ("patch_unit", ctypes.c_int32), ("rope_base", ctypes.c_double),
                 ("mrope_section", ctypes.c_int32 * 3), ("reserved2", ctypes.c_int32)]
 
 
@@ -153,9 +154,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_layout(family: int, dtype: int, num_layers: int, *, num_kv_heads: int = 0, head_dim: int = 0,
                 latent_dim: int = 0, rope_dim: int = 0, pairing: int = NEOX, rope_base: float = 10000.0,
-                page_size: int = 16, mrope_section: Sequence[int] = (0, 0, 0)) -> Layout:
-    return Layout(family, dtype, num_layers, num_kv_heads, head_dim, latent_dim, rope_dim, pairing, page_size, 0,
-                  float(rope_base), (ctypes.c_int32 * 3)(*[int(v) for v in mrope_section]), 0)
+                page_size: int = 16, mrope_section: Sequence[int] = (0, 0, 0),
+                patch_unit: int = PATCH_UNIT_AUTO) -> Layout:
+    return Layout(family, dtype, num_layers, num_kv_heads, head_dim, latent_dim, rope_dim, pairing, page_size,
+                  int(patch_unit), float(rope_base), (ctypes.c_int32 * 3)(*[int(v) for v in mrope_section]), 0)
 
 
 class ChunkDesc:

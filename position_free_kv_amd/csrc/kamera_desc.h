@@ -28,6 +28,7 @@ constexpr int kMaxFactors = 4;
 // v = (slabs - 1) * 4 + log2(k-step capacity), capacity in {1, 2, 4, 8}.
 constexpr int kMaxKSteps = 8;
 constexpr int kVariantPositions = 8;   // added to the variant: batches with per-token offsets
+constexpr int kVariantValu = 16;       // added to the variant: the patch on the VALU instead of the MFMA
 constexpr int kMfmaRangeTokens = 128;  // tokens per wave task (8 tiles)
 
 struct alignas(16) DevFactor {

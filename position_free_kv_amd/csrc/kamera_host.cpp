@@ -130,7 +130,8 @@ kamera_status check_layout(const kamera_layout* L) {
   if (L->pairing != KAMERA_NEOX && L->pairing != KAMERA_GPTJ)
     return fail(KAMERA_E_UNSUPPORTED, "unknown pairing %d", L->pairing);
   if (L->page_size < 1) return fail(KAMERA_E_SHAPE, "page_size must be >= 1 (got %d)", L->page_size);
-  if (L->reserved != 0) return fail(KAMERA_E_SHAPE, "layout.reserved must be 0");
+  if (L->patch_unit < KAMERA_PATCH_UNIT_AUTO || L->patch_unit > KAMERA_PATCH_UNIT_VALU)
+    return fail(KAMERA_E_UNSUPPORTED, "unknown patch_unit %d", L->patch_unit);
   if (!(L->rope_base > 0.0) || !std::isfinite(L->rope_base))
     return fail(KAMERA_E_SHAPE, "rope_base must be positive and finite");
   if (L->reserved2 != 0) return fail(KAMERA_E_SHAPE, "layout.reserved2 must be 0");
@@ -361,6 +362,13 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   const bool wide = L->family == KAMERA_GQA && L->head_dim == 128;
   if (mfma && need_ksteps > (wide ? kMaxKSteps / 2 : kMaxKSteps)) mfma = false;
   if (mfma && any_positions && need_ksteps > (wide ? 2 : 4)) mfma = false;
+  if (L->patch_unit == KAMERA_PATCH_UNIT_MFMA && !mfma)
+    return fail(KAMERA_E_UNSUPPORTED, "patch_unit MFMA: this batch cannot run on the bf16 matrix-core kernel "
+                                      "(dtype, head width, alignment or more k-steps than it holds)");
+  const bool valu = L->patch_unit == KAMERA_PATCH_UNIT_VALU;
+  if (valu && !(mfma && wide && !any_positions && need_ksteps <= 2))
+    return fail(KAMERA_E_UNSUPPORTED, "patch_unit VALU is built for bf16 GQA/MHA with 128-wide heads, at most 64 "
+                                      "ranks per column group and no KAMERA_POSITIONS chunk");
 
   // -------------------------------------------------------------- pack
   out.upload_bytes = ws_bytes(n, total_pages);
@@ -518,7 +526,8 @@ kamera_status pack_batch(const kamera_layout* L, const kamera_chunk* chunks, int
   if (mfma) {
     int cap_log2 = 0;
     while ((1 << cap_log2) < need_ksteps) ++cap_log2;
-    out.variant = (hd->group_cols / kSlab - 1) * 4 + cap_log2 + (out.positions ? kVariantPositions : 0);
+    out.variant = (hd->group_cols / kSlab - 1) * 4 + cap_log2 + (out.positions ? kVariantPositions : 0) +
+                  (valu ? kVariantValu : 0);
   }
   return KAMERA_OK;
 }

@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <utility>
 
 #include "kamera_desc.h"
 
@@ -202,7 +203,28 @@ struct Geo {
   static constexpr int LDS = 16 * RS;          // bytes per wave
 };
 
-template <int NSLAB, int NK, bool POS, typename C>
+// VALU form of the patch (the alternative to the MFMA contraction, for 128-wide heads): lane
+// (lg, c) holds token c's 16 * NSLAB columns x[k] (the MFMA layout), its own U pairs uw[jp] =
+// U[c][2jp, 2jp+1], and for each of its columns the V pair of rank pair c, vv[k] = V[col][2c,
+// 2c+1] as bf16x2. A row broadcast (DPP row_newbcast:jp) hands every lane of the row lane jp's
+// V pair, and v_dot2c_f32_bf16 adds both products to the fp32 value: 2 instructions per pair
+// and column, 1024 per tile at rank 32.
+template <int NSLAB, int JP>
+__device__ __forceinline__ void valu_pair(float* x, const uint32_t* vv, uint32_t u2) {
+  const bf16x2 u = __builtin_bit_cast(bf16x2, u2);
+#pragma unroll
+  for (int k = 0; k < NSLAB * 16; ++k) {
+    const int b = __builtin_amdgcn_mov_dpp((int)vv[k], 0x150 + JP, 0xf, 0xf, true);
+    x[k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, b), u, x[k], false);
+  }
+}
+template <int NSLAB, int... JP>
+__device__ __forceinline__ void valu_patch(float* x, const uint32_t* vv, const uint32_t* uw, int npairs,
+                                           std::integer_sequence<int, JP...>) {
+  ((JP < npairs ? valu_pair<NSLAB, JP>(x, vv, uw[JP]) : void()), ...);
+}
+
+template <int NSLAB, int NK, bool POS, bool VALU, typename C>
 __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int layer, int tensor,
                                           int colbase, int tok0, int ntiles, int rot, const int* kfac,
                                           const int* kstep, int lane, unsigned char* lds) {
@@ -333,12 +355,46 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
   }
 
   // ---- V operands: A[M][k] = V[col(M)][k] for every slab, tile and k-step
-  bf16x8 av[NK > 0 ? NSLAB * 4 * NK : 1];
+  bf16x8 av[(NK > 0 && !VALU) ? NSLAB * 4 * NK : 1];
   const uint16_t* ubase[NK > 0 ? NK : 1];
   int urank[NK > 0 ? NK : 1], ustride[NK > 0 ? NK : 1];
   bool uvec[NK > 0 ? NK : 1];
+  // VALU form: V pairs, U rows of 32 coefficients per k-step, and the pairs inside the rank
+  uint32_t vv[(VALU && NK > 0) ? NK * NSLAB * 16 : 1];
+  const uint16_t* uvbase[(VALU && NK > 0) ? NK : 1];
+  int uvrem[(VALU && NK > 0) ? NK : 1], vpairs[(VALU && NK > 0) ? NK : 1];
+  if constexpr (VALU) {
 #pragma unroll
-  for (int j = 0; j < NK; ++j) {
+    for (int j = 0; j < NK; ++j) {
+      const DevFactor& f = ch.fac[kfac[j]];
+      const int64_t lrel = layer - f.layer0;
+      const uint16_t* vf = (const uint16_t*)f.v + lrel * f.width * f.rank;
+      uvec[j] = f.uvec != 0;
+      uvrem[j] = f.rank - 32 * kstep[j];
+      vpairs[j] = min(16, (uvrem[j] + 1) >> 1);
+      uvbase[j] = (const uint16_t*)f.u + lrel * T * f.rank + 32 * kstep[j];
+      ustride[j] = f.rank;
+      const int k0 = 32 * kstep[j] + 2 * c;   // this lane's rank pair
+#pragma unroll
+      for (int s = 0; s < NSLAB; ++s)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rel = colbase + 64 * s + 32 * r + 8 * lg + e - f.col0;
+            const bool in = rel >= 0 && rel < f.width && k0 < f.rank;
+            uint32_t w = 0;
+            if (in) {
+              const uint16_t* p = vf + (int64_t)rel * f.rank + k0;
+              if (f.vvec) w = *(const uint32_t*)p;   // rank % 8 == 0: the pair is whole and aligned
+              else w = (uint32_t)p[0] | (k0 + 1 < f.rank ? (uint32_t)p[1] << 16 : 0u);
+            }
+            vv[j * NSLAB * 16 + 16 * s + 8 * r + e] = w;
+          }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < (VALU ? 0 : NK); ++j) {
     const DevFactor& f = ch.fac[kfac[j]];
     const int64_t lrel = layer - f.layer0;
     const uint16_t* vf = (const uint16_t*)f.v + lrel * f.width * f.rank;
@@ -395,8 +451,34 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
   };
 
 
-  if (!kNoPf) load_u(0, ucur);
+  // VALU form: token c's 32 coefficients of each k-step as 16 bf16x2 words, zero past the rank
+  uint32_t uw[(VALU && NK > 0) ? NK * 16 : 1];
+  auto load_uw = [&](int tile) {
+    const int t = min(tok0 + tile * kTileTokens + c, T - 1);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const uint16_t* p = uvbase[j] + (int64_t)t * ustride[j];
+      if (uvec[j]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 w = 8 * q < uvrem[j] ? *(const u32x4*)(p + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) uw[j * 16 + 4 * q + i] = w[i];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t lo = 2 * e < uvrem[j] ? (uint32_t)p[2 * e] : 0u;
+          const uint32_t hi = 2 * e + 1 < uvrem[j] ? (uint32_t)p[2 * e + 1] << 16 : 0u;
+          uw[j * 16 + e] = lo | hi;
+        }
+      }
+    }
+  };
+
+  if (!kNoPf && !VALU) load_u(0, ucur);
   for (int tile = 0; tile < ntiles; ++tile) {
+    if constexpr (VALU) load_uw(tile);
     if (kNoPf) {
       load_rows(tile, cur);
       load_u(tile, ucur);
@@ -405,7 +487,7 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
       if (kPrefetchPhase && tok_phase && tile + 1 < ntiles) load_phase(tile + 1, pcs, psn);
     } else if (tile + 1 < ntiles) {
       load_rows(tile + 1, nxt);
-      load_u(tile + 1, unxt);
+      if constexpr (!VALU) load_u(tile + 1, unxt);
       if (kPrefetchPhase && tok_phase) load_phase(tile + 1, pcs, psn);
     }
     if (!kPrefetchPhase && tok_phase && tile > 0) load_phase(tile, cs, sn);
@@ -457,7 +539,11 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
           x[2 * j + 1] = fmaf(a, sn[j], b * cs[j]);
         }
       }
-      if constexpr (NK > 0) {
+      if constexpr (NK > 0 && VALU) {
+#pragma unroll
+        for (int j = 0; j < NK; ++j)
+          valu_patch<NSLAB>(x, vv + j * NSLAB * 16, uw + j * 16, vpairs[j], std::make_integer_sequence<int, 16>{});
+      } else if constexpr (NK > 0) {
 #pragma unroll
         for (int set = 0; set < NSLAB * 4; ++set) {
           f32x4 acc = {x[4 * set], x[4 * set + 1], x[4 * set + 2], x[4 * set + 3]};
@@ -506,8 +592,10 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
 #pragma unroll
         for (int i = 0; i < G::NI; ++i) nxt[i] = nxt2[i];
       }
+      if constexpr (!VALU) {
 #pragma unroll
-      for (int j = 0; j < NK; ++j) ucur[j] = unxt[j];
+        for (int j = 0; j < NK; ++j) ucur[j] = unxt[j];
+      }
       if (kPrefetchPhase && tok_phase) {
 #pragma unroll
         for (int j = 0; j < NSLAB * 8; ++j) {
@@ -519,14 +607,15 @@ __device__ __forceinline__ void mfma_task(const DevHeader& hd, const C& ch, int 
   }
 }
 
-template <int NSLAB, int NKMAX, bool POS, typename C>
+template <int NSLAB, int NKMAX, bool POS, bool VALU, typename C>
 __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const C& ch, int layer,
                                               int tensor, int colbase, int tok0, int ntiles, int rot,
                                               const int* kfac, const int* kstep, int lane, unsigned char* lds) {
-#define KAMERA_NK_CASE(N)                                                                                   \
-  case N:                                                                                                  \
-    if constexpr (N <= NKMAX)                                                                              \
-      mfma_task<NSLAB, N, POS, C>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, lds); \
+#define KAMERA_NK_CASE(N)                                                                                      \
+  case N:                                                                                                     \
+    if constexpr (N <= NKMAX)                                                                                 \
+      mfma_task<NSLAB, N, POS, VALU, C>(hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane, \
+                                        lds);                                                                 \
     break;
   switch (nk) {
     KAMERA_NK_CASE(0)
@@ -543,7 +632,7 @@ __device__ __forceinline__ void mfma_dispatch(int nk, const DevHeader& hd, const
 #undef KAMERA_NK_CASE
 }
 
-template <int NSLAB, int NKMAX, bool POS, typename C>
+template <int NSLAB, int NKMAX, bool POS, bool VALU, typename C>
 __device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict__ hdr, const C* __restrict__ chunks,
                                                     unsigned char* lds_all) {
   constexpr int kWaves = mfma_waves_per_block(NSLAB, NKMAX);
@@ -597,25 +686,26 @@ __device__ __forceinline__ void rehydrate_mfma_body(const DevHeader* __restrict_
     }
   }
   if ((ch.flags & 2u) && rot == ROT_NONE && nk == 0) return;  // in place and nothing changes
-  mfma_dispatch<NSLAB, NKMAX, POS, C>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
+  mfma_dispatch<NSLAB, NKMAX, POS, VALU, C>(nk, hd, ch, layer, tensor, colbase, tok0, ntiles, rot, kfac, kstep, lane,
                               lds_all + wave * Geo<NSLAB>::LDS);
 }
 
 // The batch description read from the workspace (plans; paged or re-anchored batches;
 // batches of more than kInlineChunks chunks or with chunks of more than two factors) ...
-template <int NSLAB, int NKMAX, bool POS>
+// VALU: the patch on the VALU (dot2 + row broadcasts) instead of the MFMA; 128-wide heads only.
+template <int NSLAB, int NKMAX, bool POS, bool VALU>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma(
     const DevHeader* __restrict__ hdr, const DevChunk* __restrict__ chunks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
-  rehydrate_mfma_body<NSLAB, NKMAX, POS, DevChunk>(hdr, chunks, lds_all);
+  rehydrate_mfma_body<NSLAB, NKMAX, POS, VALU, DevChunk>(hdr, chunks, lds_all);
 }
 
 // ... or carried by the dispatch as the kernel's argument (small dense batches).
-template <int NSLAB, int NKMAX, bool POS>
+template <int NSLAB, int NKMAX, bool POS, bool VALU>
 __global__ __launch_bounds__((kWaveSize * mfma_waves_per_block(NSLAB, NKMAX))) void rehydrate_mfma_inline(
     const InlineBatch batch) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_all[mfma_waves_per_block(NSLAB, NKMAX) * Geo<NSLAB>::LDS];
-  rehydrate_mfma_body<NSLAB, NKMAX, POS, DevChunkInline>(&batch.hd, batch.ch, lds_all);
+  rehydrate_mfma_body<NSLAB, NKMAX, POS, VALU, DevChunkInline>(&batch.hd, batch.ch, lds_all);
 }
 
 // ============================================================================
@@ -896,18 +986,18 @@ hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int 
 }
 
 // `inl` non-null: the batch travels as the kernel argument (hdr and chunks unused)
-template <int NSLAB, int NKMAX, bool POS = false>
+template <int NSLAB, int NKMAX, bool POS = false, bool VALU = false>
 static hipError_t launch_one(int64_t tasks, hipStream_t stream, const DevHeader* hdr, const DevChunk* chunks,
                              const InlineBatch* inl) {
   constexpr int w = mfma_waves_per_block(NSLAB, NKMAX);
   const int64_t blocks = (tasks + w - 1) / w;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (inl == nullptr) {
-    hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0, stream,
-                       hdr, chunks);
+    hipLaunchKernelGGL((rehydrate_mfma<NSLAB, NKMAX, POS, VALU>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0,
+                       stream, hdr, chunks);
   } else {
-    hipLaunchKernelGGL((rehydrate_mfma_inline<NSLAB, NKMAX, POS>), dim3((unsigned)blocks), dim3(kWaveSize * w), 0,
-                       stream, *inl);
+    hipLaunchKernelGGL((rehydrate_mfma_inline<NSLAB, NKMAX, POS, VALU>), dim3((unsigned)blocks), dim3(kWaveSize * w),
+                       0, stream, *inl);
   }
   return hipGetLastError();
 }
@@ -929,6 +1019,9 @@ hipError_t launch_mfma(int variant, const DevHeader* hdr, const DevChunk* chunks
     case 10: return launch_one<1, 4, true>(tasks, stream, hdr, chunks, inl);
     case 12: return launch_one<2, 1, true>(tasks, stream, hdr, chunks, inl);
     case 13: return launch_one<2, 2, true>(tasks, stream, hdr, chunks, inl);
+    // the patch on the VALU (kVariantValu + the variant above; 128-wide heads, no per-token offsets)
+    case 20: return launch_one<2, 1, false, true>(tasks, stream, hdr, chunks, inl);
+    case 21: return launch_one<2, 2, false, true>(tasks, stream, hdr, chunks, inl);
     default: return hipErrorInvalidValue;
   }
 }

@@ -56,10 +56,13 @@ def _copy_kib(rows):
 
 def _own(rows, bench: dict, positions: bool):
     """The workload's own dispatches of one instantiation, in dispatch order: bench.py ends
-    with its same-pattern copy (the same chunks at delta 0 without a patch, a lighter load),
-    launched through the plain instantiation; those last launches are not the workload's."""
+    with its same-pattern copy (the same chunks at delta 0 without a patch, a lighter load);
+    when that copy runs the same instantiation (same kernel variant), its last launches are
+    not the workload's."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
-    drop = 0 if positions else bench["launches"]["pattern"]
+    ln = bench["launches"]
+    same = ln.get("pattern_variant", ln.get("plan_variant")) == ln.get("plan_variant")
+    drop = 0 if positions or not same else ln["pattern"]
     return rows[:len(rows) - drop] if drop else rows
 
 
@@ -163,6 +166,125 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
     print("\n".join(lines))
 
 
+# ----------------------------------------------------------------------------- counter comparisons
+DERIVED = [
+    ("UTCL1 translation miss rate", "TCP_UTCL1_TRANSLATION_MISS_sum",
+     ("TCP_UTCL1_TRANSLATION_MISS_sum", "TCP_UTCL1_TRANSLATION_HIT_sum")),
+    ("vector L1 -> L2 read latency (cycles per request)", "TCP_TCC_READ_REQ_LATENCY_sum", ("TCP_TCC_READ_REQ_sum",)),
+    ("vector L1 -> L2 write latency (cycles per request)", "TCP_TCC_WRITE_REQ_LATENCY_sum", ("TCP_TCC_WRITE_REQ_sum",)),
+    ("L2 hit rate", "TCC_HIT_sum", ("TCC_HIT_sum", "TCC_MISS_sum")),
+    ("UTCL2 busy share of GPU-active cycles", "GRBM_UTCL2_BUSY", ("GRBM_GUI_ACTIVE",)),
+    ("share of wave cycles waiting on instructions", "SQ_WAIT_INST_ANY", ("SQ_WAVE_CYCLES",)),
+]
+
+
+def counters(out: str, name: str, runs: list) -> None:
+    """Per-dispatch means of rocprofv3 --pmc counters over the workload's own dispatches of the
+    operator kernel, for several runs side by side. Each run is `label=dir`: dir holds pass
+    subdirectories p1, p2, ... (one rocprofv3 --pmc run each, output prefix = the workload name
+    in lower case) and, beside them, dir_p1.log, ... with each pass's bench.py JSON line."""
+    table = {}
+    cmds = []
+    for spec in runs:
+        label, d = spec.rsplit("=", 1)
+        vals = {}
+        k = 1
+        while os.path.isdir(os.path.join(out, d, f"p{k}")):
+            bench = _bench_line(out, f"{d}_p{k}.log")
+            pre = bench["config"]["name"].lower()
+            rows = _rows(os.path.join(out, d, f"p{k}", f"{pre}_counter_collection.csv"))
+            op = [r for r in rows if KERNEL in r["Kernel_Name"]]
+            # the instantiation the workload runs: the one with the most dispatches
+            by_name = {}
+            for r in op:
+                by_name.setdefault(r["Kernel_Name"].split("(")[0], set()).add(r["Dispatch_Id"])
+            main_name = max(by_name, key=lambda n: len(by_name[n]))
+            mine = [r for r in op if r["Kernel_Name"].split("(")[0] == main_name]
+            ids = sorted({int(r["Dispatch_Id"]) for r in mine})
+            drop = bench["launches"]["pattern"]
+            own = set(ids[:len(ids) - drop] if drop else ids)
+            per = {}
+            for r in mine:
+                if int(r["Dispatch_Id"]) in own:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for cn, v in per.items():
+                vals[cn] = sum(v) / len(v)
+            ctrs = sorted(per)
+            flags = " ".join(a for a in ("--page-order physical",) if "physical" in bench["config"]["workload"])
+            cmds.append(f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d OUT/{d}/p{k} -o {pre} -- "
+                        f"python3 bench.py --config {bench['config']['name']} {flags} --steps {bench['steps']} "
+                        f"--warmup {bench['warmup']} --no-cpu --no-copy".replace("  ", " "))
+            k += 1
+        table[label] = vals
+    labels = list(table)
+    names = sorted({c for v in table.values() for c in v})
+    lines = [f"# rocprofv3 counters: {KERNEL}, {name}", "",
+             "Per-dispatch means over the workload's own dispatches of the operator kernel (the same-pattern copy's "
+             "dispatches excluded). Commands (one counter pass each; OUT is the output folder):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "summarised with: python3 profile_summary.py " + " ".join(f'"{a}"' if " " in a else a
+                                                                for a in sys.argv[1:])]
+    lines += ["", "| counter | " + " | ".join(labels) + " |", "|---|" + "---|" * len(labels)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(f"{table[l][c]:.4g}" if c in table[l] else "" for l in labels) + " |")
+    lines += ["", "| derived | " + " | ".join(labels) + " |", "|---|" + "---|" * len(labels)]
+    for title, num, den in DERIVED:
+        cells = []
+        for l in labels:
+            v = table[l]
+            if num in v and all(x in v for x in den) and sum(v[x] for x in den) > 0:
+                cells.append(f"{v[num] / sum(v[x] for x in den):.4g}")
+            else:
+                cells.append("")
+        if any(cells):
+            lines.append(f"| {title} | " + " | ".join(cells) + " |")
+    with open(os.path.join(ROOT, "profiles", f"counters_{name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ----------------------------------------------------------------------------- kernel-time sweeps
+def sweep(out: str, name: str, title: str, runs: list) -> None:
+    """rocprofv3 kernel-trace averages of the operator kernel over several bench runs side by side.
+    Each run is `label=dir`: dir holds prof_trace/<prefix>_kernel_trace.csv of one
+    `rocprofv3 --kernel-trace` run of bench.py and, beside it, dir.log with its JSON line."""
+    lines = [f"# {title}", "",
+             "rocprofv3 kernel-trace averages of the operator kernel over each run's own launches (whole calls and plan "
+             "launches; the same-pattern copy excluded), with bench.py's HIP-event average of the same kernel in the "
+             "same run. Commands (OUT is the output folder):", ""]
+    rows = []
+    for spec in runs:
+        label, d = spec.rsplit("=", 1)
+        bench = _bench_line(out, f"{d}.log")
+        pre = bench["config"]["name"].lower()
+        stats = _rows(os.path.join(out, d, "prof_trace", f"{pre}_kernel_stats.csv"))
+        cands = [r for r in stats if KERNEL in r["Name"] and "_inline" not in r["Name"]]
+        main_row = max(cands, key=lambda r: int(r["Calls"]))
+        avg, n = _own_average_us(os.path.join(out, d), pre, main_row["Name"], bench, False)
+        alg = bench["algorithmic_bytes"]
+        cmd_flags = " ".join(f for f in bench.get("argv", []) if f)
+        lines.append(f"    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/{d}/prof_trace -o {pre} -- "
+                     f"python3 bench.py {cmd_flags}")
+        rows.append(f"| {label} | {main_row['Name'].split('(')[0].replace('void kamera::', '')} | {n} | {avg:.1f} | "
+                    f"{bench['kernel_us']:.1f} | {alg / 1e9:.4f} | {alg / (avg * 1e-6) / 1e9:.0f} | "
+                    f"{alg / (avg * 1e-6) / 8e12:.1%} |")
+    lines += ["", "summarised with: python3 profile_summary.py " + " ".join(f'"{a}"' if " " in a else a
+                                                                for a in sys.argv[1:])]
+    lines += ["", "| run | kernel | launches | rocprofv3 average us | bench HIP-event us | algorithmic GB | GB/s | "
+              "% of 8 TB/s |", "|---|---|---|---|---|---|---|---|"] + rows
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
+    if sys.argv[1:2] == ["--sweep"]:
+        # profile_summary.py --sweep OUT NAME TITLE label=dir [label=dir ...]
+        sweep(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        sys.exit(0)
+    if sys.argv[1:2] == ["--counters"]:
+        # profile_summary.py --counters OUT NAME label=dir [label=dir ...]
+        counters(sys.argv[2], sys.argv[3], sys.argv[4:])
+        sys.exit(0)
     args = [a for a in sys.argv[1:] if not a.startswith("--")]
     main(args[0], args[1] if len(args) > 1 else "C2", positions="--positions" in sys.argv[1:])

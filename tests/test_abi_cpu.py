@@ -416,3 +416,28 @@ def test_overlap_check_scales_with_the_batch_not_the_pool():
     e = chunk(num_tokens=5, block_table=np.array([7]), slot0=11, k_dst=None, v_dst=None)  # slots 11..15: free
     name, msg = status_of(lambda: abi.rehydrate_batched(gqa_layout(), [a, e], big_pool, (WS[0], 1), 0))
     assert name == "KAMERA_E_WORKSPACE", msg
+
+
+@pytest.mark.parametrize("case", ["unknown_unit", "valu_head64", "valu_positions", "valu_rank96", "mfma_f32"])
+def test_patch_unit_validation(case):
+    """Which unit adds the patch is validated on the host: the VALU form exists for bf16 heads of
+    128 columns with at most two k-steps and no per-token offsets; the MFMA unit for batches the
+    bf16 matrix-core kernel can run."""
+    lay, cs = gqa_layout(patch_unit=abi.PATCH_UNIT_VALU), [chunk()]
+    if case == "unknown_unit":
+        lay = gqa_layout(patch_unit=3)
+    elif case == "valu_head64":
+        lay = gqa_layout(num_kv_heads=8, head_dim=64, patch_unit=abi.PATCH_UNIT_VALU)
+    elif case == "valu_positions":
+        lay = gqa_layout(patch_unit=abi.PATCH_UNIT_VALU, mrope_section=(16, 24, 24))
+        cs = [chunk(flags=abi.PATCH | abi.POSITIONS, positions=FAKE + 0x900000)]
+    elif case == "valu_rank96":
+        cs = [chunk(factors=[dict(u=FAKE + 0x400000, v=FAKE + 0x500000, tensor=0, width=512, rank=96)])]
+    elif case == "mfma_f32":
+        lay = abi.make_layout(abi.GQA, abi.F32, 2, num_kv_heads=4, head_dim=128, rope_base=1e6,
+                              patch_unit=abi.PATCH_UNIT_MFMA)
+    name, msg = status_of(lambda: abi.rehydrate_batched(lay, cs, None, WS, 0))
+    assert name == "KAMERA_E_UNSUPPORTED", (case, name, msg)
+    ok = gqa_layout(patch_unit=abi.PATCH_UNIT_VALU)
+    name, _ = status_of(lambda: abi.rehydrate_batched(ok, [chunk()], None, (WS[0], 64), 0))
+    assert name == "KAMERA_E_WORKSPACE"   # a supported batch passes validation and stops at the workspace
