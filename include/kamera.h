@@ -39,13 +39,21 @@
  *     call; they may be freed or reused as soon as the call returns.
  *   - The caller supplies a device workspace of at least
  *     kamera_workspace_bytes(...) bytes; the library copies the packed batch
- *     description there (stream-ordered). The workspace must not be reused
- *     by another call until the work enqueued on `stream` has finished.
+ *     description there (stream-ordered). Calls on the same stream may reuse
+ *     one workspace (each call's copy-in runs after the previous call's work);
+ *     a call on another stream must not use it until the work enqueued on
+ *     `stream` has finished.
  *   - `stream` is a hipStream_t (NULL: the null stream). Work is enqueued
- *     asynchronously; nothing is synchronised.
- *   - The library never allocates device memory. It keeps a small ring of
- *     pinned, device-mapped host staging buffers per device; a small copy-in
- *     kernel on `stream` moves each packed batch into the workspace. A one-shot
+ *     asynchronously and the device is never synchronised, with one bound on
+ *     how far the host runs ahead: a call that stages its batch (below) takes
+ *     the next of 8 staging slots per device, and if that slot's previous
+ *     copy-in (8 staged calls earlier, on any stream) has not yet run on the
+ *     GPU, the call blocks the calling thread until it has.
+ *   - The library never allocates device memory. It keeps a ring of 8 pinned,
+ *     device-mapped host staging buffers per device (allocated with
+ *     hipHostMalloc on first use, grown when a batch does not fit, kept until
+ *     the process ends); a small copy-in kernel on `stream` moves each packed
+ *     batch into the workspace. A one-shot
  *     kamera_rehydrate_batched / kamera_rehydrate call on a small dense batch (at
  *     most 16 chunks, none with a block table or with more than two factors under
  *     KAMERA_PATCH) instead passes the packed batch as the kernels' argument; the
@@ -58,10 +66,13 @@
  *
  * Errors
  *   Every entry point returns a kamera_status. Arguments are validated on the
- *   host before anything is enqueued; on any error nothing is enqueued and
- *   kamera_last_error() (thread-local) describes the first problem found.
- *   KAMERA_E_HIP reports a failed HIP call (launch, copy). Faults inside a
- *   kernel surface on the stream like any other HIP error.
+ *   host before anything is enqueued; on a validation error nothing is
+ *   enqueued, and kamera_last_error() (thread-local) describes the first
+ *   problem found. KAMERA_E_HIP reports a failed HIP call (staging, launch);
+ *   a call makes up to three launches in order (copy-in, cos/sin tables,
+ *   operator), so KAMERA_E_HIP can follow the successful enqueue of the
+ *   earlier ones, which then run on the stream. Faults inside a kernel surface
+ *   on the stream like any other HIP error.
  */
 #ifndef KAMERA_H_
 #define KAMERA_H_

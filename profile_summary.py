@@ -29,6 +29,7 @@ from __future__ import annotations
 import csv
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,13 @@ def _own_average_us(out: str, pre: str, name: str, bench: dict, positions: bool)
     return sum(durs) / len(durs), len(durs)
 
 
+def _pos_arg(name: str) -> bool:
+    """The per-token-offsets template argument of an operator instantiation's name,
+    kamera::rehydrate_mfma<slabs, k-steps, positions, valu>."""
+    m = re.search(r"rehydrate_mfma<\s*\d+,\s*\d+,\s*(true|false)", name)
+    return bool(m) and m.group(1) == "true"
+
+
 def _bench_line(out: str, log: str = "trace.log") -> dict:
     with open(os.path.join(out, log)) as fh:
         return json.loads(next(ln for ln in fh if ln.startswith("{")))
@@ -92,7 +100,7 @@ def main(out: str, cfg: str, positions: bool = False) -> None:
     # the kernel the bench line measures: with --positions, the instantiation that
     # reads per-token tables (template flag true); the same-pattern copy in that
     # run is the plain variant and is listed but not summarised
-    main_row = next(r for r in stats if KERNEL in r["Name"] and (not positions or ", true>" in r["Name"]))
+    main_row = next(r for r in stats if KERNEL in r["Name"] and "_inline" not in r["Name"] and _pos_arg(r["Name"]) == positions)
     avg_us, n_own = _own_average_us(out, pre, main_row["Name"], bench, positions)
     alg = bench["algorithmic_bytes"]
     suffix = "_positions" if positions else ""

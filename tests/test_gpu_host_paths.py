@@ -147,3 +147,27 @@ def test_evicted_chunk_recalled_into_new_pages_is_byte_identical():
     for layer in range(3):
         for t in (0, 1):
             assert np.array_equal(dw.out_rows(ch2, layer, t), first[layer][t]), (layer, t)
+
+
+def test_more_staged_calls_in_flight_than_staging_slots():
+    """A paged batch is staged through a ring of 8 pinned host slots: the 9th call in flight
+    waits on the host until the copy-in of the 1st has run, then reuses its slot. Twenty
+    one-chunk calls on one stream, one workspace, no synchronisation in between (each call's
+    copy-in runs after the previous call's kernel, in stream order): every chunk, survivors
+    rotated in place and recalled chunks rehydrated into random pages, matches the oracle, and
+    no slot outside the chunks' pages changes."""
+    from position_free_kv_amd import abi
+    from tests.gpu_util import check_all, pool_untouched_ok
+    from workloads.device import DeviceWorkload
+    say("[ring] 20 staged one-chunk calls on one stream")
+    wl = make_workload("C5", num_layers=2, num_chunks=20, max_tokens=300)
+    assert all(c.block_table is not None for c in wl.chunks)
+    dw = DeviceWorkload(wl)
+    stream = torch.cuda.current_stream()
+    for d in dw.descs:
+        abi.rehydrate_batched(dw.layout, [d], dw.pool_desc, dw.workspace, stream)
+    torch.cuda.synchronize()
+    tot = check_all(dw)
+    say(f"  compared {tot['n']} elements: fail={tot['fail']} p2_only={tot['p2_only']}")
+    assert tot["fail"] == 0, tot["bad"][:3]
+    assert pool_untouched_ok(dw)
