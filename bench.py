@@ -400,6 +400,7 @@ def main() -> int:
     # ---- a plain device copy of known size: practical read+write ceiling, and the
     # reference kernel for scaling the HBM byte counters
     copy_gbps = None
+    stream_gbps = {}
     if not args.no_copy:
         n = 1 << 30
         src = torch.empty(n // 2, dtype=torch.int16, device="cuda")
@@ -413,7 +414,21 @@ def main() -> int:
         e5.record(stream)
         torch.cuda.synchronize()
         copy_gbps = 2 * n / (e4.elapsed_time(e5) / 10 * 1e-3) / 1e9
-        del src, dst
+        # the library's streaming probes over the same buffers: the HBM's practical rates for a
+        # nontemporal copy, reads alone and writes alone (the operator mixes all three)
+        sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
+        probes = {"copy": (abi.PROBE_COPY, src, dst, 2 * n), "read": (abi.PROBE_READ, src, sink, n),
+                  "write": (abi.PROBE_WRITE, None, dst, n)}
+        for name, (kind, a_, b_, moved) in probes.items():
+            for _ in range(3):
+                abi.stream_probe(kind, a_, b_, n, 0x3F803F80, stream)
+            e4.record(stream)
+            for _ in range(10):
+                abi.stream_probe(kind, a_, b_, n, 0x3F803F80, stream)
+            e5.record(stream)
+            torch.cuda.synchronize()
+            stream_gbps[name] = moved / (e4.elapsed_time(e5) / 10 * 1e-3) / 1e9
+        del src, dst, sink
 
     ms_per_step = wall_s / args.steps * 1e3
     tokens = wl.total_tokens
@@ -461,6 +476,7 @@ def main() -> int:
         "algorithmic_bytes": alg_bytes,
         "kernel_tokens_per_s": tokens / (kernel_us * 1e-6),
         "torch_copy_GBps": copy_gbps,
+        "stream_probe_GBps": stream_gbps or None,
         "kernel_source_hash": kernel_source_hash(),
         "argv": sys.argv[1:],
         "cpu_baseline": cpu,

@@ -310,6 +310,17 @@ kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tens
                                        void* v_out, double* sigma_out, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Streaming probes (measurement only, not part of the operator): nontemporal 16-byte
+ * accesses, each workgroup over a contiguous 16 KB block. KAMERA_PROBE_COPY copies `bytes`
+ * from src to dst; KAMERA_PROBE_READ reads `bytes` of src (dst: a device sink of at least
+ * 4 KB, written only for one XOR value of the data no caller builds); KAMERA_PROBE_WRITE
+ * fills `bytes` of dst with the 32-bit `value` (src unused). Timing them beside the operator
+ * gives the HBM's practical rates for the access kinds the operator mixes. `bytes` a
+ * multiple of 16, pointers 16-byte aligned; stream-ordered like every call. */
+enum { KAMERA_PROBE_COPY = 0, KAMERA_PROBE_READ = 1, KAMERA_PROBE_WRITE = 2 };
+kamera_status kamera_stream_probe(int32_t kind, const void* src, void* dst, size_t bytes, uint32_t value,
+                                  void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kamera_status_string(kamera_status status);
 /* Detail of the last error on the calling thread ("" if none). */

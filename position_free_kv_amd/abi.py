@@ -27,6 +27,7 @@ BUILD_MAX_RANK = 64
 BUILD_MAX_SUBSPACE = 80
 BUILD_MAX_ORBIT = 32
 NOALLOC_SCRATCH_BYTES = 4 << 20
+PROBE_COPY, PROBE_READ, PROBE_WRITE = 0, 1, 2
 
 STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAMERA_E_RANK",
           "KAMERA_E_DELTA", "KAMERA_E_PAGE", "KAMERA_E_OVERLAP", "KAMERA_E_ALIGN",
@@ -34,7 +35,8 @@ STATUS = ["KAMERA_OK", "KAMERA_E_NULL", "KAMERA_E_SHAPE", "KAMERA_E_DTYPE", "KAM
 EXPORTED = ["kamera_workspace_bytes", "kamera_batch_workspace_bytes", "kamera_relocate", "kamera_rehydrate",
             "kamera_rehydrate_batched", "kamera_rehydrate_batched_noalloc",
             "kamera_plan_upload", "kamera_plan_launch", "kamera_status_string", "kamera_last_error",
-            "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch", "kamera_build_orbit_patch"]
+            "kamera_version", "kamera_build_workspace_bytes", "kamera_build_patch", "kamera_build_orbit_patch",
+            "kamera_stream_probe"]
 
 
 class Layout(ctypes.Structure):
@@ -109,7 +111,8 @@ def lib() -> ctypes.CDLL:
         L.kamera_build_orbit_patch.argtypes = [ctypes.POINTER(Layout), i32, i32, ctypes.POINTER(vp),
                                                ctypes.POINTER(i64), vp, i64, i32, i32, i32, i32, vp, vp, vp, vp,
                                                sz, vp]
-        for fn in ("kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
+        L.kamera_stream_probe.argtypes = [i32, vp, vp, sz, ctypes.c_uint32, vp]
+        for fn in ("kamera_stream_probe", "kamera_relocate", "kamera_rehydrate", "kamera_rehydrate_batched",
                    "kamera_rehydrate_batched_noalloc", "kamera_plan_upload",
                    "kamera_plan_launch", "kamera_build_patch", "kamera_build_orbit_patch"):
             getattr(L, fn).restype = ctypes.c_int
@@ -307,6 +310,12 @@ def plan_upload(layout: Layout, chunks: Sequence, pool: Optional[Pool], workspac
 
 def plan_launch(plan: Plan, stream=None) -> None:
     _check(lib().kamera_plan_launch(ctypes.byref(plan), _stream(stream)))
+
+
+def stream_probe(kind: int, src, dst, nbytes: int, value: int = 0, stream=None) -> None:
+    """Streaming probe (measurement only): copy src -> dst, read src (dst a 4 KB sink), or write dst."""
+    _check(lib().kamera_stream_probe(int(kind), _ptr(src), _ptr(dst), int(nbytes), int(value) & 0xffffffff,
+                                     _stream(stream)))
 
 
 def version() -> str:

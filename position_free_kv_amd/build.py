@@ -4,7 +4,8 @@
 
 The library is the C ABI of include/kamera.h: host validation and packing
 (csrc/kamera_host.cpp) plus the gfx950 kernels: the operator
-(csrc/kamera_kernels.hip) and the patch builder (csrc/kamera_builder.hip).
+(csrc/kamera_kernels.hip), the patch builder (csrc/kamera_builder.hip) and the
+streaming probes used for measurement (csrc/kamera_probe.hip).
 """
 from __future__ import annotations
 
@@ -47,14 +48,17 @@ def build(verbose_asm: bool = False) -> str:
     kobj = os.path.join(objdir, "kamera_kernels.o")
     bobj = os.path.join(objdir, "kamera_builder.o")
     hobj = os.path.join(objdir, "kamera_host.o")
+    pobj = os.path.join(objdir, "kamera_probe.o")
     _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
           os.path.join(CSRC, "kamera_kernels.hip"), "-o", kobj])
     _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
           os.path.join(CSRC, "kamera_builder.hip"), "-o", bobj])
+    _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "-c",
+          os.path.join(CSRC, "kamera_probe.hip"), "-o", pobj])
     _run([cc, "-x", "c++", *COMMON, "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-c",
           os.path.join(CSRC, "kamera_host.cpp"), "-o", hobj])
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, bobj, hobj, "-o", tmp])
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, bobj, pobj, hobj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose_asm:
         _run([cc, f"--offload-arch={ARCH}", *COMMON, *HIP_FLAGS, "--cuda-device-only", "-S",

@@ -24,6 +24,7 @@ hipError_t launch_copy_in(void* dst, const void* src, size_t bytes, hipStream_t 
 hipError_t launch_phase_table(const DevHeader* hdr, const DevChunk* chunks, int nchunks, int64_t per_chunk,
                               hipStream_t stream, const InlineBatch* inl);
 hipError_t scratch_address(void** out);
+hipError_t launch_stream_probe(int kind, const void* src, void* dst, int64_t n16, uint32_t value, hipStream_t stream);
 hipError_t launch_fill_by_argument(void* dst, const void* src, size_t bytes, hipStream_t stream);
 }  // namespace kamera
 
@@ -913,6 +914,19 @@ kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tens
   g_last_error.clear();
   return build_impl(layout, tensor, num_orderings, x_conds, deltas, x_canon, num_tokens, col0, width, rank,
                     iterations, u_out, v_out, sigma_out, workspace, workspace_bytes, stream);
+}
+
+kamera_status kamera_stream_probe(int32_t kind, const void* src, void* dst, size_t bytes, uint32_t value,
+                                  void* stream) {
+  g_last_error.clear();
+  if (kind < KAMERA_PROBE_COPY || kind > KAMERA_PROBE_WRITE) return fail(KAMERA_E_UNSUPPORTED, "unknown probe kind %d", kind);
+  if (bytes % 16) return fail(KAMERA_E_SHAPE, "bytes must be a multiple of 16 (got %zu)", bytes);
+  if (bytes == 0) return KAMERA_OK;
+  if ((kind != KAMERA_PROBE_WRITE && !src) || !dst) return fail(KAMERA_E_NULL, "src or dst is NULL");
+  if ((src && !aligned(src, 16)) || !aligned(dst, 16)) return fail(KAMERA_E_ALIGN, "src and dst must be 16-byte aligned");
+  const hipError_t e = launch_stream_probe(kind, src, dst, (int64_t)(bytes / 16), value, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KAMERA_E_HIP, "probe launch failed: %s", hipGetErrorString(e));
+  return KAMERA_OK;
 }
 
 const char* kamera_status_string(kamera_status s) {

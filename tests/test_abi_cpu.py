@@ -441,3 +441,13 @@ def test_patch_unit_validation(case):
     ok = gqa_layout(patch_unit=abi.PATCH_UNIT_VALU)
     name, _ = status_of(lambda: abi.rehydrate_batched(ok, [chunk()], None, (WS[0], 64), 0))
     assert name == "KAMERA_E_WORKSPACE"   # a supported batch passes validation and stops at the workspace
+
+
+def test_stream_probe_validation():
+    """The measurement probes validate kind, size and alignment on the host before any launch."""
+    cases = [((5, FAKE, FAKE + 4096, 4096), "KAMERA_E_UNSUPPORTED"), ((0, FAKE, FAKE + 4096, 100), "KAMERA_E_SHAPE"),
+             ((0, None, FAKE, 4096), "KAMERA_E_NULL"), ((2, None, None, 4096), "KAMERA_E_NULL"),
+             ((1, FAKE + 8, FAKE, 4096), "KAMERA_E_ALIGN"), ((0, FAKE, FAKE, 0), "KAMERA_OK")]
+    for (kind, src, dst, n), want in cases:
+        name, msg = status_of(lambda: abi.stream_probe(kind, src, dst, n, 0, 0))
+        assert name == want, (kind, n, name, msg)

@@ -171,3 +171,23 @@ def test_more_staged_calls_in_flight_than_staging_slots():
     say(f"  compared {tot['n']} elements: fail={tot['fail']} p2_only={tot['p2_only']}")
     assert tot["fail"] == 0, tot["bad"][:3]
     assert pool_untouched_ok(dw)
+
+
+def test_stream_probes_move_what_they_say():
+    """The streaming probes bench.py times beside the operator: the copy reproduces its source
+    byte for byte (ragged last workgroup included), the write fills every word, and the read
+    leaves its sink alone for ordinary data."""
+    from position_free_kv_amd import abi
+    say("[probes]")
+    n = 16 * (3 * 1024 + 37)                        # three full 16 KB blocks and a ragged one
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    abi.stream_probe(abi.PROBE_COPY, src, dst, n)
+    abi.stream_probe(abi.PROBE_READ, src, sink, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert int(sink.abs().sum()) == 0
+    abi.stream_probe(abi.PROBE_WRITE, None, dst, n - 16, 0x01020304)
+    torch.cuda.synchronize()
+    assert bool((dst[:-4] == 0x01020304).all()) and torch.equal(dst[-4:], src[-4:])

@@ -79,3 +79,37 @@ def test_noalloc_matches_workspace_entry_point(label, kw, subset):
         got = _outputs(dw)
         assert _same(got, want), f"{label}: call {call} differs from kamera_rehydrate_batched"
     say(f"[noalloc] {label}: both calls byte-identical")
+
+
+@pytest.mark.parametrize("label,kw", [("deque paged", dict(name="C5", num_layers=2, num_chunks=10, max_tokens=280)),
+                                      ("dense re-anchored", dict(name="C2", num_layers=2, num_chunks=3, tokens=150,
+                                                                 positions=True))])
+def test_noalloc_call_in_a_captured_graph(label, kw):
+    """The callers the allocation-free entry point is for include code under graph capture: a
+    call recorded in a HIP graph (the packed batch travels in its kernels' arguments) replays to
+    the eager result bit for bit, three times, with the destinations restored and other eager
+    work between the replays. The first call on the device, which looks up the scratch array's
+    address, happens before the capture."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    kw = dict(kw)
+    wl = make_workload(kw.pop("name"), **kw)
+    dw = DeviceWorkload(wl, device="cuda:0")
+    fresh = _outputs(dw)
+    say(f"[noalloc graph] {label}")
+    abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
+    torch.cuda.synchronize()
+    eager = _outputs(dw)
+    _restore(dw, fresh)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc, torch.cuda.current_stream())
+    for rep in range(3):
+        _restore(dw, fresh)
+        abi.rehydrate_batched(dw.layout, dw.descs[:1], dw.pool_desc, dw.workspace)   # other work in between
+        _restore(dw, fresh)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(_outputs(dw), eager), f"{label}: replay {rep}"
