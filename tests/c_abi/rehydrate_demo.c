@@ -3,7 +3,10 @@
  * with rank-8 factors on K and V (Kamera preprint Eq. 1: KV = R(delta) KV_stored + U V^T)
  * into dense output rows.
  *
- *   rehydrate_demo IN OUT T DELTA
+ *   rehydrate_demo IN OUT T DELTA [noalloc]
+ *
+ * With "noalloc" the call is kamera_rehydrate_batched_noalloc (no workspace, no allocation)
+ * instead of kamera_rehydrate_batched with a hipMalloc'd workspace.
  *
  * IN holds, as raw little-endian bf16 bit patterns, in this order: K [2][T][256],
  * V [2][T][256], U_K [2][T][8], V_K [2][256][8], U_V [2][T][8], V_V [2][256][8].
@@ -32,10 +35,11 @@ static int kamera_ok(kamera_status st, const char* what) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 5) {
-    fprintf(stderr, "usage: %s IN OUT T DELTA\n", argv[0]);
+  if (argc != 5 && !(argc == 6 && strcmp(argv[5], "noalloc") == 0)) {
+    fprintf(stderr, "usage: %s IN OUT T DELTA [noalloc]\n", argv[0]);
     return 2;
   }
+  const int noalloc = argc == 6;
   const int64_t T = atoll(argv[3]);
   const int64_t delta = atoll(argv[4]);
   if (T < 1 || T > (1 << 20)) return 2;
@@ -88,21 +92,26 @@ int main(int argc, char** argv) {
   c.factors[1].v = vv;
   c.factors[1].tensor = 1;
 
-  const size_t ws_bytes = kamera_batch_workspace_bytes(&lay, &c, 1);
   void* ws = NULL;
-  if (ws_bytes == 0 || !hip_ok(hipMalloc(&ws, ws_bytes), "hipMalloc(workspace)")) return 1;
-  if (!kamera_ok(kamera_rehydrate_batched(&lay, &c, 1, NULL, ws, ws_bytes, NULL), "kamera_rehydrate_batched"))
-    return 1;
+  if (noalloc) {
+    if (!kamera_ok(kamera_rehydrate_batched_noalloc(&lay, &c, 1, NULL, NULL), "kamera_rehydrate_batched_noalloc"))
+      return 1;
+  } else {
+    const size_t ws_bytes = kamera_batch_workspace_bytes(&lay, &c, 1);
+    if (ws_bytes == 0 || !hip_ok(hipMalloc(&ws, ws_bytes), "hipMalloc(workspace)")) return 1;
+    if (!kamera_ok(kamera_rehydrate_batched(&lay, &c, 1, NULL, ws, ws_bytes, NULL), "kamera_rehydrate_batched"))
+      return 1;
+  }
   if (!hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize")) return 1;
   if (!hip_ok(hipMemcpy(out, k_out, 2 * rows * sizeof(uint16_t), hipMemcpyDeviceToHost), "hipMemcpy back")) return 1;
   f = fopen(argv[2], "wb");
   if (!f || fwrite(out, sizeof(uint16_t), 2 * rows, f) != 2 * rows) return 1;
   fclose(f);
-  (void)hipFree(ws);
+  if (ws) (void)hipFree(ws);
   (void)hipFree(dev);
   free(host);
   free(out);
-  printf("rehydrate_demo: %s, %lld tokens x %d layers rehydrated at delta %lld\n", kamera_version(), (long long)T,
-         LAYERS, (long long)delta);
+  printf("rehydrate_demo: %s, %lld tokens x %d layers rehydrated at delta %lld%s\n", kamera_version(), (long long)T,
+         LAYERS, (long long)delta, noalloc ? " (no workspace)" : "");
   return 0;
 }

@@ -1,5 +1,6 @@
 """The library called from plain C (tests/c_abi/rehydrate_demo.c: hipMalloc'd buffers,
-kamera_batch_workspace_bytes, kamera_rehydrate_batched on the null stream), checked
+kamera_batch_workspace_bytes, kamera_rehydrate_batched on the null stream, or
+kamera_rehydrate_batched_noalloc without a workspace), checked
 against the fp64 oracle: one GQA chunk of 2 heads x 128, 2 layers, rank-8 factors on K
 and V (Kamera preprint Eq. 1), bf16 tolerance as in the other parity tests."""
 import os
@@ -25,10 +26,11 @@ def bf16(x: np.ndarray) -> np.ndarray:
         np.uint16)
 
 
-@pytest.mark.parametrize("T,delta", [(1, 3), (77, -40000), (300, 123456)])
-def test_plain_c_caller_matches_oracle(T, delta):
+@pytest.mark.parametrize("T,delta,noalloc", [(1, 3, False), (77, -40000, False), (300, 123456, False),
+                                             (300, 123456, True), (33, -7, True)])
+def test_plain_c_caller_matches_oracle(T, delta, noalloc):
     assert os.path.exists(DEMO), f"{DEMO} is missing: build it with __graft_entry__.build()"
-    say(f"[c-abi] T={T} delta={delta}")
+    say(f"[c-abi] T={T} delta={delta} noalloc={noalloc}")
     rng = np.random.default_rng(T)
     k, v = bf16(rng.standard_normal((L, T, F))), bf16(rng.standard_normal((L, T, F)))
     uk, vk = bf16(0.2 * rng.standard_normal((L, T, M))), bf16(0.2 * rng.standard_normal((L, F, M)))
@@ -36,7 +38,8 @@ def test_plain_c_caller_matches_oracle(T, delta):
     with tempfile.TemporaryDirectory() as d:
         fin, fout = os.path.join(d, "in.bin"), os.path.join(d, "out.bin")
         np.concatenate([a.ravel() for a in (k, v, uk, vk, uv, vv)]).astype("<u2").tofile(fin)
-        r = subprocess.run([DEMO, fin, fout, str(T), str(delta)], capture_output=True, text=True, timeout=120)
+        r = subprocess.run([DEMO, fin, fout, str(T), str(delta)] + (["noalloc"] if noalloc else []),
+                           capture_output=True, text=True, timeout=120)
         assert r.returncode == 0, r.stderr
         say("  " + r.stdout.strip())
         out = np.fromfile(fout, dtype="<u2").reshape(2, L, T, F)
