@@ -113,3 +113,52 @@ def test_noalloc_call_in_a_captured_graph(label, kw):
         graph.replay()
         torch.cuda.synchronize()
         assert _same(_outputs(dw), eager), f"{label}: replay {rep}"
+
+
+def test_noalloc_at_its_scratch_limit():
+    """A re-anchored chunk whose cos/sin table nearly fills the 4 MiB scratch runs (and matches
+    the workspace entry point byte for byte); one token more than fits is rejected before
+    anything is enqueued, and the library keeps working afterwards."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    limit = abi.NOALLOC_SCRATCH_BYTES
+    fixed = abi.batch_workspace_bytes(*_one_chunk_batch(16)) - 16 * 64 * 8
+    T = (limit - fixed) // (64 * 8) // 16 * 16          # tokens of whole 16-token tiles that still fit
+    wl = make_workload("C2", num_layers=1, num_chunks=1, tokens=T, positions=True)
+    dw = DeviceWorkload(wl, device="cuda:0")
+    need = abi.batch_workspace_bytes(dw.layout, dw.descs)
+    say(f"[noalloc limit] T={T}: {need} of {limit} bytes")
+    assert limit - 16 * 64 * 8 < need <= limit
+    fresh = _outputs(dw)
+    abi.rehydrate_batched(dw.layout, dw.descs, dw.pool_desc, dw.workspace)
+    torch.cuda.synchronize()
+    want = _outputs(dw)
+    _restore(dw, fresh)
+    abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
+    torch.cuda.synchronize()
+    assert _same(_outputs(dw), want)
+    # one more tile does not fit: host validation rejects it, nothing runs
+    big = make_workload("C2", num_layers=1, num_chunks=1, tokens=T + 16, positions=True)
+    dwb = DeviceWorkload(big, device="cuda:0")
+    assert abi.batch_workspace_bytes(dwb.layout, dwb.descs) > limit
+    before = _outputs(dwb)
+    with pytest.raises(abi.KameraError) as err:
+        abi.rehydrate_batched_noalloc(dwb.layout, dwb.descs, dwb.pool_desc)
+    assert err.value.name == "KAMERA_E_WORKSPACE"
+    torch.cuda.synchronize()
+    assert _same(_outputs(dwb), before)
+    _restore(dw, fresh)
+    abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
+    torch.cuda.synchronize()
+    assert _same(_outputs(dw), want)
+
+
+def _one_chunk_batch(T):
+    """(layout, [desc]) of a one-chunk re-anchored GQA batch with fake device addresses, only for sizing."""
+    from position_free_kv_amd import abi
+    lay = abi.make_layout(abi.GQA, abi.BF16, 1, num_kv_heads=4, head_dim=128, rope_base=1e6,
+                          mrope_section=(16, 24, 24))
+    fake = 1 << 36
+    d = abi.ChunkDesc(num_tokens=T, delta=0, flags=abi.POSITIONS, k_src=fake, v_src=fake, k_dst=fake, v_dst=fake,
+                      positions=fake)
+    return lay, [d]
