@@ -28,13 +28,16 @@ def _gpu():
     yield
 
 
-def draw_batch(seed: int):
+def draw_batch(seed: int, kind=None, reanchor_ok: bool = True):
+    """A seeded random batch; `kind` forces the layout ("gqa128", "gqa64", "mla", "f32") and
+    reanchor_ok=False keeps every chunk on a chunk-wide delta."""
     rng = np.random.default_rng([20261202, seed])
-    kind = str(rng.choice(["gqa128", "gqa64", "mla", "f32"]))
+    drawn = str(rng.choice(["gqa128", "gqa64", "mla", "f32"]))
+    kind = kind or drawn
     pairing = GPTJ if rng.random() < 0.3 else NEOX
     L = int(rng.integers(1, 4))
     P = 16
-    reanchor = rng.random() < 0.35   # some chunks turn token by token under an M-RoPE split
+    reanchor = rng.random() < 0.35 and reanchor_ok   # some chunks turn token by token under an M-RoPE split
     if kind == "mla":
         lay = LayoutSpec(MLA, BF16, L, latent_dim=512, rope_dim=64, pairing=pairing, page_size=P,
                          mrope_section=(8, 12, 12) if reanchor else (0, 0, 0))
@@ -97,6 +100,36 @@ def test_random_batch(seed):
     say(f"[random batch {seed}] {desc}")
     dw = DeviceWorkload(wl)
     dw.run()
+    torch.cuda.synchronize()
+    tot = check_all(dw)
+    say(f"  compared {tot['n']} elements: fail={tot['fail']} p2_only={tot['p2_only']} exact={tot['exact']}")
+    assert tot["fail"] == 0, tot["bad"][:3]
+    assert pool_untouched_ok(dw)
+
+
+@pytest.mark.parametrize("seed", range(1000, 1000 + N_BATCHES // 2))
+def test_random_batch_noalloc_and_valu(seed):
+    """Batches from the same generator through the other routes: the allocation-free entry
+    point (its scratch holds the packed batch and tables), and, where the layout allows it
+    (bf16 heads of 128, no per-token offsets, at most two k-steps), the patch on the VALU
+    (every odd seed draws such a layout)."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    wl, desc = draw_batch(seed, **({"kind": "gqa128", "reanchor_ok": False} if seed % 2 else {}))
+    dw = DeviceWorkload(wl)
+    valu = wl.layout.family == GQA and wl.layout.dtype == BF16 and wl.layout.head_dim == 128 \
+        and not any(c.positions is not None for c in wl.chunks)
+    if valu:
+        dw.layout.patch_unit = abi.PATCH_UNIT_VALU
+    say(f"[random batch {seed}, no-alloc{', VALU' if valu else ''}] {desc}")
+    assert abi.batch_workspace_bytes(dw.layout, dw.descs) <= abi.NOALLOC_SCRATCH_BYTES
+    try:
+        abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
+    except abi.KameraError as e:   # more k-steps than the VALU form holds: the matrix cores instead
+        assert valu and e.name == "KAMERA_E_UNSUPPORTED", e
+        say("  VALU form not built for this batch's k-steps; matrix cores")
+        dw.layout.patch_unit = abi.PATCH_UNIT_AUTO
+        abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
     torch.cuda.synchronize()
     tot = check_all(dw)
     say(f"  compared {tot['n']} elements: fail={tot['fail']} p2_only={tot['p2_only']} exact={tot['exact']}")
