@@ -29,7 +29,7 @@ def _gpu_present() -> bool:
 
 @pytest.mark.skipif(_gpu_present(), reason="the validation tests it drives use fake device addresses")
 def test_host_code_under_address_sanitizer():
-    kobjs = [os.path.join(OBJS, f) for f in ("kamera_kernels.o", "kamera_builder.o")]
+    kobjs = [os.path.join(OBJS, f) for f in ("kamera_kernels.o", "kamera_builder.o", "kamera_probe.o")]
     assert all(os.path.exists(o) for o in kobjs), "kernel objects missing: build the library first"
     libasan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
     assert os.path.isabs(libasan), "no ASan runtime"
