@@ -269,6 +269,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the 1 GiB copy-ceiling probe")
     ap.add_argument("--rank", type=int, default=None, help="override the patch rank m of the workload")
+    ap.add_argument("--chunks", type=int, default=None,
+                    help="override the chunk count of the workload (C1-C3: chunks of the same shape; launch-size "
+                         "studies)")
     ap.add_argument("--deep-half", action="store_true",
                     help="patch only the deeper half of the layers (every factor starts at layer L // 2)")
     ap.add_argument("--shared-basis", action="store_true",
@@ -299,11 +302,16 @@ def main() -> int:
 
     from workloads import make_workload
     make_kw = dict(rank=args.rank)
+    if args.chunks is not None:
+        if args.config not in ("C1", "C2", "C3"):
+            print(json.dumps({"error": "--chunks applies to C1, C2 and C3"}), flush=True)
+            return 2
+        make_kw["num_chunks"] = args.chunks
     if args.page_order != "random":
         make_kw["page_order"] = args.page_order
     wl = make_workload(args.config, **make_kw)
     variant = (args.deep_half or args.shared_basis or args.positions or args.page_order != "random"
-               or args.patch_unit != "auto")
+               or args.patch_unit != "auto" or args.chunks is not None)
     if args.deep_half or args.shared_basis or args.positions:
         make_kw.update(shared_basis=args.shared_basis, positions=args.positions,
                        patch_layer0=wl.layout.num_layers // 2 if args.deep_half else None)
@@ -451,6 +459,7 @@ def main() -> int:
         "dtype": "f32" if wl.layout.dtype == 0 else "bf16",
         "data": "synthetic: seeded N(0,1) canonical KV, orthonormal factors with geometric spectra",
         "config": {"workload": WORKLOADS[args.config] + ("" if args.rank is None else f" (rank overridden: m={args.rank})")
+                   + ("" if args.chunks is None else f" (chunk count overridden: {args.chunks})")
                    + (" (deep-half patches: layers L/2..L-1 only)" if args.deep_half else "")
                    + (" (one V basis per layer shared by all chunks)" if args.shared_basis else "")
                    + (" (per-token (t, h, w) re-anchoring, M-RoPE sections %s)" % (wl.layout.mrope_section,)
