@@ -288,6 +288,9 @@ def main() -> int:
     ap.add_argument("--builder", action="store_true",
                     help="time the patch builder (kamera_build_patch) on one chunk-layer of --config instead")
     ap.add_argument("--builder-iterations", type=int, default=16)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary stderr line (the default run also times the 28-layer GQA batch's "
+                         "kernel, C2, after its JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this operator runs on one GPU; chunks and layers are independent, so "
@@ -490,8 +493,60 @@ def main() -> int:
         "argv": sys.argv[1:],
         "cpu_baseline": cpu,
     }
+    # the default run also times the 28-layer GQA batch's kernel (C2) after its own line, to stderr
+    sec = None
+    if args.config == "C4" and not (variant or args.rank is not None or args.no_secondary):
+        sec = prepare_secondary("C2", stream)
+    out["launches"].update(secondary=SECONDARY_LAUNCHES if sec else 0,
+                           secondary_variant=sec[1].variant if sec else None)
     print(json.dumps(out), flush=True)
+    if sec:
+        secondary_kernel_line("C2", sec, stream)
     return 0
+
+
+SECONDARY_LAUNCHES = PLAN_WARMUP + 10 + 200 + 200
+
+
+def prepare_secondary(cfg: str, stream):
+    from workloads import make_workload
+    from workloads.device import DeviceWorkload
+    wl = make_workload(cfg)
+    dw = DeviceWorkload(wl)
+    return dw, dw.plan(stream), wl
+
+
+def secondary_kernel_line(cfg: str, sec, stream) -> None:
+    """The kernel alone on a second workload, after the main line, to stderr: the same
+    plan timing as the main line (untimed launches, then 200 back to back, then 200 each
+    between its own events), so boxes can be compared on a short launch too."""
+    import torch
+    from position_free_kv_amd import abi
+    dw, plan, wl = sec
+    for _ in range(PLAN_WARMUP + 10):
+        abi.plan_launch(plan, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(200):
+        abi.plan_launch(plan, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 200 * 1e3
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(200)]
+    for ea, eb in evs:
+        ea.record(stream)
+        abi.plan_launch(plan, stream)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+    alg = dw.algorithmic_bytes()
+    print("# secondary " + json.dumps({"config": cfg, "workload": WORKLOADS[cfg], "kernel_us": us,
+                                       "kernel_us_p10_p50_p90": [per[20], per[100], per[180]],
+                                       "achieved_GBps": alg / (us * 1e-6) / 1e9,
+                                       "frac": alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                       "tokens_per_s_kernel": wl.total_tokens / (us * 1e-6)}),
+          file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

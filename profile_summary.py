@@ -57,13 +57,17 @@ def _copy_kib(rows):
 
 def _own(rows, bench: dict, positions: bool):
     """The workload's own dispatches of one instantiation, in dispatch order: bench.py ends
-    with its same-pattern copy (the same chunks at delta 0 without a patch, a lighter load);
-    when that copy runs the same instantiation (same kernel variant), its last launches are
-    not the workload's."""
+    with its same-pattern copy (the same chunks at delta 0 without a patch, a lighter load)
+    and, in the default run, a secondary workload; when those run the same instantiation
+    (same kernel variant), their launches at the end are not the workload's."""
     rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     ln = bench["launches"]
     same = ln.get("pattern_variant", ln.get("plan_variant")) == ln.get("plan_variant")
     drop = 0 if positions or not same else ln["pattern"]
+    # the default run's secondary workload comes last, through the same instantiation when its
+    # variant matches
+    if ln.get("secondary") and ln.get("secondary_variant") == ln.get("plan_variant"):
+        drop += ln["secondary"]
     return rows[:len(rows) - drop] if drop else rows
 
 
