@@ -75,6 +75,8 @@ CPU_UNITS = {"C1": 32768, "C2": 448, "C3": 448, "C4": 16, "C5": 576}
 CPU_PROCS_MAX = 16       # the host share of one GPU
 PLAN_WARMUP = 3          # untimed launches of the uploaded plan before its timed launches
 KERNEL_LAUNCHES = 100    # the kernel average covers at least this many launches
+FLUSH_BYTES = 1 << 30    # written between launches to evict the 256 MB Infinity Cache
+FLUSH_LAUNCHES = 50
 PATTERN_WARMUP = 5
 
 
@@ -389,6 +391,25 @@ def main() -> int:
     per_launch = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
     pct = lambda q: per_launch[min(len(per_launch) - 1, int(q * len(per_launch)))]
 
+    # ---- the same launches with the 256 MB Infinity Cache flushed before each: 1 GiB of
+    # unrelated writes (the library's write probe) between launches, each launch between
+    # its own event pair, so no launch can find a previous launch's factors or rows there
+    flushed = None
+    if not args.no_copy:
+        junk = torch.empty(FLUSH_BYTES // 2, dtype=torch.int16, device="cuda")
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(FLUSH_LAUNCHES)]
+        for ea, eb in fev:
+            abi.stream_probe(abi.PROBE_WRITE, None, junk, FLUSH_BYTES, 0x5A5A5A5A, stream)
+            ea.record(stream)
+            abi.plan_launch(plan, stream)
+            eb.record(stream)
+        torch.cuda.synchronize()
+        fl = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in fev)
+        flushed = {"mean": sum(fl) / len(fl), "p50": fl[len(fl) // 2], "launches": len(fl),
+                   "achieved_GBps_at_mean": dw.algorithmic_bytes() / (sum(fl) / len(fl) * 1e-6) / 1e9}
+        del junk
+
     # ---- the same chunks at delta 0 without a patch: a plain copy through the
     # kernel's own access pattern, the practical ceiling for this workload's layout
     pattern_gbps = None
@@ -478,8 +499,10 @@ def main() -> int:
         "kernel_us": kernel_us,
         "kernel_launches_timed": n_kernel,
         "kernel_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "kernel_us_after_cache_flush": flushed,
         # operator launches in this run, in order: whole calls, plan launches, same-pattern copy
-        "launches": {"calls": args.warmup + args.steps, "plan": PLAN_WARMUP + n_kernel + n_dist,
+        "launches": {"calls": args.warmup + args.steps,
+                     "plan": PLAN_WARMUP + n_kernel + n_dist + (FLUSH_LAUNCHES if flushed else 0),
                      "pattern": (PATTERN_WARMUP + n_dist) if cbytes > 0 else 0,
                      "plan_variant": plan.variant, "pattern_variant": pattern_variant},
         "pattern_copy_GBps": pattern_gbps,
