@@ -55,12 +55,22 @@ def _run_twice_identical(dw, snapshot):
 
 @pytest.mark.parametrize("name,blocks,rows", [("C2", 24, 40), ("C3", 24, 40), ("C4", 10, 24)])
 def test_fullsize_dense(name, blocks, rows):
+    """Sampled parity at full size, a second call byte-identical, and the same batch through the
+    allocation-free entry point byte-identical too (its scratch holds the whole packed batch)."""
+    from position_free_kv_amd import abi
     dw = _stage(name)
     dw.run()
     torch.cuda.synchronize()
     _sampled_parity(dw, blocks, rows, seed=int(name[1:]))
-    assert _run_twice_identical(dw, lambda: [t for buf in dw.dense for t in buf])
-    del dw
+    outs = lambda: [t for buf in dw.dense for t in buf]
+    assert _run_twice_identical(dw, outs)
+    first = [t.clone() for t in outs()]
+    for t in outs():
+        t.zero_()
+    abi.rehydrate_batched_noalloc(dw.layout, dw.descs, dw.pool_desc)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(first, outs()))
+    del dw, first
     torch.cuda.empty_cache()
 
 
@@ -113,4 +123,16 @@ def test_fullsize_deque_paged():
     torch.cuda.synchronize()
     assert torch.equal(dw.pool[0], after)
     del dw, k_before, after
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_deque_positions():
+    """C5 with its recalled chunks re-anchored token by token (survivors keep their delta):
+    paged, in place and per-token tables in one full-size batch."""
+    dw = _stage("C5", positions=True)
+    dw.run()
+    torch.cuda.synchronize()
+    _sampled_parity(dw, 24, 32, seed=155)
+    assert pool_untouched_ok(dw)
+    del dw
     torch.cuda.empty_cache()
