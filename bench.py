@@ -542,7 +542,7 @@ def prepare_secondary(cfg: str, stream):
 def secondary_kernel_line(cfg: str, sec, stream) -> None:
     """The kernel alone on a second workload, after the main line, to stderr: the same
     plan timing as the main line (untimed launches, then 200 back to back, then 200 each
-    between its own events), so boxes can be compared on a short launch too."""
+    between its own events), so machines can be compared on a short launch too."""
     import torch
     from position_free_kv_amd import abi
     dw, plan, wl = sec
