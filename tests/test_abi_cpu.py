@@ -237,6 +237,31 @@ def test_partial_page_sharing_is_not_an_overlap():
     assert name == "KAMERA_E_OVERLAP", msg
 
 
+@pytest.mark.parametrize("P", [1, 3, 24])
+def test_slot_overlap_at_other_page_sizes(P):
+    """The slot check follows the layout's page size: with P-token pages, chunk a owns slots
+    [s0, s0 + T) of its table's pages counted in P; a chunk on the next free slot of a's last
+    page passes (and stops at the too-small workspace), one on a's last slot collides."""
+    lay = gqa_layout(page_size=P)
+    pool = abi.make_pool(FAKE + 0x4000000, FAKE + 0x8000000, num_pages=64)
+    s0, T = (P - 1, 2 * P)                        # ends one slot before the end of its last page (P > 1)
+    npg = -(-(s0 + T) // P)
+    a = chunk(num_tokens=T, block_table=np.arange(10, 10 + npg), slot0=s0, k_dst=None, v_dst=None)
+    end = (s0 + T) % P                            # first free slot of a's last page (0: the page is full)
+    last = 10 + npg - 1
+    tiny = (WS[0], 1)
+    if end:
+        b = chunk(num_tokens=P - end, block_table=np.array([last]), slot0=end, k_dst=None, v_dst=None)
+        name, msg = status_of(lambda: abi.rehydrate_batched(lay, [a, b], pool, tiny, 0))
+        assert name == "KAMERA_E_WORKSPACE", msg
+    c = chunk(num_tokens=1, block_table=np.array([last]), slot0=(s0 + T - 1) % P, k_dst=None, v_dst=None)
+    name, msg = status_of(lambda: abi.rehydrate_batched(lay, [a, c], pool, tiny, 0))
+    assert name == "KAMERA_E_OVERLAP" and f"page {last}" in msg, msg
+    name, msg = status_of(lambda: abi.rehydrate_batched(lay, [chunk(num_tokens=1, block_table=np.array([1]), slot0=P,
+                                                                    k_dst=None, v_dst=None)], pool, tiny, 0))
+    assert name == "KAMERA_E_PAGE", msg
+
+
 def test_kernel_argument_route_still_checks_the_workspace():
     """A small dense batch is launched with the batch as the kernel's argument and the
     workspace unused, yet the call's contract is the same as on the workspace route: the

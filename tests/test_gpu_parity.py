@@ -191,6 +191,52 @@ def test_paged_slot0(slot0):
     assert pool_untouched_ok(dw)
 
 
+_PAGE_LAYOUTS = {
+    # two-slab MFMA path (128-wide heads), one-slab MFMA path (64-wide heads), MLA rows, generic fp32 kernel
+    "gqa128": (LayoutSpec(GQA, BF16, 2, num_kv_heads=2, head_dim=128, rope_base=1e6), 32),
+    "gqa64": (LayoutSpec(GQA, BF16, 2, num_kv_heads=4, head_dim=64, rope_base=1e4), 32),
+    "mla": (LayoutSpec(MLA, BF16, 2, latent_dim=512, rope_dim=64), 32),
+    "f32": (LayoutSpec(GQA, F32, 2, num_kv_heads=2, head_dim=64, rope_base=1e4), 8),
+}
+
+
+@pytest.mark.parametrize("P", [1, 3, 8, 24, 32, 64, 256])
+@pytest.mark.parametrize("kind", list(_PAGE_LAYOUTS))
+def test_page_sizes(kind, P):
+    """Pool pages of other sizes than 16 tokens ([K] §6 scatter into a paged pool): pages
+    smaller than a 16-token tile (1, 3, 8: every row looks its page up), sizes that are not
+    powers of two (3, 24: division instead of shifts; a tile straddles two 24-token pages), and
+    pages of 32 to 256 tokens. Each batch holds a patched chunk starting on a page's last slot,
+    an unpatched one starting mid-page, an in-place survivor and an in-place chunk with a patch;
+    outputs are checked against the oracle and every slot no chunk owns keeps its sentinel."""
+    say(f"[page size] {kind} P={P}")
+    base, rank = _PAGE_LAYOUTS[kind]
+    lay = dataclasses.replace(base, page_size=P)
+    if lay.family == MLA:
+        facs = lambda i: [factor(i, 0, 0, 0, 576, rank), factor(i, 1, 0, 512, 64, rank)]
+    else:
+        F = lay.num_kv_heads * lay.head_dim
+        facs = lambda i: [factor(i, 0, 0, 0, F, rank), factor(i, 1, 1, 0, F, rank)]
+    specs = [  # (tokens, slot0, delta, flags, role)
+        (150, P - 1, 12345, PATCH, "rehydrate"),
+        (37, P // 2, -777, 0, "rehydrate"),
+        (70, min(P - 1, 5), -4096, IN_PLACE, "survivor"),
+        (20, 0, 300, IN_PLACE | PATCH, "survivor"),
+    ]
+    need = [-(-(s0 + T) // P) for T, s0, _, _, _ in specs]
+    num_pages = sum(need) + 5
+    pages = np.random.default_rng(1000 + P).permutation(num_pages).astype(np.int32)
+    chunks, cur = [], 0
+    for i, ((T, s0, d, fl, role), n) in enumerate(zip(specs, need)):
+        chunks.append(ChunkSpec(index=i, num_tokens=T, delta=d, flags=fl, canon_id=i,
+                                factors=facs(i) if fl & PATCH else [], block_table=pages[cur:cur + n].copy(),
+                                slot0=s0, role=role))
+        cur += n
+    dw = run_dw(custom_workload(lay, chunks, dense_rows=[], num_pages=num_pages))
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
+
+
 def test_mixed_dense_paged_and_in_place_batch():
     """One batch mixing dense destinations, paged destinations, an in-place survivor and an
     empty chunk: a batch with any paged chunk runs in layer-major task order, so every

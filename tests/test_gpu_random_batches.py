@@ -3,7 +3,7 @@ families (GQA with 64- and 128-wide heads, MLA, fp32), both pairings, 0 to 4 fac
 chunk with assorted ranks, column ranges and first layers, chunk counts on both sides of the
 kernel-argument limit (16), empty chunks, deltas up to +-(2^31 - 1), per-token (t, h, w)
 offsets on some chunks (QV-PIC Eq. 2, under an M-RoPE section split), and mixes of dense
-destinations, paged destinations and in-place survivors. Every batch is compared with the
+destinations, paged destinations (pages of 1 to 64 tokens) and in-place survivors. Every batch is compared with the
 oracle element by element (Kamera preprint Eq. 1; same bar as the other parity tests), and
 the pool slots no chunk owns must keep their sentinel.
 """
@@ -36,7 +36,8 @@ def draw_batch(seed: int, kind=None, reanchor_ok: bool = True):
     kind = kind or drawn
     pairing = GPTJ if rng.random() < 0.3 else NEOX
     L = int(rng.integers(1, 4))
-    P = 16
+    # pool page size from a stream of its own (the main stream's draws are those of 16-token pages)
+    P = int(np.random.default_rng([20261202, seed, 1]).choice([16, 16, 16, 1, 3, 8, 24, 64]))
     reanchor = rng.random() < 0.35 and reanchor_ok   # some chunks turn token by token under an M-RoPE split
     if kind == "mla":
         lay = LayoutSpec(MLA, BF16, L, latent_dim=512, rope_dim=64, pairing=pairing, page_size=P,
@@ -89,7 +90,8 @@ def draw_batch(seed: int, kind=None, reanchor_ok: bool = True):
             buf += 1
         chunks.append(ChunkSpec(**kw))
     npos = sum(c.positions is not None for c in chunks)
-    desc = f"{kind} {'gptj' if pairing == GPTJ else 'neox'} L={L} chunks={n} paged={sum(paged)} re-anchored={npos}"
+    desc = (f"{kind} {'gptj' if pairing == GPTJ else 'neox'} L={L} chunks={n} paged={sum(paged)} page_size={P} "
+            f"re-anchored={npos}")
     return custom_workload(lay, chunks, num_pages=num_pages if any(paged) else 0), desc
 
 
