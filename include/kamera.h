@@ -130,9 +130,9 @@ typedef struct kamera_layout {
   int32_t dtype;         /* KAMERA_BF16 or KAMERA_F32 (all tensors of a call share it)    */
   int32_t num_layers;    /* L >= 1                                                        */
   int32_t num_kv_heads;  /* GQA: H_kv >= 1                                                */
-  int32_t head_dim;      /* GQA: even, >= 2; the rotary band is the whole head            */
+  int32_t head_dim;      /* GQA: even, in [2, 512]; the rotary band is the whole head     */
   int32_t latent_dim;    /* MLA: c_KV width >= 0                                          */
-  int32_t rope_dim;      /* MLA: k_rope width, even, >= 2                                 */
+  int32_t rope_dim;      /* MLA: k_rope width, even, in [2, 512]                          */
   int32_t pairing;       /* KAMERA_NEOX or KAMERA_GPTJ                                    */
   int32_t page_size;     /* tokens per pool page (>= 1); used by paged destinations       */
   int32_t patch_unit;    /* KAMERA_PATCH_UNIT_*: which unit adds the patch (see below)     */
@@ -313,7 +313,8 @@ kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tens
 /* Streaming probes (measurement only, not part of the operator): nontemporal 16-byte
  * accesses, each workgroup over a contiguous 16 KB block. KAMERA_PROBE_COPY copies `bytes`
  * from src to dst; KAMERA_PROBE_READ reads `bytes` of src (dst: a device sink of at least
- * 4 KB, written only for one XOR value of the data no caller builds); KAMERA_PROBE_WRITE
+ * 4 KB, stored to only when the XOR of a workgroup's words equals one fixed 16-byte value,
+ * which keeps the loads from being dropped); KAMERA_PROBE_WRITE
  * fills `bytes` of dst with the 32-bit `value` (src unused). Timing them beside the operator
  * gives the HBM's practical rates for the access kinds the operator mixes. `bytes` a
  * multiple of 16, pointers 16-byte aligned; stream-ordered like every call. */
