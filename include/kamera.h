@@ -313,7 +313,7 @@ kamera_status kamera_build_orbit_patch(const kamera_layout* layout, int32_t tens
 /* Streaming probes (measurement only, not part of the operator): nontemporal 16-byte
  * accesses, each workgroup over a contiguous 16 KB block. KAMERA_PROBE_COPY copies `bytes`
  * from src to dst; KAMERA_PROBE_READ reads `bytes` of src (dst: a device sink of at least
- * 4 KB, stored to only when the XOR of a workgroup's words equals one fixed 16-byte value,
+ * 4 KB, stored to only when the XOR of the words one thread read equals a fixed 16-byte value,
  * which keeps the loads from being dropped); KAMERA_PROBE_WRITE
  * fills `bytes` of dst with the 32-bit `value` (src unused). Timing them beside the operator
  * gives the HBM's practical rates for the access kinds the operator mixes. `bytes` a
