@@ -75,7 +75,7 @@ struct alignas(16) DevChunk {
 };
 
 struct alignas(16) DevHeader {
-  uint32_t zeros[4];    // 16 zero bytes: operand reads of lanes with no data point here
+  uint32_t reserved[4];  // zero
   int64_t total_tasks;
   int32_t nchunks;
   int32_t family;
