@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from tests.gpu_util import (check_all, custom_workload, factor, gqa_chunks, pool_untouched_ok, say,
-                            touched_tensors)
+                            sentinel_code, touched_tensors)
 from workloads import make_workload
 from workloads.configs import (BF16, F32, GPTJ, GQA, IN_PLACE, MLA, NEOX, PATCH, POSITIONS, ChunkSpec, LayoutSpec,
                                grid_positions)
@@ -235,6 +235,73 @@ def test_page_sizes(kind, P):
     dw = run_dw(custom_workload(lay, chunks, dense_rows=[], num_pages=num_pages))
     assert_parity(dw)
     assert pool_untouched_ok(dw)
+
+
+@pytest.mark.parametrize("case", ["gqa_mfma", "gqa_stride_not_8", "mla"])
+def test_strided_sources_and_pool_layers(case):
+    """Sources that are slices of larger buffers (src_layer_stride > T*F, first row at an
+    offset) and a pool whose layers are further apart than num_pages pages (layer_stride):
+    the operator must follow the strides it is given. A source stride that is not a multiple
+    of 8 elements takes the plain kernel (the 16-byte row loads need 8-element alignment);
+    the others run on the matrix-core kernel. Destinations are checked against the oracle
+    and every pool slot no chunk owns, the padding pages included, keeps its sentinel."""
+    from position_free_kv_amd import abi
+    from workloads.device import DeviceWorkload
+    say(f"[strides] {case}")
+    P = 16
+    if case == "mla":
+        lay = LayoutSpec(MLA, BF16, 3, latent_dim=512, rope_dim=64, page_size=P)
+        facs = lambda i: [factor(i, 0, 0, 0, 576, 32), factor(i, 1, 0, 512, 64, 32)]
+    else:
+        lay = LayoutSpec(GQA, BF16, 3, num_kv_heads=2, head_dim=128, rope_base=1e6, page_size=P)
+        facs = lambda i: [factor(i, 0, 0, 0, 256, 32), factor(i, 1, 1, 0, 256, 32)]
+    pages = np.random.default_rng(11).permutation(24).astype(np.int32)
+    chunks = [ChunkSpec(index=0, num_tokens=150, delta=4321, flags=PATCH, canon_id=0, factors=facs(0), dst_buffer=0),
+              ChunkSpec(index=1, num_tokens=70, delta=-999, flags=PATCH, canon_id=1, factors=facs(1),
+                        block_table=pages[0:5].copy(), slot0=3),
+              ChunkSpec(index=2, num_tokens=100, delta=-2048, flags=IN_PLACE, canon_id=2,
+                        block_table=pages[5:12].copy(), slot0=7, role="survivor")]
+    wl = custom_workload(lay, chunks, dense_rows=[150], num_pages=24)
+    dw = DeviceWorkload(wl)
+    L, F = dw.L, dw.F
+    keep = []
+    # sources: every layer's rows inside a larger buffer, the first row `off` elements in
+    extra = 4 if case == "gqa_stride_not_8" else 8 * F
+    off = 8 * 3
+    for ch, d in zip(wl.chunks, dw.descs):
+        if ch.in_place:
+            continue
+        stride = ch.num_tokens * F + extra
+        ptrs = []
+        for src in dw.canon[ch.canon_id]:
+            flat = torch.full((off + L * stride,), -1, dtype=src.dtype, device=src.device)
+            for layer in range(L):
+                flat[off + layer * stride: off + layer * stride + ch.num_tokens * F] = src[layer].reshape(-1)
+            keep.append(flat)
+            ptrs.append(flat.data_ptr() + off * flat.element_size())
+        d.c.k_src = ptrs[0]
+        d.c.v_src = ptrs[1] if len(ptrs) > 1 else None
+        d.c.src_layer_stride = stride
+    # pool: 3 pages of padding after each layer's 24 pages (sentinel-filled, never written)
+    pad = 3
+    padded = []
+    for t in dw.pool:
+        q = torch.full((L, wl.num_pages + pad, P, F), int(np.uint16(sentinel_code(BF16)).view(np.int16)),
+                       dtype=t.dtype, device=t.device)
+        q[:, :wl.num_pages] = t
+        padded.append(q)
+    dw.pool = padded
+    dw.pool_desc = abi.make_pool(padded[0], padded[1] if len(padded) == 2 else None, wl.num_pages,
+                                 layer_stride=(wl.num_pages + pad) * P * F)
+    plan = abi.plan_upload(dw.layout, dw.descs, dw.pool_desc, dw.workspace)
+    assert plan.kernel == (2 if case == "gqa_stride_not_8" else 1)   # 1: matrix-core kernel, 2: plain kernel
+    abi.plan_launch(plan)
+    torch.cuda.synchronize()
+    assert_parity(dw)
+    assert pool_untouched_ok(dw)
+    code = int(np.uint16(sentinel_code(BF16)).view(np.int16))
+    for q in padded:   # the padding pages between layers
+        assert bool((q[:, wl.num_pages:] == code).all())
 
 
 def test_mixed_dense_paged_and_in_place_batch():
