@@ -202,12 +202,14 @@ def counters(out: str, name: str, runs: list) -> None:
     in lower case) and, beside them, dir_p1.log, ... with each pass's bench.py JSON line."""
     table = {}
     cmds = []
+    hashes = set()
     for spec in runs:
         label, d = spec.rsplit("=", 1)
         vals = {}
         k = 1
         while os.path.isdir(os.path.join(out, d, f"p{k}")):
             bench = _bench_line(out, f"{d}_p{k}.log")
+            hashes.add(bench["kernel_source_hash"])
             pre = bench["config"]["name"].lower()
             rows = _rows(os.path.join(out, d, f"p{k}", f"{pre}_counter_collection.csv"))
             op = [r for r in rows if KERNEL in r["Kernel_Name"]]
@@ -236,6 +238,7 @@ def counters(out: str, name: str, runs: list) -> None:
     labels = list(table)
     names = sorted({c for v in table.values() for c in v})
     lines = [f"# rocprofv3 counters: {KERNEL}, {name}", "",
+             f"kernel source hash: {', '.join(sorted(hashes))}", "",
              "Per-dispatch means over the workload's own dispatches of the operator kernel (the same-pattern copy's "
              "dispatches excluded). Commands (one counter pass each; OUT is the output folder):", ""]
     lines += [f"    {c}" for c in cmds]
@@ -270,9 +273,11 @@ def sweep(out: str, name: str, title: str, runs: list) -> None:
              "launches; the same-pattern copy excluded), with bench.py's HIP-event average of the same kernel in the "
              "same run. Commands (OUT is the output folder):", ""]
     rows = []
+    hashes = set()
     for spec in runs:
         label, d = spec.rsplit("=", 1)
         bench = _bench_line(out, f"{d}.log")
+        hashes.add(bench["kernel_source_hash"])
         pre = bench["config"]["name"].lower()
         stats = _rows(os.path.join(out, d, "prof_trace", f"{pre}_kernel_stats.csv"))
         cands = [r for r in stats if KERNEL in r["Name"] and "_inline" not in r["Name"]]
@@ -286,7 +291,8 @@ def sweep(out: str, name: str, title: str, runs: list) -> None:
                     f"{bench['kernel_us']:.1f} | {alg / 1e9:.4f} | {alg / (avg * 1e-6) / 1e9:.0f} | "
                     f"{alg / (avg * 1e-6) / 8e12:.1%} |")
     lines += ["", "summarised with: python3 profile_summary.py " + " ".join(f'"{a}"' if " " in a else a
-                                                                for a in sys.argv[1:])]
+                                                                for a in sys.argv[1:]),
+              "", f"kernel source hash: {', '.join(sorted(hashes))}"]
     lines += ["", "| run | kernel | launches | rocprofv3 average us | bench HIP-event us | algorithmic GB | GB/s | "
               "% of 8 TB/s |", "|---|---|---|---|---|---|---|---|"] + rows
     with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as fh:
